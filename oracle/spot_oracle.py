@@ -1,0 +1,259 @@
+"""CPU oracle for the SpotAttention decode and prefill hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing but the tests, the smoke check and the
+benchmark's CPU-baseline leg may import or call this module; the product path
+never does. It shares no code with the HIP library and imports nothing from it.
+
+Plain, slow and obviously correct: every quantity is widened to float64 and each
+step follows the paper's definitions in the paper's order, with library
+primitives (einsum, sort, cumsum, exp) as the only building blocks and no
+blocking, fusion or reordering of the arithmetic.
+
+Source: "SpotAttention: Plug-In Block-Sparse Routing for Pretrained Long-Context
+Transformers" (Ahmad and Yun). Sections cited below are that paper's.
+
+Readings where the paper is silent or open (each is listed with its reason in the
+design notes of the repository):
+  * scores carry no 1/sqrt(d_idx) factor and the softmax temperature is 1 (§2.1 gives
+    the bare formula; Appendix A, Table 3 lists temperature 1.0);
+  * K_min and K_max bound the total set size |S_q| (Eq. 8 states the floor on |S_q|;
+    the cap is the same kind of bound), so the nucleus is clamped to
+    [K_min - r, K_max - r] where r = |S_sink u S_rec|;
+  * "reaches p" means cumulative residual mass >= p; p >= 1 keeps every residual
+    block, p <= 0 keeps none before the floor;
+  * ties in score are broken by the lower block index; -0.0 equals +0.0;
+  * an empty selected set gives a zero output row;
+  * the selected set is reported in ascending block order.
+
+Every function here is pinned by tests/test_oracle_pins.py to closed forms,
+brute force on tiny inputs, textbook library routines or figures printed in the
+paper; no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Selector K-cache decoding (§5.3 and Appendix G: INT4 microscale, group 32,
+# 4.5 bits per element = 4-bit codes plus one 16-bit scale per 32 elements).
+# ---------------------------------------------------------------------------
+def dequant_int4_g32(codes, scales):
+    """Decode INT4 codes with one fp16 scale per 32 elements.
+
+    codes  uint8 [..., n/2]: element 2i in the low nibble, element 2i+1 in the high
+           nibble, each a two's-complement value in [-8, 7];
+    scales float16 [..., n/32].
+    Returns float64 [..., n] with value = code * scale, computed exactly.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    lo = (codes & 0x0F).astype(np.int64)
+    hi = (codes >> 4).astype(np.int64)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    n = codes.shape[-1] * 2
+    vals = np.empty(codes.shape[:-1] + (n,), dtype=np.float64)
+    vals[..., 0::2] = lo
+    vals[..., 1::2] = hi
+    scale_per_elem = np.repeat(scales, 32, axis=-1)
+    assert scale_per_elem.shape == vals.shape
+    return vals * scale_per_elem
+
+
+# ---------------------------------------------------------------------------
+# Selector scoring (§2.1 score formula; §2.3 per-block maximum).
+# ---------------------------------------------------------------------------
+def select_score(sel_q, sel_w, sel_k):
+    """Block scores s_bar[b, blk] = max over the block's selector keys j of
+    sum_h w[b,h] * ReLU(q[b,h,:] . k[b,blk,j,h,:]).
+
+    sel_q [B][H][d_idx], sel_w [B][H], sel_k [B][nb][kpb][H][d_idx] (already decoded).
+    Returns float64 [B][nb].
+    """
+    q = np.asarray(sel_q, dtype=np.float64)
+    w = np.asarray(sel_w, dtype=np.float64)
+    k = np.asarray(sel_k, dtype=np.float64)
+    dots = np.einsum("bhi,bnjhi->bnjh", q, k)          # q_h . k_{h,t}
+    per_key = (w[:, None, None, :] * np.maximum(dots, 0.0)).sum(axis=-1)
+    return per_key.max(axis=-1)                         # max over t in the block
+
+
+# ---------------------------------------------------------------------------
+# Dual top-p selection (§2.3, Eq. 7 and Eq. 8).
+# ---------------------------------------------------------------------------
+def reserved_set(nb, n_sink, n_rec):
+    """S_sink (first n_sink blocks) union S_rec (last n_rec blocks), clipped to [0, nb)."""
+    sink = set(range(0, min(n_sink, nb)))
+    rec = set(range(max(nb - n_rec, 0), nb))
+    return sorted(sink | rec)
+
+
+def select_topp_row(scores, p, K_min, K_max, n_sink, n_rec):
+    """Dual top-p on one query's block scores.
+
+    1. reserve the sink prefix and the recency suffix;
+    2. softmax of the scores over the residual blocks only (Eq. 7);
+    3. sort the residual blocks by score descending (lower index first on ties) and
+       take the smallest prefix whose cumulative mass reaches p (the nucleus);
+    4. clamp the prefix length so that |S| lies in [K_min, K_max] (Eq. 8's floor, and
+       the cap), extending or cutting along the same order;
+    5. S = reserved union prefix, reported in ascending order.
+
+    Returns (sel: sorted list of block indices, info: dict of diagnostics).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    nb = s.shape[0]
+    reserved = reserved_set(nb, n_sink, n_rec)
+    r = len(reserved)
+    if K_max < r:
+        raise ValueError("K_max smaller than the reserved set")
+    rset = set(reserved)
+    residual = np.array([i for i in range(nb) if i not in rset], dtype=np.int64)
+    info = {"r": r, "n_res": len(residual), "k_p": 0, "k": 0, "mass": 0.0}
+    if len(residual) == 0:
+        info["k_p"] = 0
+        return list(range(nb)), info
+    sr = s[residual]
+    m = sr.max()
+    e = np.exp(sr - m)
+    Z = e.sum()
+    order = np.lexsort((residual, -sr))                 # score desc, then index asc
+    n_res = len(residual)
+    if p >= 1.0:
+        k_p = n_res
+    elif p <= 0.0:
+        k_p = 0
+    else:
+        cum = np.cumsum(e[order])
+        hit = np.nonzero(cum >= p * Z)[0]
+        k_p = int(hit[0]) + 1 if len(hit) else n_res
+    lo = max(0, K_min - r)
+    hi = K_max - r
+    k = min(max(k_p, lo), hi, n_res)
+    chosen = residual[order[:k]]
+    sel = sorted(set(reserved) | set(int(c) for c in chosen))
+    info.update(k_p=k_p, k=k, mass=float(e[order[:k]].sum() / Z),
+                cum=np.cumsum(e[order]) / Z, order=residual[order], sorted_scores=sr[order])
+    return sel, info
+
+
+def select_topp(scores, p, K_min, K_max, n_sink, n_rec):
+    """Row-wise dual top-p over scores [B][nb]; returns a list of sorted index lists
+    and a list of per-row diagnostics."""
+    scores = np.asarray(scores, dtype=np.float64)
+    sels, infos = [], []
+    for row in scores:
+        sel, info = select_topp_row(row, p, K_min, K_max, n_sink, n_rec)
+        sels.append(sel)
+        infos.append(info)
+    return sels, infos
+
+
+# ---------------------------------------------------------------------------
+# Attention over the selected blocks (§2.3: the layer attends only to keys in
+# blocks of S_q; one set per query, shared by every head of the layer).
+# Written as dense softmax attention with -inf outside the selected keys.
+# ---------------------------------------------------------------------------
+def token_mask(sel, L, block):
+    """Boolean [L]: True for tokens whose block is in ``sel``."""
+    mask = np.zeros(L, dtype=bool)
+    nbl = -(-L // block)
+    for blk in sel:
+        blk = int(blk)
+        if 0 <= blk < nbl:
+            mask[blk * block: min((blk + 1) * block, L)] = True
+    return mask
+
+
+def sparse_attention(q, K, V, sels, block, sm_scale, heads=None):
+    """Decode attention restricted to the selected blocks.
+
+    q [B][Hq][d]; K, V [B][Hkv][L][d]; sels[b] = block indices for query b.
+    Query head hq reads KV head hq // (Hq/Hkv). Returns float64 [B][Hq][d]
+    (rows not in ``heads`` are left at zero when a subset of (b, hq) is given).
+    """
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv, L = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for b in range(B):
+        mask = token_mask(sels[b], L, block)
+        if not mask.any():
+            continue
+        for g in range(Hkv):
+            hqs = [h for h in range(g * G, (g + 1) * G) if heads is None or (b, h) in heads]
+            if not hqs:
+                continue
+            Kg = np.asarray(K[b, g], dtype=np.float64)
+            Vg = np.asarray(V[b, g], dtype=np.float64)
+            for hq in hqs:
+                z = (Kg @ np.asarray(q[b, hq], dtype=np.float64)) * sm_scale
+                z = np.where(mask, z, -np.inf)
+                w = np.exp(z - z.max())
+                out[b, hq] = (w @ Vg) / w.sum()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Prefill tile variant (§2.1: one score per query-block x key-block tile;
+# §2.3 selection; causal attention within the tile).
+# ---------------------------------------------------------------------------
+def prefill_tile_score(sel_q, sel_w, sel_k, q_pos0, block):
+    """Tile block scores for a tile of Tq consecutive queries at positions
+    q_pos0 .. q_pos0+Tq-1.
+
+    sel_q [B][Tq][H][d_idx], sel_w [B][Tq][H], sel_k [B][nb][kpb][H][d_idx].
+    A block is visible to a query when its first token is at or before the query's
+    position. The tile score of a block is the maximum, over the tile's queries that
+    see it, of that query's block score. Returns float64 [B][nb_vis] with
+    nb_vis = ceil((q_pos0 + Tq) / block).
+    """
+    q = np.asarray(sel_q, dtype=np.float64)
+    w = np.asarray(sel_w, dtype=np.float64)
+    k = np.asarray(sel_k, dtype=np.float64)
+    B, Tq = q.shape[0], q.shape[1]
+    nb_vis = -(-(q_pos0 + Tq) // block)
+    k = k[:, :nb_vis]
+    dots = np.einsum("bqhi,bnjhi->bqnjh", q, k)
+    per_key = (w[:, :, None, None, :] * np.maximum(dots, 0.0)).sum(axis=-1)
+    per_q = per_key.max(axis=-1)                           # [B][Tq][nb_vis]
+    pos = q_pos0 + np.arange(Tq)
+    first_tok = np.arange(nb_vis) * block
+    visible = first_tok[None, :] <= pos[:, None]           # [Tq][nb_vis]
+    per_q = np.where(visible[None], per_q, -np.inf)
+    return per_q.max(axis=1)
+
+
+def prefill_attention(Q, K, V, sels, block, sm_scale, q_pos0, heads=None):
+    """Causal attention for a prefill tile restricted to the selected blocks.
+
+    Q [B][Hq][Tq][d]; K, V [B][Hkv][L][d]. Query i (position q_pos0 + i) reads the
+    tokens t <= q_pos0 + i whose block is selected. Returns float64 [B][Hq][Tq][d].
+    """
+    Q = np.asarray(Q)
+    B, Hq, Tq, d = Q.shape
+    Hkv, L = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, Tq, d), dtype=np.float64)
+    pos = q_pos0 + np.arange(Tq)
+    for b in range(B):
+        sel_mask = token_mask(sels[b], L, block)
+        causal = np.arange(L)[None, :] <= pos[:, None]      # [Tq][L]
+        mask = causal & sel_mask[None, :]
+        for g in range(Hkv):
+            hqs = [h for h in range(g * G, (g + 1) * G) if heads is None or (b, h) in heads]
+            if not hqs:
+                continue
+            Kg = np.asarray(K[b, g], dtype=np.float64)
+            Vg = np.asarray(V[b, g], dtype=np.float64)
+            for hq in hqs:
+                z = (np.asarray(Q[b, hq], dtype=np.float64) @ Kg.T) * sm_scale   # [Tq][L]
+                z = np.where(mask, z, -np.inf)
+                zmax = z.max(axis=1, keepdims=True)
+                has = np.isfinite(zmax)
+                w = np.where(mask, np.exp(z - np.where(has, zmax, 0.0)), 0.0)
+                den = w.sum(axis=1, keepdims=True)
+                out[b, hq] = np.where(has, (w @ Vg) / np.where(den > 0, den, 1.0), 0.0)
+    return out

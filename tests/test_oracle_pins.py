@@ -1,0 +1,391 @@
+"""Pins for the CPU oracle: closed forms, brute force on tiny inputs, textbook
+library routines, and figures printed in the SpotAttention paper.
+
+Each test is chosen so that a plausible mistake in the oracle (a dropped ReLU or
+weight, a stray 1/sqrt(d), a sum in place of a max, softmax over all blocks
+instead of the residual ones, > in place of >=, a wrong tie order, a wrong clamp,
+a transposed operand, a causal off-by-one) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spot_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------- score
+def test_score_planted_closed_form():
+    # k_h = 3 q_h for every head: q.k = 3|q_h|^2 >= 0, so s = 3 sum_h w_h |q_h|^2.
+    r = rng(1)
+    B, nb, kpb, H, d = 2, 5, 1, 3, 8
+    q = r.standard_normal((B, H, d))
+    w = np.abs(r.standard_normal((B, H)))
+    k = r.standard_normal((B, nb, kpb, H, d))
+    k[:, 2, 0] = 3.0 * q
+    s = O.select_score(q, w, k)
+    expect = 3.0 * (w * (q * q).sum(-1)).sum(-1)
+    np.testing.assert_allclose(s[:, 2], expect, rtol=1e-14)
+
+
+def test_score_relu_and_sign_of_w():
+    r = rng(2)
+    q = r.standard_normal((1, 2, 4))
+    w = np.array([[2.0, -0.5]])
+    k = np.zeros((1, 3, 1, 2, 4))
+    k[0, 0, 0, 0] = -q[0, 0]          # negative dot on head 0 -> ReLU -> 0
+    k[0, 0, 0, 1] = -q[0, 1]
+    k[0, 1, 0, 0] = q[0, 0]           # head 0 only: 2 |q0|^2
+    k[0, 2, 0, 1] = q[0, 1]           # head 1 only, negative weight: -0.5 |q1|^2
+    s = O.select_score(q, w, k)
+    assert s[0, 0] == 0.0
+    assert s[0, 1] == pytest.approx(2.0 * (q[0, 0] ** 2).sum(), rel=1e-14)
+    assert s[0, 2] == pytest.approx(-0.5 * (q[0, 1] ** 2).sum(), rel=1e-14)
+
+
+def test_score_block_max_over_keys():
+    # The block score is the maximum over its keys (per-block max pooling, §2.3),
+    # not a sum or a mean: compare with one-key blocks scored separately.
+    r = rng(3)
+    B, nb, kpb, H, d = 2, 4, 5, 3, 6
+    q = r.standard_normal((B, H, d))
+    w = r.standard_normal((B, H))
+    k = r.standard_normal((B, nb, kpb, H, d))
+    s = O.select_score(q, w, k)
+    singles = np.stack([O.select_score(q, w, k[:, :, j:j + 1])[..., None]
+                        for j in range(kpb)], -1)[..., 0, :]
+    np.testing.assert_array_equal(s, singles.max(-1))
+    assert not np.allclose(s, singles.sum(-1))
+
+
+def test_score_is_not_scaled_by_sqrt_d():
+    q = np.ones((1, 1, 16))
+    k = np.ones((1, 1, 1, 1, 16))
+    w = np.ones((1, 1))
+    assert O.select_score(q, w, k)[0, 0] == 16.0
+
+
+# ----------------------------------------------------------------------------- int4
+def test_int4_nibble_order_and_sign():
+    codes = np.array([[0x87, 0x10, 0xF0]], dtype=np.uint8)   # elements: 7,-8, 0,1, 0,-1
+    codes = np.concatenate([codes, np.zeros((1, 13), np.uint8)], axis=1)
+    scales = np.array([[0.5]], dtype=np.float16)
+    v = O.dequant_int4_g32(codes, scales)
+    np.testing.assert_array_equal(v[0, :6], [3.5, -4.0, 0.0, 0.5, 0.0, -0.5])
+    assert v.shape == (1, 32)
+
+
+def test_int4_every_code_value():
+    # the 256 byte values decode to every (lo, hi) pair of two's-complement nibbles
+    codes = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    v = O.dequant_int4_g32(codes, np.ones((16, 1), np.float16))
+    lo = v[:, 0::2].ravel()
+    hi = v[:, 1::2].ravel()
+    nib = lambda x: x - 16 if x >= 8 else x
+    assert [int(x) for x in lo] == [nib(b & 15) for b in range(256)]
+    assert [int(x) for x in hi] == [nib(b >> 4) for b in range(256)]
+
+
+def test_int4_group_scale_and_quantizer_roundtrip():
+    from block_sparse_long_spot_amd.workloads import quantize_int4_g32
+    x = torch.randn(3, 4, 64, generator=torch.Generator().manual_seed(5))
+    codes, scales = quantize_int4_g32(x)
+    assert codes.shape == (3, 4, 32) and scales.shape == (3, 4, 2)
+    v = O.dequant_int4_g32(codes.numpy(), scales.numpy())
+    step = np.repeat(scales.float().numpy().astype(np.float64), 32, -1)
+    err = np.abs(v - x.double().numpy())
+    assert (err <= 0.5 * step * (1 + 1e-6) + 1e-12).all()
+    # each group's largest element maps to code +-7 exactly
+    g = x.reshape(3, 4, 2, 32).abs().amax(-1)
+    np.testing.assert_allclose(scales.float().numpy(), (g / 7).half().float().numpy())
+
+
+def test_int4_bytes_match_pages_figures():
+    fig = json.load(open(GOLDEN))
+    n = 1024
+    codes_bytes, scale_bytes = n // 2, (n // 32) * 2
+    bits = 8 * (codes_bytes + scale_bytes) / n
+    assert bits == fig["int4_bits_per_element"]["value"]
+    assert round(bits / 16, 3) == fig["int4_fraction_of_bf16"]["value"]
+    # the paper's selector cache: 4.50 GiB in BF16 at 128K shrinks to 1.27 GiB
+    bf16 = fig["selector_cache_gib_bf16_128k"]["value"]
+    assert round(bf16 * bits / 16, 2) == fig["selector_cache_gib_int4_128k"]["value"]
+    # "3.5x" is the printed 4.50 / 1.27 = 3.54, truncated to one decimal
+    shrink = bf16 / fig["selector_cache_gib_int4_128k"]["value"]
+    assert math.floor(shrink * 10) / 10 == fig["selector_cache_shrink"]["value"]
+    # FP4 (E2M1) with an 8-bit shared scale is 4.25 bits -> 1.20 GiB
+    assert round(bf16 * 4.25 / 16, 2) == fig["selector_cache_gib_fp4_128k"]["value"]
+    # at Table 3 geometry (4 heads x 128 dims per token) 4.50 GiB is 36 layers x 128K tokens
+    per_layer = 131072 * fig["table3_H_idx"]["value"] * fig["table3_d_idx"]["value"] * 2
+    assert 36 * per_layer == bf16 * 2 ** 30
+    assert fig["table3_K_min_tokens"]["value"] // fig["table3_block_size"]["value"] == \
+        fig["table3_K_min_blocks"]["value"]
+
+
+# ----------------------------------------------------------------------------- top-p
+def brute_force_nucleus(res_scores, p):
+    """Smallest subset size of the residual blocks whose softmax mass reaches p,
+    by enumerating every subset."""
+    e = np.exp(res_scores - res_scores.max())
+    Z = e.sum()
+    n = len(e)
+    for size in range(0, n + 1):
+        best = max((sum(e[list(c)]) for c in itertools.combinations(range(n), size)),
+                   default=0.0)
+        if best >= p * Z - 1e-12 * Z:
+            return size, best / Z
+    return n, 1.0
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topp_brute_force_minimal_nucleus(seed):
+    r = rng(100 + seed)
+    nb = int(r.integers(4, 13))
+    n_sink, n_rec = int(r.integers(0, 3)), int(r.integers(0, 3))
+    s = r.standard_normal(nb) * float(r.choice([0.5, 2.0, 5.0]))
+    p = float(r.choice([0.3, 0.5, 0.7, 0.9, 0.95]))
+    reserved = O.reserved_set(nb, n_sink, n_rec)
+    res = [i for i in range(nb) if i not in reserved]
+    sel, info = O.select_topp_row(s, p, K_min=0, K_max=nb, n_sink=n_sink, n_rec=n_rec)
+    assert set(reserved) <= set(sel)
+    if not res:
+        assert sel == list(range(nb))
+        return
+    size, best_mass = brute_force_nucleus(s[res], p)
+    assert info["k_p"] == size
+    chosen = [i for i in sel if i not in reserved]
+    assert len(chosen) == size
+    e = np.exp(s[res] - s[res].max())
+    mass = sum(e[res.index(i)] for i in chosen) / e.sum()
+    assert mass == pytest.approx(best_mass, rel=1e-12)   # the prefix is a heaviest subset
+    assert mass >= p - 1e-12
+    if size > 1:                                          # one fewer block falls short
+        worst_drop = min(e[res.index(i)] for i in chosen) / e.sum()
+        assert mass - worst_drop < p
+
+
+def test_topp_softmax_is_over_residual_blocks_only():
+    # A huge sink score must not shrink the residual distribution (Eq. 7).
+    s = np.array([50.0, 1.0, 0.9, 0.8, 0.7, 0.0])
+    sel, info = O.select_topp_row(s, 0.5, 0, 6, n_sink=1, n_rec=1)
+    e = np.exp(np.array([1.0, 0.9, 0.8, 0.7]) - 1.0)
+    cum = np.cumsum(e) / e.sum()
+    assert info["k_p"] == int(np.argmax(cum >= 0.5)) + 1 == 2
+    assert sel == [0, 1, 2, 5]
+
+
+def test_topp_reaches_means_greater_or_equal():
+    # two residual blocks of equal score: mass 0.5 each; p = 0.5 is reached by one block
+    s = np.array([0.0, 3.0, 3.0])
+    sel, info = O.select_topp_row(s, 0.5, 0, 3, n_sink=1, n_rec=0)
+    assert info["k_p"] == 1 and sel == [0, 1]
+
+
+def test_topp_ties_lower_index_first_and_negative_zero():
+    s = np.array([1.0, 2.0, 2.0, 2.0, -0.0, 0.0, 2.0, 5.0])
+    sel, info = O.select_topp_row(s, 0.0, K_min=3, K_max=3, n_sink=0, n_rec=1)
+    assert sel == [1, 2, 7]
+    sel, _ = O.select_topp_row(s, 0.0, K_min=7, K_max=7, n_sink=0, n_rec=1)
+    assert sel == [0, 1, 2, 3, 4, 6, 7]      # -0.0 at index 4 ties +0.0 at 5: lower first
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_topp_static_topk_special_case(seed):
+    # p = 0 with K_min = K_max = K + r is static top-K (Eq. 6) on the residual blocks
+    r = rng(300 + seed)
+    nb = int(r.integers(5, 40))
+    s = np.round(r.standard_normal(nb), 1)             # rounding creates ties
+    n_sink, n_rec = 1, 2
+    reserved = O.reserved_set(nb, n_sink, n_rec)
+    K = int(r.integers(0, nb - len(reserved) + 1))
+    sel, _ = O.select_topp_row(s, 0.0, K + len(reserved), K + len(reserved), n_sink, n_rec)
+    chosen = set(sel) - set(reserved)
+    rest = set(range(nb)) - set(sel)
+    assert len(chosen) == K
+    for a in chosen:
+        for b in rest:
+            assert s[a] > s[b] or (s[a] == s[b] and a < b)
+
+
+def test_topp_floor_and_cap_bound_the_total():
+    r = rng(7)
+    s = r.standard_normal(64)
+    s[10] = 40.0                                        # nucleus of size 1
+    sel, info = O.select_topp_row(s, 0.9, K_min=16, K_max=20, n_sink=1, n_rec=2)
+    assert info["k_p"] == 1 and len(sel) == 16 and info["k"] == 13
+    s2 = np.zeros(64)                                   # flat: nucleus = 0.9 * 61
+    sel2, info2 = O.select_topp_row(s2, 0.9, K_min=4, K_max=20, n_sink=1, n_rec=2)
+    assert info2["k_p"] == math.ceil(0.9 * 61 - 1e-9) and len(sel2) == 20
+    assert sel2 == [0] + list(range(1, 18)) + [62, 63]  # cap keeps the lowest indices on ties
+
+
+def test_topp_edge_cases():
+    s = rng(8).standard_normal(10)
+    assert O.select_topp_row(s, 1.0, 0, 10, 1, 1)[0] == list(range(10))
+    assert O.select_topp_row(s, 0.0, 0, 10, 1, 1)[0] == [0, 9]
+    assert O.select_topp_row(s, 0.5, 0, 10, 6, 6)[0] == list(range(10))   # empty residual
+    assert O.select_topp_row(s, 0.0, 50, 10, 0, 0)[0] == list(range(10))  # floor above nb
+    assert O.select_topp_row(s, 0.7, 2, 2, 1, 1)[0] == [0, 9]             # K_max == r
+    with pytest.raises(ValueError):
+        O.select_topp_row(s, 0.7, 0, 1, 1, 1)
+
+
+def test_topp_monotone_in_p_and_shift_invariant():
+    r = rng(9)
+    s = r.standard_normal(200) * 3
+    prev = set()
+    for p in np.linspace(0.0, 1.0, 21):
+        sel, _ = O.select_topp_row(s, p, 4, 200, 1, 4)
+        assert prev <= set(sel)
+        prev = set(sel)
+        assert O.select_topp_row(s + 123.0, p, 4, 200, 1, 4)[0] == sel
+
+
+@pytest.mark.parametrize("s_exp", [1.1, 1.3, 2.0])
+def test_topp_zipf_closed_form(s_exp):
+    # scores t_r = s ln(n/r) give residual masses r^-s / H_n(s); the nucleus size is the
+    # first k whose generalised harmonic partial sum reaches p H_n(s).
+    n, p = 2043, 0.95
+    rank = np.arange(1, n + 1)
+    perm = rng(10).permutation(n)
+    scores = np.zeros(n + 5)
+    res_idx = np.arange(1, n + 1)
+    scores[res_idx[perm]] = s_exp * np.log(n / rank)
+    sel, info = O.select_topp_row(scores, p, 0, n + 5, n_sink=1, n_rec=4)
+    terms = [float(x) ** -s_exp for x in rank]
+    Hn = math.fsum(terms)
+    acc, kp = 0.0, None
+    for k, t in enumerate(terms, 1):
+        acc += t
+        if acc >= p * Hn:
+            kp = k
+            break
+    assert info["k_p"] == kp
+    if s_exp == 1.1:
+        assert 1000 < kp < 1200          # the 128K workload's nucleus is far above K_max=256
+
+
+# ----------------------------------------------------------------------------- attention
+def sdpa_gqa(q, K, V, mask, scale):
+    """torch's scaled_dot_product_attention in float64 on the CPU, GQA by repetition.
+    q [Hq][T][d], K/V [Hkv][L][d], mask [T][L] boolean (True = attend)."""
+    Hq, Hkv = q.shape[0], K.shape[0]
+    Kr = torch.from_numpy(np.repeat(K, Hq // Hkv, axis=0))
+    Vr = torch.from_numpy(np.repeat(V, Hq // Hkv, axis=0))
+    qt = torch.from_numpy(q)
+    m = torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        qt, Kr, Vr, attn_mask=m, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("L", [256, 300, 64 * 5 - 1])
+def test_attention_all_blocks_equals_dense(L):
+    r = rng(11)
+    B, Hq, Hkv, d, block = 2, 8, 2, 16, 64
+    q = r.standard_normal((B, Hq, d))
+    K = r.standard_normal((B, Hkv, L, d))
+    V = r.standard_normal((B, Hkv, L, d))
+    nb = -(-L // block)
+    scale = 1 / math.sqrt(d)
+    out = O.sparse_attention(q, K, V, [list(range(nb))] * B, block, scale)
+    for b in range(B):
+        ref = sdpa_gqa(q[b][:, None, :], K[b], V[b], np.ones((1, L), bool), scale)[:, 0]
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_subset_equals_masked_sdpa():
+    r = rng(12)
+    B, Hq, Hkv, d, L, block = 1, 4, 1, 8, 200, 64
+    q = r.standard_normal((B, Hq, d))
+    K = r.standard_normal((B, Hkv, L, d))
+    V = r.standard_normal((B, Hkv, L, d))
+    sel = [1, 3]                                    # block 3 is the partial last block
+    out = O.sparse_attention(q, K, V, [sel], block, 0.3)
+    mask = np.zeros((1, L), bool)
+    mask[0, 64:128] = True
+    mask[0, 192:200] = True
+    ref = sdpa_gqa(q[0][:, None, :], K[0], V[0], mask, 0.3)[:, 0]
+    np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_equal_keys_give_mean_of_values():
+    r = rng(13)
+    B, Hq, Hkv, d, L, block = 1, 2, 1, 4, 256, 64
+    q = r.standard_normal((B, Hq, d))
+    K = np.tile(r.standard_normal(d), (B, Hkv, L, 1))
+    V = r.standard_normal((B, Hkv, L, d))
+    out = O.sparse_attention(q, K, V, [[0, 2]], block, 1.0)
+    expect = np.concatenate([V[0, 0, 0:64], V[0, 0, 128:192]]).mean(0)
+    np.testing.assert_allclose(out[0, 0], expect, rtol=1e-12)
+    np.testing.assert_allclose(out[0, 1], expect, rtol=1e-12)
+
+
+def test_attention_gqa_head_mapping_and_empty_set():
+    r = rng(14)
+    q = r.standard_normal((1, 4, 8))
+    K = r.standard_normal((1, 2, 64, 8))
+    V = np.zeros((1, 2, 64, 8))
+    V[0, 1] = 1.0                                    # only KV head 1 carries ones
+    out = O.sparse_attention(q, K, V, [[0]], 64, 1.0)
+    np.testing.assert_array_equal(out[0, :2], 0.0)   # query heads 0,1 -> KV head 0
+    np.testing.assert_allclose(out[0, 2:], 1.0)      # query heads 2,3 -> KV head 1
+    out = O.sparse_attention(q, K, V + 1, [[]], 64, 1.0)
+    np.testing.assert_array_equal(out, 0.0)
+
+
+# ----------------------------------------------------------------------------- prefill
+def test_prefill_all_blocks_equals_causal_sdpa():
+    r = rng(15)
+    B, Hq, Hkv, Tq, d, L, block = 1, 4, 2, 40, 8, 300, 64
+    q_pos0 = L - Tq
+    Q = r.standard_normal((B, Hq, Tq, d))
+    K = r.standard_normal((B, Hkv, L, d))
+    V = r.standard_normal((B, Hkv, L, d))
+    nb = -(-L // block)
+    out = O.prefill_attention(Q, K, V, [list(range(nb))], block, 0.25, q_pos0)
+    mask = np.arange(L)[None, :] <= (q_pos0 + np.arange(Tq))[:, None]
+    ref = sdpa_gqa(Q[0], K[0], V[0], mask, 0.25)
+    np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_subset_equals_masked_sdpa():
+    r = rng(16)
+    B, Hq, Hkv, Tq, d, L, block = 1, 2, 1, 70, 8, 320, 64
+    q_pos0 = 250
+    Q = r.standard_normal((B, Hq, Tq, d))
+    K = r.standard_normal((B, Hkv, L, d))
+    V = r.standard_normal((B, Hkv, L, d))
+    sel = [0, 2, 3, 4]
+    out = O.prefill_attention(Q, K, V, [sel], block, 0.5, q_pos0)
+    tok_sel = np.zeros(L, bool)
+    for blk in sel:
+        tok_sel[blk * 64:(blk + 1) * 64] = True
+    mask = (np.arange(L)[None, :] <= (q_pos0 + np.arange(Tq))[:, None]) & tok_sel[None]
+    ref = sdpa_gqa(Q[0], K[0], V[0], mask, 0.5)
+    np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_tile_score_is_max_over_visible_queries():
+    r = rng(17)
+    B, Tq, H, di, nb, block = 1, 8, 2, 4, 6, 4
+    q_pos0 = 14                                      # queries at 14..21 -> blocks 3..5
+    sq = r.standard_normal((B, Tq, H, di))
+    w = np.abs(r.standard_normal((B, Tq, H)))
+    k = r.standard_normal((B, nb, 1, H, di))
+    k[0, 5, 0] = 3.0 * sq[0, 7]                      # block 5 starts at 20: seen by q 6, 7
+    s = O.prefill_tile_score(sq, w, k, q_pos0, block)
+    assert s.shape == (1, 6)
+    per_q = np.stack([O.select_score(sq[:, i], w[:, i], k) for i in range(Tq)], 1)
+    np.testing.assert_allclose(s[0, :5], per_q[0, :, :5].max(0), rtol=1e-14)
+    assert s[0, 5] == per_q[0, 6:, 5].max()
+    assert s[0, 5] >= 3.0 * (w[0, 7] * (sq[0, 7] ** 2).sum(-1)).sum() * (1 - 1e-14)
