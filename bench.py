@@ -1,0 +1,255 @@
+"""Decode-step benchmark: selector scoring + dual top-p + sparse attention at L=128K.
+
+    python bench.py [--steps K] [--warmup W] [--workload c3_128k_b8] [--no-cpu-baseline]
+
+Times K back-to-back decode steps (the three C calls per step, enqueued on one stream)
+between device synchronisations, with inputs already resident in HBM, and prints one
+JSON line. HIP events recorded between the calls on the launch stream give each
+call's average duration; the sparse-attention call is the dominant kernel and its
+algorithmic bytes per launch over that duration is the roofline figure. The CPU
+baseline is the fp64 oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+import block_sparse_long_spot_amd as spot
+from block_sparse_long_spot_amd import workloads as W
+from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
+
+METRIC = "decode step µs (select+top-p+sparse attn) at L=128K; achieved HBM GB/s %peak"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def selected_tokens(sel_idx, sel_cnt, L, block):
+    idx = sel_idx.cpu().numpy()
+    cnt = sel_cnt.cpu().numpy()
+    tot = 0
+    nbl = -(-L // block)
+    for b in range(idx.shape[0]):
+        for blk in idx[b, : int(cnt[b])]:
+            if 0 <= blk < nbl:
+                tot += min((int(blk) + 1) * block, L) - int(blk) * block
+    return tot
+
+
+def byte_budget(wl, B, tokens):
+    """Algorithmic bytes of one step, split by call."""
+    es = 4 if wl.dtype == "f32" else 2
+    n_el = B * wl.nb * wl.kpb * wl.H_idx * wl.d_idx
+    if wl.sel_k_dtype == "int4":
+        selk = n_el // 2 + (n_el // 32) * 2
+    else:
+        selk = n_el * (4 if wl.sel_k_dtype == "f32" else 2)
+    score = selk + B * wl.H_idx * (wl.d_idx * es + 4) + B * wl.nb * 4
+    topp = B * wl.nb * 4 + B * wl.K_max * 4 + B * 8
+    attn = tokens * wl.Hkv * wl.d * 2 * es + B * wl.Hq * wl.d * 2 * es
+    algorithmic = selk + B * wl.H_idx * (wl.d_idx * es + 4) + tokens * wl.Hkv * wl.d * 2 * es \
+        + B * wl.Hq * wl.d * 2 * es
+    return {"score": score, "topp": topp, "attn": attn, "step": algorithmic}
+
+
+def time_steps(inp, wl, bufs, steps, warmup, stream):
+    for _ in range(warmup):
+        decode_step(inp, wl, bufs, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            ev[i][0].record(stream)
+            spot.spot_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"],
+                                   inp.get("sel_k_scale"), bufs.scores, stream=stream)
+            ev[i][1].record(stream)
+            spot.spot_select_topp(bufs.scores, bufs.sel_idx, bufs.sel_cnt, bufs.sel_mass, wl.p,
+                                  wl.K_min, wl.K_max, wl.n_sink, wl.n_rec, stream=stream)
+            ev[i][2].record(stream)
+            spot.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx, bufs.sel_cnt,
+                                  bufs.out, bufs.workspace, 1.0 / math.sqrt(wl.d),
+                                  block=wl.block, stream=stream)
+            ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {"score": [], "topp": [], "attn": [], "step": []}
+    for e in ev:
+        per["score"].append(e[0].elapsed_time(e[1]) * 1e3)
+        per["topp"].append(e[1].elapsed_time(e[2]) * 1e3)
+        per["attn"].append(e[2].elapsed_time(e[3]) * 1e3)
+        per["step"].append(e[0].elapsed_time(e[3]) * 1e3)
+    gpu_total_us = ev[0][0].elapsed_time(ev[-1][3]) * 1e3
+    return wall, gpu_total_us, per
+
+
+def time_flushed(inp, wl, bufs, reps, stream):
+    """Per-step time with a 1 GiB write between steps (outside the events), so that no
+    step reads data left in the last-level caches by the previous one."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    times = []
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            scratch.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            decode_step(inp, wl, bufs, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+    del scratch
+    return times
+
+
+def cpu_baseline(wl, inp, b_sample=1, heads_sample=None):
+    """The fp64 oracle (scoring, dual top-p, dense masked attention) on a bounded
+    sample: batch rows [0, b_sample), all heads, full L. Scaled to one whole step."""
+    from oracle import spot_oracle as O   # test infrastructure, CPU baseline only
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    sel_q = inp["sel_q"][:b_sample].to("cpu", torch.float64).numpy()
+    sel_w = inp["sel_w"][:b_sample].to("cpu", torch.float64).numpy()
+    if inp["sel_k"].dtype == torch.uint8:
+        codes = inp["sel_k"][:b_sample].cpu().numpy()
+        scales = inp["sel_k_scale"][:b_sample].cpu().numpy()
+    else:
+        keys = inp["sel_k"][:b_sample].to("cpu", torch.float64).numpy()
+    q = inp["q"][:b_sample].to("cpu", torch.float64).numpy()
+
+    class KV:
+        def __init__(self, t):
+            self.t, self.shape = t, (b_sample,) + tuple(t.shape[1:])
+
+        def __getitem__(self, key):
+            b, g = key
+            return self.t[b, g].to("cpu", torch.float64).numpy()
+
+    t0 = time.perf_counter()
+    if inp["sel_k"].dtype == torch.uint8:
+        keys = O.dequant_int4_g32(codes, scales)
+    s = O.select_score(sel_q, sel_w, keys)
+    sels, _ = O.select_topp(s, float(np.float32(wl.p)), wl.K_min, wl.K_max, wl.n_sink, wl.n_rec)
+    O.sparse_attention(q, KV(inp["K"]), KV(inp["V"]), sels, wl.block, 1 / math.sqrt(wl.d))
+    dt = time.perf_counter() - t0
+    B = inp["q"].shape[0]
+    return {"value": dt * 1e6 * B / b_sample, "unit": "us", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"batch rows 0..{b_sample - 1} of {B} (all {wl.Hq} heads, L={wl.L}), "
+                      f"{dt:.2f} s measured, scaled x{B / b_sample:g} to one step; includes "
+                      "device-to-host copies of the sampled K/V rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_128k_b8", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flushed-reps", type=int, default=50)
+    ap.add_argument("--extra-b1", action="store_true", default=True)
+    ap.add_argument("--no-extra-b1", dest="extra_b1", action="store_false")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode step runs on one device; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    spot.load()
+    wl = W.WORKLOADS[a.workload]
+    if wl.prefill_Tq:
+        print("choose a decode workload", file=sys.stderr)
+        sys.exit(2)
+    log(f"bench: workload {wl.name}, generating inputs on the GPU")
+    inp = W.make_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    dt = inp["q"].dtype
+    bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, dt)
+    log(f"bench: warmup {a.warmup}, timing {a.steps} steps")
+    wall, gpu_total_us, per = time_steps(inp, wl, bufs, a.steps, a.warmup, stream)
+    tokens = selected_tokens(bufs.sel_idx, bufs.sel_cnt, wl.L, wl.block)
+    budget = byte_budget(wl, wl.B, tokens)
+    us_step = wall * 1e6 / a.steps
+    mean = {k: statistics.fmean(v) for k, v in per.items()}
+    med = {k: statistics.median(v) for k, v in per.items()}
+    log(f"bench: {us_step:.1f} us/step wall, event means {mean}")
+    flushed = time_flushed(inp, wl, bufs, a.flushed_reps, stream) if a.flushed_reps else []
+    attn_gbps = budget["attn"] / (mean["attn"] * 1e-6) / 1e9
+    step_gbps = budget["step"] / (us_step * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(us_step, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded; Zipf(1.1) selector masses, N(0,1) KV cache)",
+        "config": {"workload": wl.name, "batch": wl.B, "L": wl.L, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "head_dim": wl.d, "block": wl.block, "H_idx": wl.H_idx, "d_idx": wl.d_idx,
+                   "selector_cache": wl.sel_k_dtype, "p": wl.p, "K_min": wl.K_min,
+                   "K_max": wl.K_max, "n_sink": wl.n_sink, "n_rec": wl.n_rec,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "spot_sparse_attn (split-K pass + combine)",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": budget["attn"], "avg_launch_us": round(mean["attn"], 3)},
+        "step_hbm": {"algorithmic_bytes": budget["step"], "GBps": round(step_gbps, 1),
+                     "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                     "selected_tokens": tokens},
+        "per_call_us": {"mean": {k: round(v, 3) for k, v in mean.items()},
+                        "median": {k: round(v, 3) for k, v in med.items()}},
+        "gpu_event_us_per_step": round(gpu_total_us / a.steps, 3),
+        "flushed_step_us": ({"median": round(statistics.median(flushed), 3),
+                             "p10": round(float(np.percentile(flushed, 10)), 3),
+                             "p90": round(float(np.percentile(flushed, 90)), 3),
+                             "reps": len(flushed)} if flushed else None),
+        "pages_context": "paper: 3.9x FlashAttention, 1.8x Twilight end-to-end decode tok/s "
+                         "at 128K on one NVIDIA B200 (not comparable to this metric)",
+    }
+    if a.extra_b1 and wl.name == "c3_128k_b8":
+        wl1 = W.WORKLOADS["c3_128k_b1"]
+        inp1 = {k: (v[:1].contiguous() if isinstance(v, torch.Tensor) else v)
+                for k, v in inp.items()}
+        bufs1 = DecodeBuffers(1, wl1.nb, wl1.Hq, wl1.d, wl1.K_max, dt)
+        w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
+        tok1 = selected_tokens(bufs1.sel_idx, bufs1.sel_cnt, wl1.L, wl1.block)
+        b1 = byte_budget(wl1, 1, tok1)
+        u1 = w1 * 1e6 / a.steps
+        result["batch1"] = {"us_per_step": round(u1, 3),
+                            "GBps": round(b1["step"] / (u1 * 1e-6) / 1e9, 1),
+                            "per_call_us_mean": {k: round(statistics.fmean(v), 3)
+                                                 for k, v in p1.items()},
+                            "note": "batch row 0 of the same inputs"}
+        del inp1, bufs1
+    if not a.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, inp, b_sample=1)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

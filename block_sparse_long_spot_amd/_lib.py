@@ -1,0 +1,174 @@
+"""ctypes binding to libspot.so: one Python function per C entry point, same names.
+
+Argument marshalling only: every function takes torch tensors that already live on
+the GPU, checks their dtype/shape/contiguity against the C ABI's layout, and passes
+raw pointers and the current torch stream to the library. No computation happens
+here and there is no fallback: if the library or a GPU is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspot.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "spot.h")
+
+SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_DEVICE = 0, -1, -2, -3
+SPOT_F32, SPOT_BF16, SPOT_INT4_G32 = 0, 1, 2
+
+_lib = None
+
+
+class SpotError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libspot.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_long_spot_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.spot_select_score.argtypes = [vp, i, vp, vp, vp, i, vp, i, i, i, i, i, vp]
+    lib.spot_select_score.restype = i
+    lib.spot_select_topp.argtypes = [vp, vp, vp, vp, i, i, f, i, i, i, i, vp]
+    lib.spot_select_topp.restype = i
+    lib.spot_sparse_attn_workspace_bytes.argtypes = [i, i, i, i]
+    lib.spot_sparse_attn_workspace_bytes.restype = sz
+    lib.spot_sparse_attn.argtypes = [vp, vp, vp, i, vp, vp, i, vp, vp, sz, i, i, i, i, i, i, f,
+                                     vp]
+    lib.spot_sparse_attn.restype = i
+    lib.spot_prefill_select_score.argtypes = [vp, i, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i,
+                                              vp]
+    lib.spot_prefill_select_score.restype = i
+    lib.spot_prefill_attn.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, i, i, f,
+                                      vp]
+    lib.spot_prefill_attn.restype = i
+    lib.spot_status_string.argtypes = [i]
+    lib.spot_status_string.restype = ctypes.c_char_p
+    lib.spot_abi_version.argtypes = []
+    lib.spot_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def declared_symbols() -> list:
+    """Names of every function the C header declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"SPOT_API\s+[\w\s\*]+?\b(spot_\w+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return load().spot_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != SPOT_OK:
+        raise SpotError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libspot must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libspot must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPOT_F32
+    if t.dtype == torch.bfloat16:
+        return SPOT_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def spot_select_score(sel_q, sel_w, sel_k, sel_k_scale, scores, kpb: int = 1, stream=None):
+    """scores[B][nb] <- selector block scores. sel_k is [B][nb][kpb][H][d_idx] (fp32/bf16)
+    or INT4 codes uint8 [B][nb][kpb][H][d_idx/2] with sel_k_scale fp16 [..][d_idx/32]."""
+    B, H, d_idx = sel_q.shape
+    nb = scores.shape[1]
+    if sel_k.dtype == torch.uint8:
+        k_dtype = SPOT_INT4_G32
+        assert sel_k_scale is not None and sel_k_scale.dtype == torch.float16
+    else:
+        k_dtype = _dtype_code(sel_k)
+    assert scores.dtype == torch.float32 and sel_w.dtype == torch.float32
+    st = load().spot_select_score(_ptr(sel_q), _dtype_code(sel_q), _ptr(sel_w), _ptr(sel_k),
+                                  _ptr(sel_k_scale), k_dtype, _ptr(scores), B, nb, kpb, H,
+                                  d_idx, _stream(stream))
+    _check("spot_select_score", st)
+
+
+def spot_select_topp(scores, sel_idx, sel_cnt, sel_mass, p: float, K_min: int, K_max: int,
+                     n_sink: int, n_rec: int, stream=None):
+    """sel_idx[B][K_max] (ascending, -1 padded), sel_cnt[B], optional sel_mass[B]."""
+    B, nb = scores.shape
+    assert sel_idx.dtype == torch.int32 and sel_idx.shape == (B, K_max)
+    assert sel_cnt.dtype == torch.int32
+    st = load().spot_select_topp(_ptr(scores), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_mass), B,
+                                 nb, float(p), K_min, K_max, n_sink, n_rec, _stream(stream))
+    _check("spot_select_topp", st)
+
+
+def spot_sparse_attn_workspace_bytes(B: int, Hq: int, d: int, K_max: int) -> int:
+    return int(load().spot_sparse_attn_workspace_bytes(B, Hq, d, K_max))
+
+
+def spot_sparse_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, workspace, sm_scale: float,
+                     block: int = 64, stream=None):
+    """out[B][Hq][d] <- attention of q over the selected blocks of K/V [B][Hkv][L][d]."""
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    K_max = sel_idx.shape[1]
+    st = load().spot_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
+                                 _ptr(sel_idx), _ptr(sel_cnt), K_max, _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, L,
+                                 block, float(sm_scale), _stream(stream))
+    _check("spot_sparse_attn", st)
+
+
+def spot_prefill_select_score(sel_q, sel_w, sel_k, scores, q_pos0: int, block: int = 64,
+                              kpb: int = 1, stream=None):
+    """scores[B][nb_vis] <- tile block scores of the Tq queries at q_pos0.."""
+    B, Tq, H, d_idx = sel_q.shape
+    nb_cache = sel_k.shape[1]
+    st = load().spot_prefill_select_score(_ptr(sel_q), _dtype_code(sel_q), _ptr(sel_w),
+                                          _ptr(sel_k), None, _dtype_code(sel_k), _ptr(scores), B,
+                                          Tq, q_pos0, nb_cache, kpb, H, d_idx, block,
+                                          _stream(stream))
+    _check("spot_prefill_select_score", st)
+
+
+def spot_prefill_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, q_pos0: int,
+                      sm_scale: float, block: int = 64, stream=None):
+    """out[B][Hq][Tq][d] <- causal attention of the tile over the selected blocks."""
+    B, Hq, Tq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    K_max = sel_idx.shape[1]
+    st = load().spot_prefill_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
+                                  _ptr(sel_idx), _ptr(sel_cnt), K_max, _ptr(out), B, Hq, Hkv,
+                                  Tq, q_pos0, d, L, block, float(sm_scale), _stream(stream))
+    _check("spot_prefill_attn", st)
+
+
+def spot_abi_version() -> int:
+    return int(load().spot_abi_version())

@@ -1,0 +1,479 @@
+// Decode attention over the selected KV blocks (SpotAttention §2.3: the layer attends
+// only to keys in blocks of S_q, one S_q per query shared by every head).
+//
+// Split-K: the selected-block list of one (query, KV head) is cut into runs of
+// `bps` blocks; a work-group reduces one run with an online softmax for the G query
+// heads that share the KV head (GQA), and writes (m, l, acc) per head. A combine
+// kernel then merges the runs of each (query, head) in split order.
+//
+// HBM-bound (about 4 flop per byte in bf16 with G = 4). Two pass-1 kernels:
+//  * attn_partial_mfma (bf16, d in {64,128}): each wave owns whole 64-token blocks.
+//    q.K^T runs on the MFMA units (v_mfma_f32_16x16x32_bf16, the G heads padded to
+//    16 rows): every lane loads 16 contiguous bytes of a K row straight into the
+//    B-operand layout, no LDS staging and no bf16->fp32 conversion. P.V runs on the
+//    VALU: each lane owns 8 head dims of a set of tokens, reading V rows with
+//    coalesced 16-byte loads, and probabilities come through a per-wave LDS tile.
+//  * attn_partial_generic (fp32 or bf16, any supported shape): one wave per run;
+//    lane = token for q.K^T, lane = head dim for P.V.
+// Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
+#include "device_common.h"
+#include "spot_internal.h"
+
+namespace spot {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBlk = 64;  // tokens per KV block
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f(x); }
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = f_to_bf16_rne(v); }
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---------------------------------------------------------------- generic pass 1
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void attn_partial_generic(
+    const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, int K_max,
+    float* __restrict__ ws_acc, float2* __restrict__ ws_ml, int Hq, int Hkv, int L,
+    float qscale, int bps, int nsplit) {
+  constexpr int DPL = D / 64;  // head dims per lane in P.V
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int j0 = split * bps;
+  if (j0 >= cnt) return;
+  const int j1 = min(j0 + bps, cnt);
+  const int lane = threadIdx.x;
+  __shared__ float qs[G][D];
+  __shared__ float ps[kBlk][G];
+  for (int i = lane; i < G * D; i += 64) {
+    const int h = i / D, dd = i % D;
+    qs[h][dd] = to_f(q[((size_t)b * Hq + g * G + h) * D + dd]) * qscale;
+  }
+  __syncthreads();
+  float m[G], l[G], acc[G][DPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) acc[h][c] = 0.f;
+  }
+  const int nbl = (L + kBlk - 1) / kBlk;
+  const T* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
+  const T* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+  for (int j = j0; j < j1; ++j) {
+    const int blk = sel_idx[(size_t)b * K_max + j];
+    if (blk < 0 || blk >= nbl) continue;
+    const int tok = blk * kBlk + lane;
+    const bool tv = tok < L;
+    const T* kr = Kg + (size_t)(tv ? tok : L - 1) * D;
+    float z[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) z[h] = 0.f;
+#pragma unroll 4
+    for (int d0 = 0; d0 < D; d0 += 8) {
+      float kv[8];
+      load8(kr + d0, kv);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) z[h] = fmaf(qs[h][d0 + n], kv[n], z[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float zz = tv ? z[h] : -INFINITY;
+      const float mn = fmaxf(m[h], group_max<64>(zz));
+      const float alpha = exp2f(m[h] - mn);
+      const float pp = exp2f(zz - mn);
+      ps[lane][h] = pp;
+      l[h] = l[h] * alpha + group_sum<64>(pp);
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) acc[h][c] *= alpha;
+      m[h] = mn;
+    }
+    __syncthreads();
+    const int tend = min(kBlk, L - blk * kBlk);
+    for (int t = 0; t < tend; ++t) {
+      const T* vr = Vg + (size_t)(blk * kBlk + t) * D + lane * DPL;
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) {
+        const float v = to_f(vr[c]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h][c] = fmaf(ps[t][h], v, acc[h][c]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const size_t o = ((size_t)b * Hq + g * G + h) * nsplit + split;
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) ws_acc[o * D + lane * DPL + c] = acc[h][c];
+    if (lane == 0) ws_ml[o] = make_float2(m[h], l[h]);
+  }
+}
+
+// ---------------------------------------------------------------- MFMA pass 1 (bf16)
+template <int D, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_partial_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
+    const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
+    const int32_t* __restrict__ sel_cnt, int K_max, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml, int Hq, int Hkv, int L, float qscale, int bps, int nsplit) {
+  constexpr int KS = D / 32;   // MFMA k-steps over the head dim
+  constexpr int DC = D / 8;    // lanes covering one V row (8 dims each)
+  constexpr int TG = 64 / DC;  // token groups in P.V
+  constexpr int TPL = DC;      // tokens per lane per block in P.V (= 64 / TG)
+  constexpr int NG = (G + 3) / 4;  // 16-lane groups that hold real heads in S
+  static_assert(G <= 8, "at most 8 query heads per KV head");
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int j0 = split * bps;
+  if (j0 >= cnt) return;
+  const int j1 = min(j0 + bps, cnt);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;  // MFMA operand coordinates
+  const int dc = lane % DC, tg = lane / DC;   // P.V coordinates
+
+  __shared__ __attribute__((aligned(16))) float Ps[NW][kBlk][G < 4 ? 4 : G];
+  __shared__ float mm[NW][G], ll[NW][G];
+  __shared__ float accs[NW][G][D];
+
+  // A operand: row = query head of the group (zero rows beyond G), k = head dim
+  bf16x8_t qa[KS];
+  {
+    const bool hv = row < G;
+    const uint16_t* qp = q + ((size_t)b * Hq + g * G + (hv ? row : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + s * 32 + kg * 8);
+      if (!hv) v = bf16x8_t{};
+      qa[s] = v;
+    }
+  }
+
+  float mrow[4], lrow[4];  // state of heads kg*4 + r (meaningful for kg < NG)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+
+  const int nbl = (L + kBlk - 1) / kBlk;
+  const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
+  const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+
+  for (int j = j0 + wave; j < j1; j += NW) {
+    const int blk = sel_idx[(size_t)b * K_max + j];
+    if (blk < 0 || blk >= nbl) continue;
+    const int t0 = blk * kBlk;
+    bf16x8_t kb[4][KS];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int tok = min(t0 + T * 16 + row, L - 1);
+      const uint16_t* kp = Kg + (size_t)tok * D + kg * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kb[T][s] = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
+    }
+    uint4 vv[TPL];
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const int tok = min(t0 + i * TG + tg, L - 1);
+      vv[i] = *reinterpret_cast<const uint4*>(Vg + (size_t)tok * D + dc * 8);
+    }
+    // S[head][token] for the 4 tiles of 16 tokens
+    floatx4_t sa[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      floatx4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb[T][s], a, 0, 0, 0);
+      sa[T] = a;
+    }
+    float z[4][4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const bool tv = t0 + T * 16 + row < L;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[T][r] = tv ? sa[T][r] * qscale : -INFINITY;
+    }
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float bm = fmaxf(fmaxf(z[0][r], z[1][r]), fmaxf(z[2][r], z[3][r]));
+      bm = group_max<16>(bm);
+      const float mn = fmaxf(mrow[r], bm);
+      alpha[r] = exp2f(mrow[r] - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        z[T][r] = exp2f(z[T][r] - mn);
+        rs += z[T][r];
+      }
+      rs = group_sum<16>(rs);
+      lrow[r] = lrow[r] * alpha[r] + rs;
+      mrow[r] = mn;
+    }
+    // probabilities to the wave's LDS tile, [token][head]
+    if (kg < NG) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        float* dst = &Ps[wave][T * 16 + row][kg * 4];
+        if constexpr (G >= 4) {
+          *reinterpret_cast<float4*>(dst) = make_float4(z[T][0], z[T][1], z[T][2], z[T][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < G; ++r) dst[r] = z[T][r];
+        }
+      }
+    }
+    // rescale the accumulators by each head's alpha (heads live in lane groups)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = readlane_f(alpha[h & 3], (h >> 2) * 16);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] *= a;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const int tok = i * TG + tg;
+      float ph[G];
+      if constexpr (G >= 4) {
+#pragma unroll
+        for (int h4 = 0; h4 < G; h4 += 4) {
+          const float4 pv = *reinterpret_cast<const float4*>(&Ps[wave][tok][h4]);
+          ph[h4] = pv.x;
+          ph[h4 + 1] = pv.y;
+          ph[h4 + 2] = pv.z;
+          ph[h4 + 3] = pv.w;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) ph[h] = Ps[wave][tok][h];
+      }
+      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[2 * c] = bf16_lo(w4[c]);
+        v[2 * c + 1] = bf16_hi(w4[c]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(ph[h], v[c], acc[h][c]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // sum the token groups: lanes dc, dc + DC, ... hold the same head dims
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float x = acc[h][c];
+#pragma unroll
+      for (int o = DC; o < 64; o <<= 1) x += shfl_xor_f(x, o);
+      acc[h][c] = x;
+    }
+  if (lane < DC) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) accs[wave][h][dc * 8 + c] = acc[h][c];
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mh = readlane_f(mrow[h & 3], (h >> 2) * 16);
+    const float lh = readlane_f(lrow[h & 3], (h >> 2) * 16);
+    if (lane == 0) {
+      mm[wave][h] = mh;
+      ll[wave][h] = lh;
+    }
+  }
+  __syncthreads();
+  // merge the waves of this work-group and write the run's partial result
+  for (int o = threadIdx.x; o < G * D; o += NW * 64) {
+    const int h = o / D, dd = o % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w][h]);
+    float ls = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sc = mm[w][h] == -INFINITY ? 0.f : exp2f(mm[w][h] - M);
+      ls += sc * ll[w][h];
+      a += sc * accs[w][h][dd];
+    }
+    const size_t idx = ((size_t)b * Hq + g * G + h) * nsplit + split;
+    ws_acc[idx * D + dd] = a;
+    if (dd == 0) ws_ml[idx] = make_float2(M, ls);
+  }
+}
+
+// ---------------------------------------------------------------- pass 2: combine
+template <typename T, int D>
+__global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ ws_acc,
+                                                  const float2* __restrict__ ws_ml,
+                                                  const int32_t* __restrict__ sel_cnt,
+                                                  int K_max, T* __restrict__ out, int Hq,
+                                                  int bps, int nsplit) {
+  const int rowi = blockIdx.x;  // b * Hq + hq
+  const int b = rowi / Hq;
+  const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int ns = (cnt + bps - 1) / bps;
+  const float2* ml = ws_ml + (size_t)rowi * nsplit;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
+  float res = 0.f;
+  if (M != -INFINITY) {
+    float ls = 0.f, a = 0.f;
+    const float* ap = ws_acc + (size_t)rowi * nsplit * D + threadIdx.x;
+    for (int s = 0; s < ns; ++s) {
+      const float2 v = ml[s];
+      const float w = v.x == -INFINITY ? 0.f : exp2f(v.x - M);
+      ls += w * v.y;
+      a += w * ap[(size_t)s * D];
+    }
+    res = a / ls;
+  }
+  store_out(out + (size_t)rowi * D + threadIdx.x, res);
+}
+
+template <typename T, int D, int G>
+hipError_t launch_generic(const void* q, const void* k, const void* v, const int32_t* sel_idx,
+                          const int32_t* sel_cnt, int K_max, float* ws_acc, float2* ws_ml,
+                          int B, int Hq, int Hkv, int L, float qscale, AttnSplit sp,
+                          hipStream_t stream) {
+  dim3 grid(sp.nsplit, Hkv, B);
+  hipLaunchKernelGGL((attn_partial_generic<T, D, G>), grid, dim3(64), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(k),
+                     static_cast<const T*>(v), sel_idx, sel_cnt, K_max, ws_acc, ws_ml, Hq, Hkv,
+                     L, qscale, sp.blocks_per_split, sp.nsplit);
+  return hipGetLastError();
+}
+
+constexpr int kMfmaWaves = 4;
+
+template <int D, int G>
+hipError_t launch_mfma(const void* q, const void* k, const void* v, const int32_t* sel_idx,
+                       const int32_t* sel_cnt, int K_max, float* ws_acc, float2* ws_ml, int B,
+                       int Hq, int Hkv, int L, float qscale, AttnSplit sp, hipStream_t stream) {
+  dim3 grid(sp.nsplit, Hkv, B);
+  hipLaunchKernelGGL((attn_partial_mfma<D, G, kMfmaWaves>), grid, dim3(kMfmaWaves * 64), 0,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws_acc, ws_ml,
+                     Hq, Hkv, L, qscale, sp.blocks_per_split, sp.nsplit);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
+                    const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, float* ws_acc,
+                    float2* ws_ml, int B, int Hq, int Hkv, int L, float qscale, AttnSplit sp,
+                    hipStream_t stream) {
+  const int G = Hq / Hkv;
+#define SPOT_ARGS q, k, v, sel_idx, sel_cnt, K_max, ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (fast) {
+      switch (G) {
+        case 1: return launch_mfma<D, 1>(SPOT_ARGS);
+        case 2: return launch_mfma<D, 2>(SPOT_ARGS);
+        case 4: return launch_mfma<D, 4>(SPOT_ARGS);
+        default: return launch_mfma<D, 8>(SPOT_ARGS);
+      }
+    }
+  }
+  switch (G) {
+    case 1: return launch_generic<T, D, 1>(SPOT_ARGS);
+    case 2: return launch_generic<T, D, 2>(SPOT_ARGS);
+    case 4: return launch_generic<T, D, 4>(SPOT_ARGS);
+    default: return launch_generic<T, D, 8>(SPOT_ARGS);
+  }
+#undef SPOT_ARGS
+}
+
+}  // namespace
+
+AttnSplit attn_split_plan(int B, int Hkv, int K_max, bool bf16_fast_path) {
+  AttnSplit sp;
+  const long units = (long)B * Hkv;
+  if (!bf16_fast_path) {
+    sp.blocks_per_split = 4;
+  } else {
+    // the largest run length that still gives >= 1024 work-groups, within [4, 64]
+    int bps = 4;
+    for (int c = 64; c >= 4; c >>= 1) {
+      if (units * ((K_max + c - 1) / c) >= 1024) {
+        bps = c;
+        break;
+      }
+    }
+    sp.blocks_per_split = bps;
+  }
+  sp.nsplit = (K_max + sp.blocks_per_split - 1) / sp.blocks_per_split;
+  return sp;
+}
+
+hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                              bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,
+                              int K_max, void* out, void* workspace, int B, int Hq, int Hkv,
+                              int d, int L, float sm_scale, hipStream_t stream) {
+  const bool fast = bf16;
+  const AttnSplit sp = attn_split_plan(B, Hkv, K_max, fast);
+  float* ws_acc = static_cast<float*>(workspace);
+  float2* ws_ml = reinterpret_cast<float2*>(ws_acc + (size_t)B * Hq * sp.nsplit * d);
+  const float qscale = sm_scale * kLog2e;
+  hipError_t e;
+  if (bf16) {
+    e = d == 64 ? launch_d<uint16_t, 64>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
+                                         ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream)
+                : launch_d<uint16_t, 128>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
+                                          ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream);
+  } else {
+    e = d == 64 ? launch_d<float, 64>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max,
+                                      ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream)
+                : launch_d<float, 128>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max,
+                                       ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream);
+  }
+  if (e != hipSuccess) return e;
+  dim3 grid(B * Hq);
+  if (bf16) {
+    if (d == 64)
+      hipLaunchKernelGGL((attn_combine<uint16_t, 64>), grid, dim3(64), 0, stream, ws_acc, ws_ml,
+                         sel_cnt, K_max, static_cast<uint16_t*>(out), Hq, sp.blocks_per_split,
+                         sp.nsplit);
+    else
+      hipLaunchKernelGGL((attn_combine<uint16_t, 128>), grid, dim3(128), 0, stream, ws_acc,
+                         ws_ml, sel_cnt, K_max, static_cast<uint16_t*>(out), Hq,
+                         sp.blocks_per_split, sp.nsplit);
+  } else {
+    if (d == 64)
+      hipLaunchKernelGGL((attn_combine<float, 64>), grid, dim3(64), 0, stream, ws_acc, ws_ml,
+                         sel_cnt, K_max, static_cast<float*>(out), Hq, sp.blocks_per_split,
+                         sp.nsplit);
+    else
+      hipLaunchKernelGGL((attn_combine<float, 128>), grid, dim3(128), 0, stream, ws_acc, ws_ml,
+                         sel_cnt, K_max, static_cast<float*>(out), Hq, sp.blocks_per_split,
+                         sp.nsplit);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace spot

@@ -1,0 +1,164 @@
+// C ABI of libspot: argument validation and dispatch to the HIP launchers.
+// Every check happens on the host before anything is enqueued; no HIP call is made
+// for an invalid or unsupported argument set.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/spot.h"
+#include "spot_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+int from_hip(hipError_t e) {
+  if (e == hipErrorNotSupported) return SPOT_ERR_UNSUPPORTED;
+  return e == hipSuccess ? SPOT_OK : SPOT_ERR_DEVICE;
+}
+
+constexpr int kMaxGrid = 65535;  // grid.y / grid.z limit used by the launchers
+
+// Common validation of a selector-cache description; returns SPOT_OK or an error.
+int check_selector(const void* sel_q, int q_dtype, const float* sel_w, const void* sel_k,
+                   const void* sel_k_scale, int k_dtype, int H_idx, int d_idx, int kpb) {
+  if (!sel_q || !sel_w || !sel_k) return SPOT_ERR_INVALID;
+  if (q_dtype != SPOT_F32 && q_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
+  if (k_dtype != SPOT_F32 && k_dtype != SPOT_BF16 && k_dtype != SPOT_INT4_G32)
+    return SPOT_ERR_INVALID;
+  if (H_idx <= 0 || d_idx <= 0 || kpb <= 0) return SPOT_ERR_INVALID;
+  if (!aligned(sel_q, 16) || !aligned(sel_w, 4) || !aligned(sel_k, 16)) return SPOT_ERR_INVALID;
+  if (k_dtype == SPOT_INT4_G32) {
+    if (!sel_k_scale || !aligned(sel_k_scale, 2)) return SPOT_ERR_INVALID;
+    if (d_idx % 32 != 0) return SPOT_ERR_INVALID;
+  } else if (sel_k_scale) {
+    return SPOT_ERR_INVALID;
+  }
+  if (d_idx != 32 && d_idx != 64 && d_idx != 128) return SPOT_ERR_UNSUPPORTED;
+  const int ch = k_dtype == SPOT_INT4_G32 ? 32 : 8;
+  const int lpr = H_idx * (d_idx / ch);
+  if (!pow2(H_idx) || lpr > 64) return SPOT_ERR_UNSUPPORTED;
+  return SPOT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spot_abi_version(void) { return 1; }
+
+const char* spot_status_string(int status) {
+  switch (status) {
+    case SPOT_OK: return "SPOT_OK";
+    case SPOT_ERR_INVALID: return "SPOT_ERR_INVALID: invalid argument";
+    case SPOT_ERR_UNSUPPORTED: return "SPOT_ERR_UNSUPPORTED: no kernel for this combination";
+    case SPOT_ERR_DEVICE: return "SPOT_ERR_DEVICE: the HIP runtime refused a launch";
+    default: return "unknown spot status";
+  }
+}
+
+int spot_select_score(const void* sel_q, int q_dtype, const float* sel_w, const void* sel_k,
+                      const void* sel_k_scale, int k_dtype, float* scores, int B, int nb,
+                      int kpb, int H_idx, int d_idx, void* stream) {
+  if (B <= 0 || nb <= 0 || !scores || !aligned(scores, 4)) return SPOT_ERR_INVALID;
+  const int c = check_selector(sel_q, q_dtype, sel_w, sel_k, sel_k_scale, k_dtype, H_idx,
+                               d_idx, kpb);
+  if (c != SPOT_OK) return c;
+  if (B > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_select_score(sel_q, q_dtype == SPOT_BF16, sel_w, sel_k,
+                                            sel_k_scale, k_dtype, scores, B, nb, kpb, H_idx,
+                                            d_idx, as_stream(stream)));
+}
+
+int spot_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt, float* sel_mass,
+                     int B, int nb, float p, int K_min, int K_max, int n_sink, int n_rec,
+                     void* stream) {
+  if (!scores || !sel_idx || !sel_cnt) return SPOT_ERR_INVALID;
+  if (!aligned(scores, 4) || !aligned(sel_idx, 4) || !aligned(sel_cnt, 4) ||
+      (sel_mass && !aligned(sel_mass, 4)))
+    return SPOT_ERR_INVALID;
+  if (B <= 0 || nb <= 0 || K_max <= 0) return SPOT_ERR_INVALID;
+  if (!isfinite(p) || n_sink < 0 || n_rec < 0 || K_min < 0) return SPOT_ERR_INVALID;
+  const int rs = n_sink < nb ? n_sink : nb;
+  const int rr = n_rec < nb ? n_rec : nb;
+  const int r = rs + rr < nb ? rs + rr : nb;
+  if (K_max < r) return SPOT_ERR_INVALID;
+  if (nb > 16384) return SPOT_ERR_UNSUPPORTED;
+  if (B > 2147483647 / 2) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_select_topp(scores, sel_idx, sel_cnt, sel_mass, B, nb, p, K_min,
+                                           K_max, n_sink, n_rec, as_stream(stream)));
+}
+
+size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || K_max <= 0) return 0;
+  // at most K_max runs per (query, head): fp32 accumulators plus (m, l)
+  return (size_t)B * Hq * K_max * ((size_t)d + 2) * sizeof(float);
+}
+
+int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, int kv_dtype,
+                     const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, void* out,
+                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
+                     int L, int block, float sm_scale, void* stream) {
+  if (!q || !k_cache || !v_cache || !sel_idx || !sel_cnt || !out || !workspace)
+    return SPOT_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(sel_idx, 4) || !aligned(sel_cnt, 4) || !aligned(workspace, 256))
+    return SPOT_ERR_INVALID;
+  if (kv_dtype != SPOT_F32 && kv_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || L <= 0 || block <= 0 || K_max <= 0)
+    return SPOT_ERR_INVALID;
+  if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
+  if (workspace_bytes < spot_sparse_attn_workspace_bytes(B, Hq, d, K_max))
+    return SPOT_ERR_INVALID;
+  const int G = Hq / Hkv;
+  if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;
+  if (block != 64) return SPOT_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
+  if (B > kMaxGrid || Hkv > kMaxGrid || (long)B * Hq > 2147483647L) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_sparse_attn(q, k_cache, v_cache, kv_dtype == SPOT_BF16, sel_idx,
+                                           sel_cnt, K_max, out, workspace, B, Hq, Hkv, d, L,
+                                           sm_scale, as_stream(stream)));
+}
+
+int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,
+                              const void* sel_k, const void* sel_k_scale, int k_dtype,
+                              float* scores, int B, int Tq, int q_pos0, int nb_cache, int kpb,
+                              int H_idx, int d_idx, int block, void* stream) {
+  if (B <= 0 || Tq <= 0 || q_pos0 < 0 || nb_cache <= 0 || block <= 0) return SPOT_ERR_INVALID;
+  if (!scores || !aligned(scores, 4)) return SPOT_ERR_INVALID;
+  const int c = check_selector(sel_q, q_dtype, sel_w, sel_k, sel_k_scale, k_dtype, H_idx,
+                               d_idx, kpb);
+  if (c != SPOT_OK) return c;
+  const long nb_vis = ((long)q_pos0 + Tq + block - 1) / block;
+  if (nb_vis > nb_cache) return SPOT_ERR_INVALID;
+  if (q_dtype != SPOT_BF16 || k_dtype != SPOT_BF16) return SPOT_ERR_UNSUPPORTED;
+  if (Tq > 128 || B > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_prefill_select_score(sel_q, sel_w, sel_k, scores, B, Tq, q_pos0,
+                                                    nb_cache, (int)nb_vis, kpb, H_idx, d_idx,
+                                                    block, as_stream(stream)));
+}
+
+int spot_prefill_attn(const void* q, const void* k_cache, const void* v_cache, int kv_dtype,
+                      const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, void* out,
+                      int B, int Hq, int Hkv, int Tq, int q_pos0, int d, int L, int block,
+                      float sm_scale, void* stream) {
+  if (!q || !k_cache || !v_cache || !sel_idx || !sel_cnt || !out) return SPOT_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(sel_idx, 4) || !aligned(sel_cnt, 4))
+    return SPOT_ERR_INVALID;
+  if (kv_dtype != SPOT_F32 && kv_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || q_pos0 < 0 || d <= 0 || L <= 0 ||
+      block <= 0 || K_max <= 0)
+    return SPOT_ERR_INVALID;
+  if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
+  if ((long)q_pos0 + Tq > L) return SPOT_ERR_INVALID;
+  const int G = Hq / Hkv;
+  if (kv_dtype != SPOT_BF16 || d != 128 || block != 64 || Tq > 128) return SPOT_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
+  if (B > kMaxGrid || Hq > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_prefill_attn(q, k_cache, v_cache, sel_idx, sel_cnt, K_max, out, B,
+                                            Hq, Hkv, Tq, q_pos0, d, L, sm_scale,
+                                            as_stream(stream)));
+}
+
+}  // extern "C"

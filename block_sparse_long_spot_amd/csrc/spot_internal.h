@@ -1,0 +1,45 @@
+// Host-side launchers implemented by the kernel translation units and called by the
+// C ABI after argument validation. Each returns hipSuccess or the launch error.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spot {
+
+// Key storage kinds for the selector cache.
+enum KeyKind { kKeyF32 = 0, kKeyBF16 = 1, kKeyInt4 = 2 };
+
+hipError_t launch_select_score(const void* sel_q, bool q_bf16, const float* sel_w,
+                               const void* sel_k, const void* sel_k_scale, int key_kind,
+                               float* scores, int B, int nb, int kpb, int H, int d_idx,
+                               hipStream_t stream);
+
+hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                              float* sel_mass, int B, int nb, float p, int K_min, int K_max,
+                              int n_sink, int n_rec, hipStream_t stream);
+
+// Split geometry of the decode attention: blocks per split (a power of two) and the
+// number of splits; a pure function of the sizes so the workspace bound holds.
+struct AttnSplit {
+  int blocks_per_split;
+  int nsplit;
+};
+AttnSplit attn_split_plan(int B, int Hkv, int K_max, bool bf16_fast_path);
+
+hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                              bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,
+                              int K_max, void* out, void* workspace, int B, int Hq, int Hkv,
+                              int d, int L, float sm_scale, hipStream_t stream);
+
+hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
+                                       const void* sel_k, float* scores, int B, int Tq,
+                                       int q_pos0, int nb_cache, int nb_vis, int kpb, int H,
+                                       int d_idx, int block, hipStream_t stream);
+
+hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* sel_idx, const int32_t* sel_cnt, int K_max,
+                               void* out, int B, int Hq, int Hkv, int Tq, int q_pos0, int d,
+                               int L, float sm_scale, hipStream_t stream);
+
+}  // namespace spot

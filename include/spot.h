@@ -1,0 +1,193 @@
+/*
+ * spot.h — C ABI of libspot: the SpotAttention decode hot path on gfx950 (MI355X).
+ *
+ * Source of the method: "SpotAttention: Plug-In Block-Sparse Routing for Pretrained
+ * Long-Context Transformers" (Ahmad and Yun, KAIST). Section, equation and table
+ * numbers below are that paper's.
+ *
+ * One decode step of one attention layer is three calls on one stream:
+ *   spot_select_score  -> a score for every past KV block      (§2.1, §2.3)
+ *   spot_select_topp   -> the per-query block set S_q           (§2.3, Eq. 7-8)
+ *   spot_sparse_attn   -> exact softmax attention over S_q      (§2.3)
+ * plus a prefill-tile variant (spot_prefill_select_score, spot_prefill_attn) for a
+ * tile of consecutive queries with a causal mask (§2.1 tile scoring; §6 notes the
+ * selector runs in the prefill regime).
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is DEVICE memory owned by the caller (allocated and freed
+ *    by the caller; the library keeps no pointer after the call returns). The library
+ *    allocates nothing, keeps no global state and never synchronises the device.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream. Every
+ *    call validates its arguments on the host, then enqueues its kernels on `stream`
+ *    and returns; results are ready when the stream reaches that point.
+ *  - Arrays are dense and row-major with the innermost index last, as written.
+ *  - Return value: SPOT_OK, or
+ *      SPOT_ERR_INVALID      bad argument (null or misaligned pointer, size <= 0, values
+ *                            out of range); nothing is enqueued;
+ *      SPOT_ERR_UNSUPPORTED  a valid combination this build has no kernel for; nothing
+ *                            is enqueued;
+ *      SPOT_ERR_DEVICE       the HIP runtime refused a launch. A fault inside a kernel
+ *                            surfaces at the caller's next synchronisation instead.
+ *  - Counts named n_sink, n_rec, K_min, K_max are counts of BLOCKS.
+ *  - NaN or infinite scores and inputs are not supported.
+ */
+#ifndef SPOT_H
+#define SPOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPOT_API __attribute__((visibility("default")))
+
+enum spot_status {
+  SPOT_OK = 0,
+  SPOT_ERR_INVALID = -1,
+  SPOT_ERR_UNSUPPORTED = -2,
+  SPOT_ERR_DEVICE = -3
+};
+
+enum spot_dtype {
+  SPOT_F32 = 0,      /* IEEE binary32 */
+  SPOT_BF16 = 1,     /* bfloat16 */
+  SPOT_INT4_G32 = 2  /* selector keys only: 4-bit two's-complement codes, two per byte
+                        (even element in the low nibble), plus one IEEE binary16 scale
+                        per 32 consecutive elements of d_idx: value = code * scale.
+                        4.5 bits per element (§5.3 and Appendix G, Table 9). */
+};
+
+/*
+ * spot_select_score — selector block scores (§2.1 score formula, §2.3 block maximum).
+ *
+ *   scores[b][blk] = max_{j < kpb} sum_{h < H_idx} sel_w[b][h] * ReLU( sum_i
+ *                    sel_q[b][h][i] * sel_k[b][blk][j][h][i] )
+ *
+ * No 1/sqrt(d_idx) factor (the paper's formula has none; temperature 1, Table 3).
+ *   sel_q        [B][H_idx][d_idx], q_dtype SPOT_F32 or SPOT_BF16; 16-byte aligned.
+ *   sel_w        [B][H_idx] fp32 mixing weights (any sign); 4-byte aligned.
+ *   sel_k        k_dtype SPOT_F32 / SPOT_BF16: [B][nb][kpb][H_idx][d_idx];
+ *                k_dtype SPOT_INT4_G32: codes uint8 [B][nb][kpb][H_idx][d_idx/2];
+ *                16-byte aligned.
+ *   sel_k_scale  SPOT_INT4_G32 only: fp16 [B][nb][kpb][H_idx][d_idx/32], 2-byte
+ *                aligned; must be NULL for the other key types.
+ *   scores       out fp32 [B][nb]; 4-byte aligned.
+ *   kpb          selector keys per block (1 = one pooled key per block; the paper's
+ *                per-token form is kpb = block size).
+ * Supported: d_idx in {32, 64, 128}; H_idx a power of two with H_idx*d_idx/8 <= 64
+ * (fp32/bf16 keys) or H_idx*d_idx/32 <= 64 (INT4 keys).
+ */
+SPOT_API int spot_select_score(const void* sel_q, int q_dtype, const float* sel_w,
+                               const void* sel_k, const void* sel_k_scale, int k_dtype,
+                               float* scores, int B, int nb, int kpb, int H_idx, int d_idx,
+                               void* stream);
+
+/*
+ * spot_select_topp — dual top-p block selection (§2.3, Eq. 7 and Eq. 8).
+ *
+ * Per query row b of scores [B][nb]:
+ *   R     = {0 .. n_sink-1} u {nb-n_rec .. nb-1}, clipped to [0, nb); r = |R|;
+ *   B_res = the other blocks. p~ = softmax over B_res of the scores (Eq. 7);
+ *   order B_res by score descending, ties by lower block index (-0.0 == +0.0);
+ *   k_p   = length of the shortest prefix whose cumulative p~ mass is >= p
+ *           (p >= 1: all of B_res; p <= 0: none);
+ *   k     = min(max(k_p, K_min - r, 0), K_max - r, |B_res|)   (|S| in [K_min, K_max]);
+ *   S     = R u (first k of the order), written in ascending block order.
+ * If B_res is empty, S is every block.
+ *   scores   fp32 [B][nb]; 4-byte aligned.
+ *   sel_idx  out int32 [B][K_max]: S ascending, then -1 up to K_max; 4-byte aligned.
+ *   sel_cnt  out int32 [B]: |S|.
+ *   sel_mass optional out fp32 [B]: p~ mass of the k chosen residual blocks (NULL to
+ *            skip). 0 when k = 0 or B_res is empty.
+ * Errors: SPOT_ERR_INVALID when p is not finite, n_sink/n_rec/K_min < 0, or
+ * K_max < r (the reserved set would not fit). Supported: 1 <= nb <= 16384.
+ * Masses are accumulated exactly in 2^-38 fixed point from double-precision
+ * exponentials, so the result does not depend on thread scheduling.
+ */
+SPOT_API int spot_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                              float* sel_mass, int B, int nb, float p, int K_min, int K_max,
+                              int n_sink, int n_rec, void* stream);
+
+/*
+ * spot_sparse_attn_workspace_bytes — size of the workspace spot_sparse_attn needs for
+ * these sizes (split-K partial results). Returns 0 for non-positive sizes.
+ */
+SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max);
+
+/*
+ * spot_sparse_attn — decode attention over the selected blocks only (§2.3: the layer
+ * attends only to keys in blocks of S_q; one S_q per query, shared by all heads).
+ *
+ * For query b and head hq (KV head g = hq / (Hq/Hkv)):
+ *   out[b][hq] = sum_t softmax_t(sm_scale * q[b][hq] . K[b][g][t]) V[b][g][t]
+ * over the tokens t < L whose block t / block is one of sel_idx[b][0 .. sel_cnt[b]-1].
+ * Entries outside [0, ceil(L/block)) are ignored; entries must not repeat. A row with
+ * no valid entry gets a zero output.
+ *   q            [B][Hq][d]; K and V [B][Hkv][L][d]; out [B][Hq][d]; all of kv_dtype
+ *                (SPOT_F32 or SPOT_BF16; bf16 output is rounded to nearest even);
+ *                16-byte aligned.
+ *   sel_idx      int32 [B][K_max], sel_cnt int32 [B] (as written by spot_select_topp).
+ *   workspace    device scratch of at least spot_sparse_attn_workspace_bytes(B, Hq, d,
+ *                K_max) bytes, 256-byte aligned; contents on entry do not matter.
+ * Split-K: each work-group reduces a run of selected blocks of one (b, KV head) with an
+ * online softmax; a second kernel merges the runs in a fixed order (deterministic).
+ * Supported: d in {64, 128}; block == 64; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
+ */
+SPOT_API int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                              int kv_dtype, const int32_t* sel_idx, const int32_t* sel_cnt,
+                              int K_max, void* out, void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int d, int L, int block,
+                              float sm_scale, void* stream);
+
+/*
+ * spot_prefill_select_score — tile block scores for a prefill tile (§2.1: one score
+ * per query-block x key-block tile; §2.3 block maximum).
+ *
+ * The tile holds Tq consecutive queries at positions q_pos0 .. q_pos0+Tq-1. Block blk
+ * is visible to query i when blk*block <= q_pos0 + i. With nb_vis =
+ * ceil((q_pos0+Tq)/block):
+ *   scores[b][blk] = max over the tile's queries i that see blk of
+ *                    max_{j<kpb} sum_h sel_w[b][i][h] * ReLU(sel_q[b][i][h] . sel_k[b][blk][j][h])
+ * for blk < nb_vis. Computed as one matrix product per selector head on the MFMA units.
+ *   sel_q   [B][Tq][H_idx][d_idx] (q_dtype), sel_w fp32 [B][Tq][H_idx];
+ *   sel_k   [B][nb_cache][kpb][H_idx][d_idx] (k_dtype SPOT_F32 or SPOT_BF16; 16-byte
+ *           aligned), sel_k_scale must be NULL;
+ *   scores  out fp32 [B][nb_vis] (row stride nb_vis).
+ * Errors: SPOT_ERR_INVALID when nb_vis > nb_cache or q_pos0 < 0.
+ * Supported: d_idx in {32, 64, 128}; bf16 queries and keys; 1 <= Tq <= 128.
+ */
+SPOT_API int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,
+                                       const void* sel_k, const void* sel_k_scale,
+                                       int k_dtype, float* scores, int B, int Tq,
+                                       int q_pos0, int nb_cache, int kpb, int H_idx,
+                                       int d_idx, int block, void* stream);
+
+/*
+ * spot_prefill_attn — causal block-sparse attention for a prefill tile.
+ *
+ * Query i of the tile (position q_pos0 + i) attends to the tokens t <= q_pos0 + i,
+ * t < L, whose block is in sel_idx[b][0 .. sel_cnt[b]-1] (the same set for the whole
+ * tile and every head). Rows with no visible selected token get zeros.
+ *   q    [B][Hq][Tq][d]; K, V [B][Hkv][L][d]; out [B][Hq][Tq][d]; kv_dtype SPOT_BF16;
+ *        16-byte aligned.
+ * Supported: d == 128, block == 64, 1 <= Tq <= 128, Hq/Hkv in {1, 2, 4, 8}.
+ */
+SPOT_API int spot_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
+                               int kv_dtype, const int32_t* sel_idx, const int32_t* sel_cnt,
+                               int K_max, void* out, int B, int Hq, int Hkv, int Tq,
+                               int q_pos0, int d, int L, int block, float sm_scale,
+                               void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+SPOT_API const char* spot_status_string(int status);
+
+/* ABI version of this library (incremented on any incompatible change). */
+SPOT_API int spot_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPOT_H */

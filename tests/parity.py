@@ -1,0 +1,141 @@
+"""Comparison rules shared by the GPU parity tests (the HIP path against the oracle).
+
+Tolerances:
+  scores   |g - r| <= 1e-5 * max(|r|, A, 1e-3 * max_row |r|), A = sum_h |w_h| sum_i |q_i k_i|
+  top-p    identical fp32 scores on both sides: the sets are equal, except that the
+           nucleus may differ by one block when a cumulative mass at the cut lies
+           within 1e-5 of p;
+  end-to-end selection (each side on its own scores): reserved blocks present; every
+           residual block scoring above tau + delta chosen, none below tau' - delta,
+           where tau / tau' are the oracle's last chosen / first unchosen score and
+           delta = 1e-5 max(|tau|, |tau'|); sizes equal, or one apart near the cut;
+  outputs  recomputed by the oracle on the GPU's own set: fp32 rows within
+           1e-5 * max |row|, bf16 within 2e-2 absolute.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import spot_oracle as O
+
+MASS_TOL = 1e-5
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def decoded_keys(inp) -> np.ndarray:
+    k = inp["sel_k"]
+    if k.dtype == torch.uint8:
+        return O.dequant_int4_g32(k.cpu().numpy(), inp["sel_k_scale"].cpu().numpy())
+    return np64(k)
+
+
+def score_magnitude(sel_q, sel_w, keys) -> np.ndarray:
+    """max_j sum_h |w_h| sum_i |q_hi k_hi|: the size of the terms a block score adds up.
+    The rounding error of an fp32 evaluation is bounded by a small multiple of
+    (d_idx + H_idx) * 2^-24 times this, so it sets the scale of the score tolerance."""
+    q = np.abs(np.asarray(sel_q, np.float64))
+    w = np.abs(np.asarray(sel_w, np.float64))
+    k = np.abs(np.asarray(keys, np.float64))
+    return (w[:, None, None, :] * np.einsum("bhi,bnjhi->bnjh", q, k)).sum(-1).max(-1)
+
+
+def assert_scores_close(g: np.ndarray, r: np.ndarray, a: np.ndarray = None):
+    """|g - r| <= 1e-5 * max(|r|, A, 1e-3 max_row |r|) with A = score_magnitude."""
+    g = np.asarray(g, np.float64)
+    scale = np.maximum(np.abs(r), 1e-3 * np.abs(r).max(axis=-1, keepdims=True))
+    if a is not None:
+        scale = np.maximum(scale, a)
+    bad = np.abs(g - r) > 1e-5 * scale
+    assert not bad.any(), (f"{bad.sum()} scores off; worst at {np.argwhere(bad)[:5].tolist()}: "
+                           f"gpu {g[bad][:5]} oracle {r[bad][:5]}")
+
+
+def gpu_sets(sel_idx: torch.Tensor, sel_cnt: torch.Tensor):
+    idx = sel_idx.cpu().numpy()
+    cnt = sel_cnt.cpu().numpy()
+    out = []
+    for b in range(idx.shape[0]):
+        row = idx[b]
+        c = int(cnt[b])
+        assert 0 <= c <= row.shape[0]
+        s = row[:c].tolist()
+        assert s == sorted(set(s)), f"row {b}: not ascending / repeated: {s[:20]}"
+        assert (row[c:] == -1).all(), f"row {b}: padding is not -1"
+        out.append(s)
+    return out
+
+
+def _near_cut(info, p):
+    """True when a cumulative residual mass next to the nucleus cut is within
+    MASS_TOL of p, so that rounding may move the cut by one block."""
+    if "cum" not in info or not (0.0 < p < 1.0):
+        return False
+    cum = info["cum"]
+    kp = info["k_p"]
+    near = False
+    for j in (kp - 2, kp - 1, kp):
+        if 0 <= j < len(cum) and abs(cum[j] - p) <= MASS_TOL:
+            near = True
+    return near
+
+
+def assert_topp_unit(gset, scores_row, p, K_min, K_max, n_sink, n_rec, tag=""):
+    """Both sides ran on identical fp32 scores."""
+    sel, info = O.select_topp_row(np.asarray(scores_row, np.float64), p, K_min, K_max,
+                                  n_sink, n_rec)
+    if gset == sel:
+        return
+    reserved = set(O.reserved_set(len(scores_row), n_sink, n_rec))
+    assert reserved <= set(gset), f"{tag}: reserved blocks missing"
+    kg = len(set(gset) - reserved)
+    assert abs(kg - info["k"]) == 1 and _near_cut(info, p), (
+        f"{tag}: gpu |S|={len(gset)} oracle |S|={len(sel)} k_p={info['k_p']} "
+        f"diff={sorted(set(gset) ^ set(sel))[:10]}")
+    assert set(gset) - reserved == set(info["order"][:kg].tolist()), f"{tag}: wrong order"
+
+
+def assert_selection_e2e(gset, s_oracle_row, p, K_min, K_max, n_sink, n_rec, tag=""):
+    """Each side ran on its own scores (GPU fp32, oracle fp64)."""
+    s = np.asarray(s_oracle_row, np.float64)
+    sel, info = O.select_topp_row(s, p, K_min, K_max, n_sink, n_rec)
+    if gset == sel:
+        return
+    nb = len(s)
+    reserved = set(O.reserved_set(nb, n_sink, n_rec))
+    G = set(gset)
+    assert reserved <= G, f"{tag}: reserved blocks missing"
+    k = info["k"]
+    srt = info.get("sorted_scores")
+    if srt is None:
+        raise AssertionError(f"{tag}: sets differ with an empty residual")
+    tau = srt[k - 1] if k > 0 else np.inf
+    tau2 = srt[k] if k < len(srt) else -np.inf
+    fin = [abs(x) for x in (tau, tau2) if np.isfinite(x)]
+    delta = 1e-5 * max(fin) if fin else 0.0
+    for blk in range(nb):
+        if blk in reserved:
+            continue
+        if s[blk] > tau + delta:
+            assert blk in G, f"{tag}: block {blk} (score {s[blk]}) above the cut is missing"
+        if s[blk] < tau2 - delta:
+            assert blk not in G, f"{tag}: block {blk} (score {s[blk]}) below the cut is chosen"
+    kg = len(G - reserved)
+    if kg != k:
+        assert abs(kg - k) == 1 and _near_cut(info, p), (
+            f"{tag}: gpu k={kg} oracle k={k} k_p={info['k_p']}, not near the cut")
+
+
+def assert_out_close(g: np.ndarray, r: np.ndarray, dtype: torch.dtype, tag=""):
+    g = np.asarray(g, np.float64)
+    if dtype == torch.float32:
+        rowmax = np.abs(r).max(axis=-1, keepdims=True)
+        err = np.abs(g - r)
+        bad = err > 1e-5 * np.maximum(rowmax, 1e-30)
+        assert not bad.any(), f"{tag}: worst rel err {(err / np.maximum(rowmax, 1e-30)).max()}"
+    else:
+        err = np.abs(g - r).max()
+        assert err <= 2e-2, f"{tag}: max abs err {err}"

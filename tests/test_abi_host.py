@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol the header declares and nothing else under the spot_ prefix, and rejects bad
+arguments before anything reaches the device. Only argument sets that fail
+validation are passed here, so no kernel is ever launched."""
+import ctypes
+import subprocess
+
+import pytest
+
+from block_sparse_long_spot_amd import _lib
+
+INVALID, UNSUPPORTED = _lib.SPOT_ERR_INVALID, _lib.SPOT_ERR_UNSUPPORTED
+F32, BF16, INT4 = _lib.SPOT_F32, _lib.SPOT_BF16, _lib.SPOT_INT4_G32
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def fake(addr=0x10000):
+    """A non-null, 256-byte-aligned address that is never dereferenced."""
+    return ctypes.c_void_p(addr)
+
+
+def test_exports_match_header(lib):
+    declared = _lib.declared_symbols()
+    assert len(declared) == 8
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " spot_" in ln})
+    assert exported == declared
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0) == "SPOT_OK"
+    for s in (INVALID, UNSUPPORTED, _lib.SPOT_ERR_DEVICE, 12345):
+        assert isinstance(_lib.status_string(s), str) and _lib.status_string(s)
+    assert lib.spot_abi_version() == 1
+
+
+def score(lib, **kw):
+    a = dict(sel_q=fake(), q_dtype=BF16, sel_w=fake(), sel_k=fake(), sel_k_scale=None,
+             k_dtype=BF16, scores=fake(), B=1, nb=8, kpb=1, H_idx=4, d_idx=64, stream=None)
+    a.update(kw)
+    return lib.spot_select_score(*a.values())
+
+
+def test_select_score_validation(lib):
+    assert score(lib, sel_q=None) == INVALID
+    assert score(lib, sel_k=fake(0x10008)) == INVALID              # misaligned keys
+    assert score(lib, B=0) == INVALID
+    assert score(lib, nb=-1) == INVALID
+    assert score(lib, kpb=0) == INVALID
+    assert score(lib, q_dtype=INT4) == INVALID
+    assert score(lib, k_dtype=7) == INVALID
+    assert score(lib, k_dtype=INT4) == INVALID                      # missing scales
+    assert score(lib, sel_k_scale=fake()) == INVALID                # scales with bf16 keys
+    assert score(lib, k_dtype=INT4, sel_k_scale=fake(), d_idx=48) == INVALID
+    assert score(lib, d_idx=96) == UNSUPPORTED
+    assert score(lib, H_idx=3) == UNSUPPORTED
+    assert score(lib, H_idx=16, d_idx=64) == UNSUPPORTED            # 128 lanes per key row
+
+
+def topp(lib, **kw):
+    a = dict(scores=fake(), sel_idx=fake(), sel_cnt=fake(), sel_mass=None, B=2, nb=64,
+             p=0.9, K_min=4, K_max=16, n_sink=1, n_rec=2, stream=None)
+    a.update(kw)
+    return lib.spot_select_topp(*a.values())
+
+
+def test_select_topp_validation(lib):
+    assert topp(lib, scores=None) == INVALID
+    assert topp(lib, sel_idx=fake(0x10002)) == INVALID
+    assert topp(lib, p=float("nan")) == INVALID
+    assert topp(lib, p=float("inf")) == INVALID
+    assert topp(lib, K_max=2) == INVALID           # reserved set (3 blocks) does not fit
+    assert topp(lib, K_max=0) == INVALID
+    assert topp(lib, n_sink=-1) == INVALID
+    assert topp(lib, K_min=-1) == INVALID
+    assert topp(lib, nb=0) == INVALID
+    assert topp(lib, nb=16385, K_max=20000) == UNSUPPORTED
+
+
+def attn(lib, **kw):
+    a = dict(q=fake(), k=fake(), v=fake(), kv_dtype=BF16, sel_idx=fake(), sel_cnt=fake(),
+             K_max=16, out=fake(), ws=fake(), ws_bytes=1 << 30, B=1, Hq=8, Hkv=2, d=128,
+             L=4096, block=64, sm_scale=0.125, stream=None)
+    a.update(kw)
+    return lib.spot_sparse_attn(*a.values())
+
+
+def test_sparse_attn_validation(lib):
+    assert attn(lib, q=None) == INVALID
+    assert attn(lib, ws=fake(0x10080)) == INVALID          # workspace not 256-byte aligned
+    assert attn(lib, ws_bytes=100) == INVALID
+    assert attn(lib, Hq=6, Hkv=4) == INVALID
+    assert attn(lib, kv_dtype=INT4) == INVALID
+    assert attn(lib, L=0) == INVALID
+    assert attn(lib, sm_scale=float("nan")) == INVALID
+    assert attn(lib, d=96) == UNSUPPORTED
+    assert attn(lib, block=16) == UNSUPPORTED
+    assert attn(lib, Hq=48, Hkv=3) == UNSUPPORTED           # 16 heads per KV head
+    ws = _lib.spot_sparse_attn_workspace_bytes(8, 32, 128, 256)
+    assert ws == 8 * 32 * 256 * 130 * 4
+    assert _lib.spot_sparse_attn_workspace_bytes(0, 32, 128, 256) == 0
+
+
+def test_prefill_validation(lib):
+    a = dict(sel_q=fake(), q_dtype=BF16, sel_w=fake(), sel_k=fake(), sel_k_scale=None,
+             k_dtype=BF16, scores=fake(), B=1, Tq=128, q_pos0=32640, nb_cache=512, kpb=1,
+             H_idx=4, d_idx=64, block=64, stream=None)
+    assert lib.spot_prefill_select_score(*{**a, "nb_cache": 100}.values()) == INVALID
+    assert lib.spot_prefill_select_score(*{**a, "q_pos0": -1}.values()) == INVALID
+    assert lib.spot_prefill_select_score(*{**a, "Tq": 256, "q_pos0": 0}.values()) == UNSUPPORTED
+    assert lib.spot_prefill_select_score(*{**a, "q_dtype": F32}.values()) == UNSUPPORTED
+    b = dict(q=fake(), k=fake(), v=fake(), kv_dtype=BF16, sel_idx=fake(), sel_cnt=fake(),
+             K_max=512, out=fake(), B=1, Hq=32, Hkv=8, Tq=128, q_pos0=32640, d=128, L=32768,
+             block=64, sm_scale=0.08, stream=None)
+    assert lib.spot_prefill_attn(*{**b, "q_pos0": 32700}.values()) == INVALID   # past L
+    assert lib.spot_prefill_attn(*{**b, "d": 64}.values()) == UNSUPPORTED
+    assert lib.spot_prefill_attn(*{**b, "kv_dtype": F32}.values()) == UNSUPPORTED

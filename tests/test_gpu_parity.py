@@ -1,0 +1,382 @@
+"""GPU parity: every C entry point against the CPU oracle on the same seeded inputs.
+
+Small and ragged cases cover several tiles and every supported shape; the five
+workloads run end to end, the 128K ones at full size in the launch configuration the
+benchmark times (the split plan is a function of the sizes only), with outputs
+compared on sampled rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_spot_amd import _lib
+from block_sparse_long_spot_amd import workloads as W
+from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
+from oracle import spot_oracle as O
+from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
+                    assert_topp_unit, decoded_keys, gpu_sets, np64, score_magnitude)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    _lib.load()   # raises when libspot.so is missing: no fallback exists
+
+
+def cpu_gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+# ------------------------------------------------------------------ spot_select_score
+SCORE_CASES = [
+    # B, nb, kpb, H, d_idx, q dtype, key kind
+    (1, 64, 1, 4, 32, "f32", "f32"),
+    (3, 333, 1, 4, 64, "bf16", "bf16"),
+    (2, 1000, 1, 4, 64, "f32", "bf16"),
+    (2, 77, 3, 2, 128, "bf16", "bf16"),
+    (2, 130, 16, 4, 128, "bf16", "bf16"),
+    (1, 50, 1, 8, 32, "f32", "f32"),
+    (2, 300, 1, 16, 32, "bf16", "f32"),
+    (1, 9, 2, 1, 64, "f32", "f32"),
+    (2, 257, 1, 4, 64, "bf16", "int4"),
+    (2, 65, 4, 4, 64, "f32", "int4"),
+    (1, 100, 1, 2, 128, "bf16", "int4"),
+    (1, 31, 1, 16, 32, "f32", "int4"),
+    (2, 2048, 1, 4, 64, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_select_score_parity(case):
+    B, nb, kpb, H, di, qd, kk = case
+    log(f"score case {case}")
+    g = cpu_gen(nb * 7 + kpb)
+    qt = torch.float32 if qd == "f32" else torch.bfloat16
+    sel_q = torch.randn(B, H, di, generator=g).to(qt)
+    sel_w = torch.randn(B, H, generator=g)            # signed weights
+    keys = torch.randn(B, nb, kpb, H, di, generator=g)
+    if kk == "int4":
+        codes, scales = W.quantize_int4_g32(keys)
+        inp = {"sel_k": codes, "sel_k_scale": scales}
+    else:
+        inp = {"sel_k": keys.to(torch.float32 if kk == "f32" else torch.bfloat16),
+               "sel_k_scale": None}
+    scores = torch.full((B, nb), float("nan"), device=DEV)
+    _lib.spot_select_score(sel_q.to(DEV), sel_w.to(DEV), inp["sel_k"].to(DEV),
+                           None if inp["sel_k_scale"] is None else inp["sel_k_scale"].to(DEV),
+                           scores, kpb=kpb)
+    torch.cuda.synchronize()
+    keys = decoded_keys(inp)
+    ref = O.select_score(np64(sel_q), np64(sel_w), keys)
+    assert_scores_close(np64(scores), ref, score_magnitude(np64(sel_q), np64(sel_w), keys))
+
+
+# ------------------------------------------------------------------ spot_select_topp
+def _topp_rows(kind, B, nb, g):
+    if kind == "normal":
+        return torch.randn(B, nb, generator=g) * 3
+    if kind == "wide":
+        return torch.randn(B, nb, generator=g) * 30
+    if kind == "ties":
+        return torch.round(torch.randn(B, nb, generator=g) * 2) / 2
+    if kind == "flat":
+        return torch.zeros(B, nb)
+    if kind == "signed_zero":
+        x = torch.round(torch.randn(B, nb, generator=g))
+        x[x == 0] = -0.0
+        x[:, ::3] = 0.0
+        return x
+    if kind == "zipf":
+        ranks = torch.stack([torch.randperm(nb, generator=g) for _ in range(B)]).float() + 1
+        return 1.1 * torch.log(nb / ranks)
+    raise ValueError(kind)
+
+
+TOPP_CASES = [
+    # nb, kind, p, K_min, K_max, n_sink, n_rec
+    (1, "normal", 0.9, 0, 1, 0, 0),
+    (3, "normal", 0.9, 0, 3, 1, 1),
+    (7, "ties", 0.5, 2, 7, 1, 1),
+    (64, "normal", 0.9, 4, 16, 1, 2),
+    (64, "ties", 0.0, 10, 10, 1, 2),
+    (100, "wide", 0.95, 0, 100, 2, 3),
+    (255, "signed_zero", 0.7, 5, 200, 1, 4),
+    (256, "flat", 0.9, 4, 256, 1, 4),
+    (257, "normal", 1.0, 0, 257, 1, 4),
+    (512, "normal", 0.95, 16, 128, 1, 4),
+    (512, "zipf", 0.95, 16, 512, 1, 4),
+    (1000, "ties", 0.9, 0, 1000, 0, 0),
+    (2048, "zipf", 0.95, 16, 256, 1, 4),
+    (2048, "normal", 0.95, 16, 256, 1, 4),
+    (2048, "wide", 0.3, 0, 2048, 1, 4),
+    (3000, "normal", 0.8, 32, 3000, 8, 16),
+    (4096, "zipf", 0.9, 0, 4096, 1, 4),
+    (5000, "ties", 0.95, 16, 600, 1, 4),
+    (8192, "zipf", 0.9, 32, 8192, 8, 16),
+    (12000, "normal", 0.95, 32, 1000, 8, 16),
+    (16384, "zipf", 0.95, 32, 16384, 8, 16),
+    (40, "normal", 0.9, 100, 40, 1, 2),         # floor above nb
+    (10, "normal", 0.9, 0, 10, 6, 6),           # empty residual
+    (20, "normal", -0.5, 3, 20, 1, 1),          # p <= 0: floor only
+    (20, "normal", 1.7, 0, 8, 1, 1),            # p >= 1: cap binds
+]
+
+
+@pytest.mark.parametrize("case", TOPP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_select_topp_parity(case):
+    nb, kind, p, K_min, K_max, n_sink, n_rec = case
+    log(f"topp case {case}")
+    B = 4
+    g = cpu_gen(nb * 13 + int(abs(p) * 100))
+    scores = _topp_rows(kind, B, nb, g).float().contiguous()
+    sd = scores.to(DEV)
+    sel_idx = torch.full((B, K_max), 12345, dtype=torch.int32, device=DEV)
+    sel_cnt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    sel_mass = torch.full((B,), -1.0, device=DEV)
+    _lib.spot_select_topp(sd, sel_idx, sel_cnt, sel_mass, p, K_min, K_max, n_sink, n_rec)
+    torch.cuda.synchronize()
+    sets = gpu_sets(sel_idx, sel_cnt)
+    pf = float(np.float32(p))
+    masses = sel_mass.cpu().numpy()
+    for b in range(B):
+        row = scores[b].double().numpy()
+        assert_topp_unit(sets[b], row, pf, K_min, K_max, n_sink, n_rec, tag=f"row {b}")
+        sel, info = O.select_topp_row(row, pf, K_min, K_max, n_sink, n_rec)
+        if sets[b] == sel and info["n_res"] > 0:
+            assert abs(masses[b] - info["mass"]) <= 1e-6, (masses[b], info["mass"])
+
+
+def test_select_topp_deterministic():
+    g = cpu_gen(99)
+    scores = (torch.randn(8, 2048, generator=g) * 4).to(DEV)
+    outs = []
+    for _ in range(3):
+        idx = torch.empty(8, 256, dtype=torch.int32, device=DEV)
+        cnt = torch.empty(8, dtype=torch.int32, device=DEV)
+        _lib.spot_select_topp(scores, idx, cnt, None, 0.95, 16, 256, 1, 4)
+        outs.append((idx.cpu(), cnt.cpu()))
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0]) and torch.equal(o[1], outs[0][1])
+
+
+# ------------------------------------------------------------------ spot_sparse_attn
+ATTN_CASES = [
+    # B, Hq, Hkv, d, L, K_max, dtype, pattern
+    (1, 8, 2, 64, 4096, 16, "f32", "random"),
+    (2, 8, 8, 128, 1000, 9, "f32", "random"),
+    (1, 16, 2, 64, 4000, 40, "f32", "ragged_last"),
+    (2, 8, 2, 128, 777, 13, "bf16", "ragged_last"),
+    (3, 32, 8, 128, 8192, 64, "bf16", "random"),
+    (2, 4, 4, 128, 3000, 30, "bf16", "random"),
+    (2, 8, 4, 64, 2500, 17, "bf16", "random"),
+    (1, 16, 2, 128, 5000, 33, "bf16", "random"),
+    (2, 8, 1, 64, 640, 10, "bf16", "all"),
+    (2, 32, 8, 128, 4096, 64, "bf16", "invalid_entries"),
+    (3, 8, 2, 64, 1024, 8, "f32", "empty_rows"),
+    (3, 32, 8, 128, 1024, 8, "bf16", "empty_rows"),
+    (1, 32, 8, 128, 70, 2, "bf16", "all"),
+    (4, 32, 8, 128, 20000, 256, "bf16", "random"),
+]
+
+
+def _sets_for(pattern, B, nb, K_max, g):
+    sets = []
+    for b in range(B):
+        if pattern == "all":
+            s = list(range(min(nb, K_max)))
+        elif pattern == "ragged_last":
+            c = int(torch.randint(1, K_max + 1, (1,), generator=g))
+            s = sorted(set(torch.randperm(nb - 1, generator=g)[: c - 1].tolist()) | {nb - 1})
+        elif pattern == "empty_rows":
+            s = [] if b % 2 == 0 else sorted(torch.randperm(nb, generator=g)[:K_max].tolist())
+        else:
+            c = int(torch.randint(1, K_max + 1, (1,), generator=g))
+            s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
+        sets.append(s)
+    return sets
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_sparse_attn_parity(case):
+    B, Hq, Hkv, d, L, K_max, dt, pattern = case
+    log(f"attn case {case}")
+    g = cpu_gen(L + d + K_max)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q = torch.randn(B, Hq, d, generator=g).to(tdt)
+    K = torch.randn(B, Hkv, L, d, generator=g).to(tdt)
+    V = torch.randn(B, Hkv, L, d, generator=g).to(tdt)
+    nb = -(-L // 64)
+    sets = _sets_for(pattern, B, nb, K_max, g)
+    idx = torch.full((B, K_max), -1, dtype=torch.int32)
+    cnt = torch.zeros(B, dtype=torch.int32)
+    for b, s in enumerate(sets):
+        idx[b, : len(s)] = torch.tensor(s, dtype=torch.int32)
+        cnt[b] = len(s)
+    if pattern == "invalid_entries":   # out-of-range entries inside the count are ignored
+        for b in range(B):
+            c = int(cnt[b])
+            if c < K_max:
+                idx[b, c] = nb + 5
+                cnt[b] = c + 1
+            idx[b, 0] = -1
+    scale = 1.0 / math.sqrt(d)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV).to(tdt)
+    ws = torch.empty(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
+                     device=DEV)
+    idx_d, cnt_d = idx.to(DEV), cnt.to(DEV)
+    _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx_d, cnt_d, out, ws, scale)
+    torch.cuda.synchronize()
+    used = [[int(x) for x in idx[b, : int(cnt[b])]] for b in range(B)]
+    ref = O.sparse_attention(np64(q), np64(K), np64(V), used, 64, scale)
+    assert_out_close(np64(out), ref, tdt, tag=str(case))
+
+
+def test_sparse_attn_deterministic():
+    g = cpu_gen(5)
+    B, Hq, Hkv, d, L, K_max = 2, 32, 8, 128, 16384, 64
+    q = torch.randn(B, Hq, d, generator=g).bfloat16().to(DEV)
+    K = torch.randn(B, Hkv, L, d, generator=g).bfloat16().to(DEV)
+    V = torch.randn(B, Hkv, L, d, generator=g).bfloat16().to(DEV)
+    idx = torch.stack([torch.randperm(256, generator=g)[:K_max].sort().values
+                       for _ in range(B)]).int().to(DEV)
+    cnt = torch.full((B,), K_max, dtype=torch.int32, device=DEV)
+    ws = torch.empty(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
+                     device=DEV)
+    outs = []
+    for _ in range(3):
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=DEV)
+        _lib.spot_sparse_attn(q, K, V, idx, cnt, out, ws, 1 / math.sqrt(d))
+        outs.append(out.cpu())
+    assert all(torch.equal(o, outs[0]) for o in outs[1:])
+
+
+# ------------------------------------------------------------------ end to end
+def run_e2e(wl, inp_dev, check_rows=None, tag=""):
+    """Run the three calls, then check scores, selection and (sampled) outputs."""
+    B = inp_dev["q"].shape[0]
+    dt = inp_dev["q"].dtype
+    bufs = DecodeBuffers(B, wl.nb, wl.Hq, wl.d, wl.K_max, dt)
+    decode_step(inp_dev, wl, bufs)
+    torch.cuda.synchronize()
+    log(f"{tag}: GPU step done")
+    keys = decoded_keys(inp_dev)
+    ref_scores = O.select_score(np64(inp_dev["sel_q"]), np64(inp_dev["sel_w"]), keys)
+    assert_scores_close(np64(bufs.scores), ref_scores,
+                        score_magnitude(np64(inp_dev["sel_q"]), np64(inp_dev["sel_w"]), keys))
+    sets = gpu_sets(bufs.sel_idx, bufs.sel_cnt)
+    pf = float(np.float32(wl.p))
+    for b in range(B):
+        assert_selection_e2e(sets[b], ref_scores[b], pf, wl.K_min, wl.K_max, wl.n_sink,
+                             wl.n_rec, tag=f"{tag} row {b}")
+    # top-p on the GPU's own scores must match the oracle's rule exactly
+    gs = np64(bufs.scores)
+    for b in range(B):
+        assert_topp_unit(sets[b], gs[b], pf, wl.K_min, wl.K_max, wl.n_sink, wl.n_rec,
+                         tag=f"{tag} unit row {b}")
+    log(f"{tag}: scores and selection match")
+    heads = None
+    if check_rows is not None:
+        heads = set(check_rows)
+    Kr = np64(inp_dev["K"]) if heads is None else _lazy_kv(inp_dev["K"])
+    Vr = np64(inp_dev["V"]) if heads is None else _lazy_kv(inp_dev["V"])
+    ref = O.sparse_attention(np64(inp_dev["q"]), Kr, Vr, sets, wl.block,
+                             1.0 / math.sqrt(wl.d), heads=heads)
+    got = np64(bufs.out)
+    if heads is None:
+        assert_out_close(got, ref, dt, tag=tag)
+    else:
+        for (b, h) in heads:
+            assert_out_close(got[b, h][None], ref[b, h][None], dt, tag=f"{tag} ({b},{h})")
+    log(f"{tag}: outputs match")
+    return bufs, sets
+
+
+class _lazy_kv:
+    """Indexable view of a device KV cache that copies one [L][d] slice at a time."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = t.shape
+
+    def __getitem__(self, key):
+        b, g = key
+        return self.t[b, g].to("cpu", torch.float64).numpy()
+
+
+@pytest.mark.parametrize("name", ["c1_small_f32", "c2_32k_b4"])
+def test_workload_end_to_end(name):
+    wl = W.WORKLOADS[name]
+    log(f"e2e {name}")
+    inp = W.make_inputs(wl, device="cpu")
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    bufs, sets = run_e2e(wl, dev, tag=name)
+    if wl.structure == "planted":
+        for b, s in enumerate(sets):
+            assert set(inp["planted"][b]) <= set(s), "planted blocks must be selected"
+            if name == "c1_small_f32":
+                assert len(s) == 7       # 4 tied planted blocks + 3 reserved
+            else:
+                assert len(s) == 16      # the K_min floor binds
+
+
+@pytest.fixture(scope="module")
+def big_inputs():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            wl = W.WORKLOADS[name]
+            log(f"generating {name} on the GPU")
+            cache[name] = W.make_inputs(wl, device=DEV)
+            torch.cuda.synchronize()
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", ["c3_128k_b1", "c3_128k_b8", "c4_128k_b8_int4"])
+def test_workload_full_size(name, big_inputs):
+    wl = W.WORKLOADS[name]
+    inp = big_inputs(name)
+    B = wl.B
+    rows = [(b, (5 * b + 3) % wl.Hq) for b in range(B)] + [(0, 0), (B - 1, wl.Hq - 1)]
+    bufs, sets = run_e2e(wl, inp, check_rows=rows, tag=name)
+    for s in sets:
+        if wl.sel_k_dtype == "int4":
+            # 4-bit keys add score noise that sharpens the distribution: the nucleus
+            # is no longer capped, so only the bounds on |S| hold
+            assert wl.K_min <= len(s) <= wl.K_max
+        else:
+            assert len(s) == wl.K_max     # the Zipf(1.1) nucleus is far above the cap
+
+
+def test_workload_budgets_vary(big_inputs):
+    """Zipf exponents spread over [1.3, 2.0] across the batch give different budgets."""
+    wl = W.WORKLOADS["c3_128k_b8"].with_(zipf_spread=(1.3, 2.0), L=32768)
+    inp = W.make_inputs(wl, device=DEV)
+    bufs, sets = run_e2e(wl, inp, check_rows=[(0, 1), (7, 30)], tag="c3-spread")
+    sizes = [len(s) for s in sets]
+    assert len(set(sizes)) >= 4, sizes
+
+
+def test_decode_step_bit_reproducible():
+    wl = W.WORKLOADS["c2_32k_b4"]
+    inp = W.make_inputs(wl, device=DEV, seed=7)
+    outs = []
+    for _ in range(2):
+        bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+        decode_step(inp, wl, bufs)
+        outs.append((bufs.scores.cpu(), bufs.sel_idx.cpu(), bufs.out.cpu()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
