@@ -211,7 +211,7 @@ def main():
                    "selector_cache": wl.sel_k_dtype, "p": wl.p, "K_min": wl.K_min,
                    "K_max": wl.K_max, "n_sink": wl.n_sink, "n_rec": wl.n_rec,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "spot_sparse_attn (split-K pass + combine)",
+        "roofline": {"bound": "hbm", "kernel": "attn_mfma (spot_sparse_attn: split-K runs and their merge in one kernel)",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": budget["attn"], "avg_launch_us": round(mean["attn"], 3)},

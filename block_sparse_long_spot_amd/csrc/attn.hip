@@ -1,19 +1,22 @@
 // Decode attention over the selected KV blocks (SpotAttention §2.3: the layer attends
 // only to keys in blocks of S_q, one S_q per query shared by every head).
 //
-// Split-K: the selected-block list of one (query, KV head) is cut into runs of
+// Split-K: the selected-block list of one (query, KV head) "unit" is cut into runs of
 // `bps` blocks; a work-group reduces one run with an online softmax for the G query
-// heads that share the KV head (GQA), and writes (m, l, acc) per head. A combine
-// kernel then merges the runs of each (query, head) in split order.
+// heads that share the KV head (GQA). A unit with a single run writes its output
+// directly; otherwise every run stores (m, l, acc) per head and attn_combine merges the
+// runs in run order (deterministic). Cross-work-group merging inside one kernel would
+// need an agent-scope release/acquire per work-group, which on this multi-XCD part is
+// an L2 writeback plus invalidate; a second small kernel is cheaper.
 //
-// HBM-bound (about 4 flop per byte in bf16 with G = 4). Two pass-1 kernels:
-//  * attn_partial_mfma (bf16, d in {64,128}): each wave owns whole 64-token blocks.
+// HBM-bound (about 4 flop per byte in bf16 with G = 4). Two run kernels:
+//  * attn_mfma (bf16, d in {64,128}): each wave owns whole 64-token blocks.
 //    q.K^T runs on the MFMA units (v_mfma_f32_16x16x32_bf16, the G heads padded to
 //    16 rows): every lane loads 16 contiguous bytes of a K row straight into the
 //    B-operand layout, no LDS staging and no bf16->fp32 conversion. P.V runs on the
 //    VALU: each lane owns 8 head dims of a set of tokens, reading V rows with
 //    coalesced 16-byte loads, and probabilities come through a per-wave LDS tile.
-//  * attn_partial_generic (fp32 or bf16, any supported shape): one wave per run;
+//  * attn_generic (fp32 or bf16, any supported shape): one wave per run;
 //    lane = token for q.K^T, lane = head dim for P.V.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
 #include "device_common.h"
@@ -34,18 +37,50 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// The run result of this work-group (per head: max m, sum l, unnormalised acc[D]) is
+// in LDS: the output itself when the unit has one run, else the run's partial result.
+template <typename T, int D, int G, int NT>
+__device__ void finish_run(const float (&racc)[G][D], const float (&rm)[G],
+                           const float (&rl)[G], int b, int g, int split, int ns, int Hq,
+                           int nsplit, float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
+                           T* __restrict__ out) {
+  for (int o = threadIdx.x; o < G * D; o += NT) {
+    const int h = o / D, dd = o % D;
+    if (ns == 1) {
+      const float v = rl[h] > 0.f ? racc[h][dd] / rl[h] : 0.f;
+      store_out(out + ((size_t)b * Hq + g * G + h) * D + dd, v);
+    } else {
+      const size_t idx = ((size_t)b * Hq + g * G + h) * nsplit + split;
+      ws_acc[idx * D + dd] = racc[h][dd];
+      if (dd == 0) ws_ml[idx] = make_float2(rm[h], rl[h]);
+    }
+  }
+}
+
+// A unit with no selected block: zero output rows.
+template <typename T, int D, int G, int NT>
+__device__ void zero_rows(int b, int g, int Hq, T* __restrict__ out) {
+  for (int o = threadIdx.x; o < G * D; o += NT)
+    store_out(out + ((size_t)b * Hq + g * G) * D + o, 0.f);
+}
+
 // ---------------------------------------------------------------- generic pass 1
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void attn_partial_generic(
+__global__ __launch_bounds__(64) void attn_generic(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, int K_max,
-    float* __restrict__ ws_acc, float2* __restrict__ ws_ml, int Hq, int Hkv, int L,
-    float qscale, int bps, int nsplit) {
+    float* __restrict__ ws_acc, float2* __restrict__ ws_ml, T* __restrict__ out, int Hq,
+    int Hkv, int L, float qscale, int bps, int nsplit) {
   constexpr int DPL = D / 64;  // head dims per lane in P.V
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int ns = (cnt + bps - 1) / bps;
+  if (ns == 0) {
+    if (split == 0) zero_rows<T, D, G, 64>(b, g, Hq, out);
+    return;
+  }
+  if (split >= ns) return;
   const int j0 = split * bps;
-  if (j0 >= cnt) return;
   const int j1 = min(j0 + bps, cnt);
   const int lane = threadIdx.x;
   __shared__ float qs[G][D];
@@ -109,22 +144,29 @@ __global__ __launch_bounds__(64) void attn_partial_generic(
     }
     __syncthreads();
   }
+  __shared__ float racc[G][D];
+  __shared__ float rm[G], rl[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const size_t o = ((size_t)b * Hq + g * G + h) * nsplit + split;
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) ws_acc[o * D + lane * DPL + c] = acc[h][c];
-    if (lane == 0) ws_ml[o] = make_float2(m[h], l[h]);
+    for (int c = 0; c < DPL; ++c) racc[h][lane * DPL + c] = acc[h][c];
+    if (lane == 0) {
+      rm[h] = m[h];
+      rl[h] = l[h];
+    }
   }
+  __syncthreads();
+  finish_run<T, D, G, 64>(racc, rm, rl, b, g, split, ns, Hq, nsplit, ws_acc, ws_ml, out);
 }
 
 // ---------------------------------------------------------------- MFMA pass 1 (bf16)
 template <int D, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_partial_mfma(
+__global__ __launch_bounds__(NW * 64) void attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml, int Hq, int Hkv, int L, float qscale, int bps, int nsplit) {
+    float2* __restrict__ ws_ml, uint16_t* __restrict__ out, int Hq, int Hkv, int L,
+    float qscale, int bps, int nsplit) {
   constexpr int KS = D / 32;   // MFMA k-steps over the head dim
   constexpr int DC = D / 8;    // lanes covering one V row (8 dims each)
   constexpr int TG = 64 / DC;  // token groups in P.V
@@ -134,8 +176,13 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_mfma(
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int ns = (cnt + bps - 1) / bps;
+  if (ns == 0) {
+    if (split == 0) zero_rows<uint16_t, D, G, NW * 64>(b, g, Hq, out);
+    return;
+  }
+  if (split >= ns) return;
   const int j0 = split * bps;
-  if (j0 >= cnt) return;
   const int j1 = min(j0 + bps, cnt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;  // MFMA operand coordinates
@@ -308,7 +355,9 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_mfma(
     }
   }
   __syncthreads();
-  // merge the waves of this work-group and write the run's partial result
+  // merge the waves of this work-group into the run result
+  __shared__ float racc[G][D];
+  __shared__ float rm[G], rl[G];
   for (int o = threadIdx.x; o < G * D; o += NW * 64) {
     const int h = o / D, dd = o % D;
     float M = -INFINITY;
@@ -321,51 +370,84 @@ __global__ __launch_bounds__(NW * 64) void attn_partial_mfma(
       ls += sc * ll[w][h];
       a += sc * accs[w][h][dd];
     }
-    const size_t idx = ((size_t)b * Hq + g * G + h) * nsplit + split;
-    ws_acc[idx * D + dd] = a;
-    if (dd == 0) ws_ml[idx] = make_float2(M, ls);
+    racc[h][dd] = a;
+    if (dd == 0) {
+      rm[h] = M;
+      rl[h] = ls;
+    }
   }
+  __syncthreads();
+  finish_run<uint16_t, D, G, NW * 64>(racc, rm, rl, b, g, split, ns, Hq, nsplit, ws_acc, ws_ml,
+                                      out);
 }
 
-// ---------------------------------------------------------------- pass 2: combine
+// ---------------------------------------------------------------- merge of the runs
+// One work-group per (query, head) with at least two runs; thread = head dim. Runs are
+// read 16 at a time (one memory round trip per 16) and merged with an online rescale
+// in run order.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ ws_acc,
                                                   const float2* __restrict__ ws_ml,
                                                   const int32_t* __restrict__ sel_cnt,
                                                   int K_max, T* __restrict__ out, int Hq,
                                                   int bps, int nsplit) {
+  constexpr int CH = 16;
   const int rowi = blockIdx.x;  // b * Hq + hq
   const int b = rowi / Hq;
   const int cnt = min(max(sel_cnt[b], 0), K_max);
   const int ns = (cnt + bps - 1) / bps;
+  if (ns <= 1) return;  // written by the run kernel
   const float2* ml = ws_ml + (size_t)rowi * nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
-  float res = 0.f;
-  if (M != -INFINITY) {
-    float ls = 0.f, a = 0.f;
-    const float* ap = ws_acc + (size_t)rowi * nsplit * D + threadIdx.x;
-    for (int s = 0; s < ns; ++s) {
-      const float2 v = ml[s];
-      const float w = v.x == -INFINITY ? 0.f : exp2f(v.x - M);
-      ls += w * v.y;
-      a += w * ap[(size_t)s * D];
+  const float* ap = ws_acc + (size_t)rowi * nsplit * D + threadIdx.x;
+  float M = -INFINITY, ls = 0.f, a = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += CH) {
+    float2 v[CH];
+    float x[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const bool ok = s0 + i < ns;
+      v[i] = ok ? ml[s0 + i] : make_float2(-INFINITY, 0.f);
+      x[i] = ok ? ap[(size_t)(s0 + i) * D] : 0.f;
     }
-    res = a / ls;
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, v[i].x);
+    if (Mc == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - Mc);
+    ls *= sc;
+    a *= sc;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const float w = v[i].x == -INFINITY ? 0.f : exp2f(v[i].x - Mc);
+      ls += w * v[i].y;
+      a += w * x[i];
+    }
+    M = Mc;
   }
-  store_out(out + (size_t)rowi * D + threadIdx.x, res);
+  store_out(out + (size_t)rowi * D + threadIdx.x, ls > 0.f ? a / ls : 0.f);
+}
+
+struct Ws {
+  float* acc;
+  float2* ml;
+};
+
+Ws carve(void* workspace, int B, int Hq, int d, int nsplit) {
+  Ws w;
+  w.acc = static_cast<float*>(workspace);
+  w.ml = reinterpret_cast<float2*>(w.acc + (size_t)B * Hq * nsplit * d);
+  return w;
 }
 
 template <typename T, int D, int G>
 hipError_t launch_generic(const void* q, const void* k, const void* v, const int32_t* sel_idx,
-                          const int32_t* sel_cnt, int K_max, float* ws_acc, float2* ws_ml,
-                          int B, int Hq, int Hkv, int L, float qscale, AttnSplit sp,
-                          hipStream_t stream) {
+                          const int32_t* sel_cnt, int K_max, Ws ws, void* out, int B, int Hq,
+                          int Hkv, int L, float qscale, AttnSplit sp, hipStream_t stream) {
   dim3 grid(sp.nsplit, Hkv, B);
-  hipLaunchKernelGGL((attn_partial_generic<T, D, G>), grid, dim3(64), 0, stream,
+  hipLaunchKernelGGL((attn_generic<T, D, G>), grid, dim3(64), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), sel_idx, sel_cnt, K_max, ws_acc, ws_ml, Hq, Hkv,
-                     L, qscale, sp.blocks_per_split, sp.nsplit);
+                     static_cast<const T*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml,
+                     static_cast<T*>(out), Hq, Hkv, L, qscale, sp.blocks_per_split, sp.nsplit);
   return hipGetLastError();
 }
 
@@ -373,40 +455,47 @@ constexpr int kMfmaWaves = 4;
 
 template <int D, int G>
 hipError_t launch_mfma(const void* q, const void* k, const void* v, const int32_t* sel_idx,
-                       const int32_t* sel_cnt, int K_max, float* ws_acc, float2* ws_ml, int B,
-                       int Hq, int Hkv, int L, float qscale, AttnSplit sp, hipStream_t stream) {
+                       const int32_t* sel_cnt, int K_max, Ws ws, void* out, int B, int Hq,
+                       int Hkv, int L, float qscale, AttnSplit sp, hipStream_t stream) {
   dim3 grid(sp.nsplit, Hkv, B);
-  hipLaunchKernelGGL((attn_partial_mfma<D, G, kMfmaWaves>), grid, dim3(kMfmaWaves * 64), 0,
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws_acc, ws_ml,
-                     Hq, Hkv, L, qscale, sp.blocks_per_split, sp.nsplit);
+  hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves>), grid, dim3(kMfmaWaves * 64), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml,
+                     static_cast<uint16_t*>(out), Hq, Hkv, L, qscale, sp.blocks_per_split,
+                     sp.nsplit);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
-                    const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, float* ws_acc,
-                    float2* ws_ml, int B, int Hq, int Hkv, int L, float qscale, AttnSplit sp,
+                    const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, Ws ws,
+                    void* out, int B, int Hq, int Hkv, int L, float qscale, AttnSplit sp,
                     hipStream_t stream) {
   const int G = Hq / Hkv;
-#define SPOT_ARGS q, k, v, sel_idx, sel_cnt, K_max, ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream
-  if constexpr (std::is_same<T, uint16_t>::value) {
-    if (fast) {
-      switch (G) {
-        case 1: return launch_mfma<D, 1>(SPOT_ARGS);
-        case 2: return launch_mfma<D, 2>(SPOT_ARGS);
-        case 4: return launch_mfma<D, 4>(SPOT_ARGS);
-        default: return launch_mfma<D, 8>(SPOT_ARGS);
-      }
+  hipError_t e;
+#define SPOT_ARGS q, k, v, sel_idx, sel_cnt, K_max, ws, out, B, Hq, Hkv, L, qscale, sp, stream
+  if (std::is_same<T, uint16_t>::value && fast) {
+    switch (G) {
+      case 1: e = launch_mfma<D, 1>(SPOT_ARGS); break;
+      case 2: e = launch_mfma<D, 2>(SPOT_ARGS); break;
+      case 4: e = launch_mfma<D, 4>(SPOT_ARGS); break;
+      default: e = launch_mfma<D, 8>(SPOT_ARGS); break;
+    }
+  } else {
+    switch (G) {
+      case 1: e = launch_generic<T, D, 1>(SPOT_ARGS); break;
+      case 2: e = launch_generic<T, D, 2>(SPOT_ARGS); break;
+      case 4: e = launch_generic<T, D, 4>(SPOT_ARGS); break;
+      default: e = launch_generic<T, D, 8>(SPOT_ARGS); break;
     }
   }
-  switch (G) {
-    case 1: return launch_generic<T, D, 1>(SPOT_ARGS);
-    case 2: return launch_generic<T, D, 2>(SPOT_ARGS);
-    case 4: return launch_generic<T, D, 4>(SPOT_ARGS);
-    default: return launch_generic<T, D, 8>(SPOT_ARGS);
-  }
 #undef SPOT_ARGS
+  if (e != hipSuccess) return e;
+  if (sp.nsplit > 1)
+    hipLaunchKernelGGL((attn_combine<T, D>), dim3(B * Hq), dim3(D), 0, stream, ws.acc, ws.ml,
+                       sel_cnt, K_max, static_cast<T*>(out), Hq, sp.blocks_per_split,
+                       sp.nsplit);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -417,10 +506,10 @@ AttnSplit attn_split_plan(int B, int Hkv, int K_max, bool bf16_fast_path) {
   if (!bf16_fast_path) {
     sp.blocks_per_split = 4;
   } else {
-    // the largest run length that still gives >= 1024 work-groups, within [4, 64]
+    // the longest run (<= 32 blocks) that still gives >= 256 work-groups
     int bps = 4;
-    for (int c = 64; c >= 4; c >>= 1) {
-      if (units * ((K_max + c - 1) / c) >= 1024) {
+    for (int c = 32; c >= 4; c >>= 1) {
+      if (units * ((K_max + c - 1) / c) >= 256) {
         bps = c;
         break;
       }
@@ -431,49 +520,28 @@ AttnSplit attn_split_plan(int B, int Hkv, int K_max, bool bf16_fast_path) {
   return sp;
 }
 
+size_t attn_workspace_bytes(int B, int Hq, int d, int K_max) {
+  // runs per unit are at most K_max (one block per run)
+  return (size_t)B * Hq * K_max * ((size_t)d + 2) * sizeof(float);
+}
+
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,
                               int K_max, void* out, void* workspace, int B, int Hq, int Hkv,
                               int d, int L, float sm_scale, hipStream_t stream) {
   const bool fast = bf16;
   const AttnSplit sp = attn_split_plan(B, Hkv, K_max, fast);
-  float* ws_acc = static_cast<float*>(workspace);
-  float2* ws_ml = reinterpret_cast<float2*>(ws_acc + (size_t)B * Hq * sp.nsplit * d);
+  const Ws ws = carve(workspace, B, Hq, d, sp.nsplit);
   const float qscale = sm_scale * kLog2e;
-  hipError_t e;
-  if (bf16) {
-    e = d == 64 ? launch_d<uint16_t, 64>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
-                                         ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream)
-                : launch_d<uint16_t, 128>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
-                                          ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream);
-  } else {
-    e = d == 64 ? launch_d<float, 64>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max,
-                                      ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream)
-                : launch_d<float, 128>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max,
-                                       ws_acc, ws_ml, B, Hq, Hkv, L, qscale, sp, stream);
-  }
-  if (e != hipSuccess) return e;
-  dim3 grid(B * Hq);
-  if (bf16) {
-    if (d == 64)
-      hipLaunchKernelGGL((attn_combine<uint16_t, 64>), grid, dim3(64), 0, stream, ws_acc, ws_ml,
-                         sel_cnt, K_max, static_cast<uint16_t*>(out), Hq, sp.blocks_per_split,
-                         sp.nsplit);
-    else
-      hipLaunchKernelGGL((attn_combine<uint16_t, 128>), grid, dim3(128), 0, stream, ws_acc,
-                         ws_ml, sel_cnt, K_max, static_cast<uint16_t*>(out), Hq,
-                         sp.blocks_per_split, sp.nsplit);
-  } else {
-    if (d == 64)
-      hipLaunchKernelGGL((attn_combine<float, 64>), grid, dim3(64), 0, stream, ws_acc, ws_ml,
-                         sel_cnt, K_max, static_cast<float*>(out), Hq, sp.blocks_per_split,
-                         sp.nsplit);
-    else
-      hipLaunchKernelGGL((attn_combine<float, 128>), grid, dim3(128), 0, stream, ws_acc, ws_ml,
-                         sel_cnt, K_max, static_cast<float*>(out), Hq, sp.blocks_per_split,
-                         sp.nsplit);
-  }
-  return hipGetLastError();
+  if (bf16)
+    return d == 64 ? launch_d<uint16_t, 64>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
+                                            ws, out, B, Hq, Hkv, L, qscale, sp, stream)
+                   : launch_d<uint16_t, 128>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
+                                             ws, out, B, Hq, Hkv, L, qscale, sp, stream);
+  return d == 64 ? launch_d<float, 64>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max, ws,
+                                       out, B, Hq, Hkv, L, qscale, sp, stream)
+                 : launch_d<float, 128>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max, ws,
+                                        out, B, Hq, Hkv, L, qscale, sp, stream);
 }
 
 }  // namespace spot

@@ -91,8 +91,7 @@ int spot_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt, fl
 
 size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max) {
   if (B <= 0 || Hq <= 0 || d <= 0 || K_max <= 0) return 0;
-  // at most K_max runs per (query, head): fp32 accumulators plus (m, l)
-  return (size_t)B * Hq * K_max * ((size_t)d + 2) * sizeof(float);
+  return spot::attn_workspace_bytes(B, Hq, d, K_max);
 }
 
 int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, int kv_dtype,

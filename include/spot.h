@@ -130,9 +130,11 @@ SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max
  *                16-byte aligned.
  *   sel_idx      int32 [B][K_max], sel_cnt int32 [B] (as written by spot_select_topp).
  *   workspace    device scratch of at least spot_sparse_attn_workspace_bytes(B, Hq, d,
- *                K_max) bytes, 256-byte aligned; contents on entry do not matter.
+ *                K_max) bytes, 256-byte aligned; contents on entry do not matter. Calls
+ *                that run at the same time must not share a workspace.
  * Split-K: each work-group reduces a run of selected blocks of one (b, KV head) with an
- * online softmax; a second kernel merges the runs in a fixed order (deterministic).
+ * online softmax; a second kernel merges the runs of every (b, head) in run order, so
+ * the result is deterministic.
  * Supported: d in {64, 128}; block == 64; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
  */
 SPOT_API int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -96,6 +96,13 @@ def _topp_rows(kind, B, nb, g):
         x[x == 0] = -0.0
         x[:, ::3] = 0.0
         return x
+    if kind.startswith("tiebin"):
+        # 10 high blocks, then a group of n equal scores where the cut falls, then noise
+        n = int(kind[6:])
+        x = torch.rand(B, nb, generator=g) - 2.0
+        x[:, 5:15] = 4.0
+        x[:, 20:20 + n] = 2.5
+        return x
     if kind == "zipf":
         ranks = torch.stack([torch.randperm(nb, generator=g) for _ in range(B)]).float() + 1
         return 1.1 * torch.log(nb / ranks)
@@ -125,6 +132,10 @@ TOPP_CASES = [
     (8192, "zipf", 0.9, 32, 8192, 8, 16),
     (12000, "normal", 0.95, 32, 1000, 8, 16),
     (16384, "zipf", 0.95, 32, 16384, 8, 16),
+    (200, "tiebin64", 0.9, 0, 200, 1, 2),       # 64 tied blocks at the cut: one-wave rank
+    (200, "tiebin65", 0.9, 0, 200, 1, 2),       # 65 tied blocks: exact radix fallback
+    (300, "tiebin65", 0.9, 0, 40, 1, 2),        # fallback, then the cap inside the bin
+    (300, "tiebin64", 0.5, 30, 300, 1, 2),      # floor lands inside the tied bin
     (40, "normal", 0.9, 100, 40, 1, 2),         # floor above nb
     (10, "normal", 0.9, 0, 10, 6, 6),           # empty residual
     (20, "normal", -0.5, 3, 20, 1, 1),          # p <= 0: floor only
@@ -231,7 +242,7 @@ def test_sparse_attn_parity(case):
             idx[b, 0] = -1
     scale = 1.0 / math.sqrt(d)
     out = torch.full((B, Hq, d), float("nan"), device=DEV).to(tdt)
-    ws = torch.empty(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
+    ws = torch.zeros(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
                      device=DEV)
     idx_d, cnt_d = idx.to(DEV), cnt.to(DEV)
     _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx_d, cnt_d, out, ws, scale)
@@ -250,7 +261,7 @@ def test_sparse_attn_deterministic():
     idx = torch.stack([torch.randperm(256, generator=g)[:K_max].sort().values
                        for _ in range(B)]).int().to(DEV)
     cnt = torch.full((B,), K_max, dtype=torch.int32, device=DEV)
-    ws = torch.empty(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
+    ws = torch.zeros(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
                      device=DEV)
     outs = []
     for _ in range(3):
