@@ -1,18 +1,282 @@
 // Prefill-tile variant: tile block scoring and causal block-sparse attention.
+//
+// Tile scoring (SpotAttention §2.1: one score per query-block x key-block tile, so
+// selection runs as a tensor-core matmul; §2.3 per-block maximum). For every selector
+// head h, S_h = Qsel_h [Tq x d_idx] . Ksel_h^T [d_idx x blocks] runs on the MFMA units
+// (v_mfma_f32_16x16x32_bf16); the epilogue applies ReLU and the per-query weight w[q][h],
+// adds the heads, and keeps the maximum over the tile's queries that can see the block.
+//
+// Attention: one work-group per (16-query row tile, KV head); wave w computes query
+// head g*G + w, so the G heads of a KV group share every K/V block the work-group
+// stages in LDS (K row-major, V transposed). Per selected block:
+//   S' = K . Q^T   (tokens x queries; A = K from LDS, B = Q from registers)
+// whose accumulator layout gives each lane 8 scores of one query row. Those become,
+// after the online softmax and a bf16 conversion, the A operand of
+//   O += P . V     (B = V^T read from LDS in the same token order),
+// so P never leaves registers. Causal and L masks are applied per element.
 #include "device_common.h"
 #include "spot_internal.h"
 
 namespace spot {
+namespace {
 
-hipError_t launch_prefill_select_score(const void*, const float*, const void*, float*, int, int,
-                                       int, int, int, int, int, int, int, hipStream_t) {
-  return hipErrorNotSupported;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBlk = 64;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f_to_bf16_rne(lo)) | (static_cast<uint32_t>(f_to_bf16_rne(hi)) << 16);
 }
 
-hipError_t launch_prefill_attn(const void*, const void*, const void*, const int32_t*,
-                               const int32_t*, int, void*, int, int, int, int, int, int, int,
-                               float, hipStream_t) {
-  return hipErrorNotSupported;
+// ---------------------------------------------------------------- tile scoring
+// Wave = 16 blocks (columns) x all Tq queries (rows, 16 per MFMA row tile).
+template <int DIDX>
+__global__ __launch_bounds__(64) void prefill_score_kernel(
+    const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
+    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int Tq, int q_pos0,
+    int nb_cache, int nb_vis, int kpb, int H, int block) {
+  constexpr int KS = DIDX / 32;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, kg = lane >> 4;
+  const int b = blockIdx.y;
+  const int blk0 = blockIdx.x * 16;
+  const int blk = blk0 + col;                      // B-operand column of this lane
+  const int blk_c = min(blk, nb_vis - 1);
+  const int n_rt = (Tq + 15) / 16;
+  const uint16_t* qb = sel_q + (size_t)b * Tq * H * DIDX;
+  const float* wb = sel_w + (size_t)b * Tq * H;
+  float best = -INFINITY;  // max over (visible query, key j) for column blk0 + col
+  for (int j = 0; j < kpb; ++j) {
+    for (int rt = 0; rt < n_rt; ++rt) {
+      floatx4_t tot = {0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < H; ++h) {
+        const uint16_t* kp =
+            sel_k + ((((size_t)b * nb_cache + blk_c) * kpb + j) * H + h) * DIDX + kg * 8;
+        const int qr = min(rt * 16 + col, Tq - 1);  // A-operand row of this lane
+        const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
+        floatx4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
+          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, c, 0, 0, 0);
+        }
+        // c[r] = S_h[query rt*16 + kg*4 + r][column col]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = min(rt * 16 + kg * 4 + r, Tq - 1);
+          tot[r] += wb[(size_t)qi * H + h] * fmaxf(c[r], 0.f);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = rt * 16 + kg * 4 + r;
+        const bool vis = qi < Tq && (long)blk * block <= (long)q_pos0 + qi;
+        if (vis) best = fmaxf(best, tot[r]);
+      }
+    }
+  }
+  // lanes col, col+16, col+32, col+48 hold the same column
+  best = fmaxf(best, shfl_xor_f(best, 16));
+  best = fmaxf(best, shfl_xor_f(best, 32));
+  if (kg == 0 && blk < nb_vis) scores[(size_t)b * nb_vis + blk] = best;
+}
+
+// ---------------------------------------------------------------- attention
+constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
+constexpr int kVPad = 68;   // V^T row stride in bf16 (128 B + 8 B)
+
+template <int G>
+__global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
+    const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
+    const int32_t* __restrict__ sel_cnt, int K_max, uint16_t* __restrict__ out, int Hq,
+    int Hkv, int Tq, int q_pos0, int L, float qscale) {
+  constexpr int D = 128;
+  constexpr int NT = G * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kKPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kVPad];
+
+  const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hq = g * G + wave;
+  const int row = lane & 15, kg = lane >> 4;
+  const int q0 = rt * 16;
+  const int my_q = q0 + row;                // query row this lane's softmax state tracks
+  const int my_pos = q_pos0 + my_q;
+
+  // B operand of S' = K.Q^T: column = query row, k = head dim
+  bf16x8_t qb[4];
+  {
+    const uint16_t* qp =
+        Q + (((size_t)b * Hq + hq) * Tq + min(my_q, Tq - 1)) * D + kg * 8;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
+  }
+  float m = -INFINITY, l = 0.f;       // state of query row `row` (same in its 4 lane groups)
+  floatx4_t o[8];                     // O[query (kg*4 + r)][d = dt*16 + row]
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int nbl = (L + kBlk - 1) / kBlk;
+  const int last_pos = q_pos0 + min(q0 + 15, Tq - 1);  // furthest query of the tile
+  const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
+  const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+
+  for (int j = 0; j < cnt; ++j) {
+    const int blk = sel_idx[(size_t)b * K_max + j];
+    if (blk < 0 || blk >= nbl || blk * kBlk > last_pos) continue;  // uniform
+    const int t0 = blk * kBlk;
+    // stage K (row-major) and V (transposed) of this block
+    for (int c = tid; c < kBlk * (D / 8); c += NT) {
+      const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      const int tok = min(t0 + t, L - 1);
+      const uint4 kv = *reinterpret_cast<const uint4*>(Kg + (size_t)tok * D + d0);
+      *reinterpret_cast<uint4*>(&Ks[t * kKPad + d0]) = kv;
+      const uint4 vv = *reinterpret_cast<const uint4*>(Vg + (size_t)tok * D + d0);
+      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Vt[(d0 + 2 * i) * kVPad + t] = static_cast<uint16_t>(w4[i] & 0xffffu);
+        Vt[(d0 + 2 * i + 1) * kVPad + t] = static_cast<uint16_t>(w4[i] >> 16);
+      }
+    }
+    __syncthreads();
+    // S'[token][query] for 4 tiles of 16 tokens
+    floatx4_t sc[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      floatx4_t a = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kp = &Ks[(T * 16 + row) * kKPad + kg * 8];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(kp + s * 32),
+                                                    qb[s], a, 0, 0, 0);
+      sc[T] = a;  // sc[T][r] = S[query row][token T*16 + kg*4 + r]
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + T * 16 + kg * 4 + r;
+        const float z = (t <= my_pos && t < L) ? sc[T][r] * qscale : -INFINITY;
+        sc[T][r] = z;
+        bm = fmaxf(bm, z);
+      }
+    bm = fmaxf(bm, shfl_xor_f(bm, 16));
+    bm = fmaxf(bm, shfl_xor_f(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pz = mn == -INFINITY ? 0.f : exp2f(sc[T][r] - mn);
+        sc[T][r] = pz;
+        rs += pz;
+      }
+    rs += shfl_xor_f(rs, 16);
+    rs += shfl_xor_f(rs, 32);
+    l = l * alpha + rs;
+    m = mn;
+    // rescale O rows kg*4 + r by the alpha of those rows (held by lanes with that row)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, kg * 4 + r, 64);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt][r] *= ar;
+    }
+    // P as the A operand: k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+      u32x4 pk;
+      pk[0] = pack_bf16x2(sc[2 * s][0], sc[2 * s][1]);
+      pk[1] = pack_bf16x2(sc[2 * s][2], sc[2 * s][3]);
+      pk[2] = pack_bf16x2(sc[2 * s + 1][0], sc[2 * s + 1][1]);
+      pk[3] = pack_bf16x2(sc[2 * s + 1][2], sc[2 * s + 1][3]);
+      const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint16_t* vp = &Vt[(dt * 16 + row) * kVPad + 32 * s + 4 * kg];
+        u32x4 vb;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+        vb[0] = lo.x;
+        vb[1] = lo.y;
+        vb[2] = hi.x;
+        vb[3] = hi.y;
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb),
+                                                        o[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // normalise: rows kg*4 + r need the l of those rows
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float lr = __shfl(l, kg * 4 + r, 64);
+    const int qi = q0 + kg * 4 + r;
+    if (qi < Tq) {
+      uint16_t* op = out + (((size_t)b * Hq + hq) * Tq + qi) * D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        op[dt * 16 + row] = f_to_bf16_rne(lr > 0.f ? o[dt][r] / lr : 0.f);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
+                                       const void* sel_k, float* scores, int B, int Tq,
+                                       int q_pos0, int nb_cache, int nb_vis, int kpb, int H,
+                                       int d_idx, int block, hipStream_t stream) {
+  dim3 grid((nb_vis + 15) / 16, B);
+  const uint16_t* q = static_cast<const uint16_t*>(sel_q);
+  const uint16_t* k = static_cast<const uint16_t*>(sel_k);
+  switch (d_idx) {
+    case 32:
+      hipLaunchKernelGGL(prefill_score_kernel<32>, grid, dim3(64), 0, stream, q, sel_w, k,
+                         scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block);
+      break;
+    case 64:
+      hipLaunchKernelGGL(prefill_score_kernel<64>, grid, dim3(64), 0, stream, q, sel_w, k,
+                         scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block);
+      break;
+    default:
+      hipLaunchKernelGGL(prefill_score_kernel<128>, grid, dim3(64), 0, stream, q, sel_w, k,
+                         scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* sel_idx, const int32_t* sel_cnt, int K_max,
+                               void* out, int B, int Hq, int Hkv, int Tq, int q_pos0, int d,
+                               int L, float sm_scale, hipStream_t stream) {
+  (void)d;
+  const int G = Hq / Hkv;
+  dim3 grid((Tq + 15) / 16, Hkv, B);
+  const float qscale = sm_scale * kLog2e;
+  const uint16_t* Qp = static_cast<const uint16_t*>(q);
+  const uint16_t* Kp = static_cast<const uint16_t*>(k_cache);
+  const uint16_t* Vp = static_cast<const uint16_t*>(v_cache);
+  uint16_t* Op = static_cast<uint16_t*>(out);
+#define SPOT_PF(GG)                                                                         \
+  hipLaunchKernelGGL(prefill_attn_kernel<GG>, grid, dim3(GG * 64), 0, stream, Qp, Kp, Vp, \
+                     sel_idx, sel_cnt, K_max, Op, Hq, Hkv, Tq, q_pos0, L, qscale)
+  switch (G) {
+    case 1: SPOT_PF(1); break;
+    case 2: SPOT_PF(2); break;
+    case 4: SPOT_PF(4); break;
+    default: SPOT_PF(8); break;
+  }
+#undef SPOT_PF
+  return hipGetLastError();
 }
 
 }  // namespace spot

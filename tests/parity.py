@@ -139,3 +139,16 @@ def assert_out_close(g: np.ndarray, r: np.ndarray, dtype: torch.dtype, tag=""):
     else:
         err = np.abs(g - r).max()
         assert err <= 2e-2, f"{tag}: max abs err {err}"
+
+
+def tile_score_magnitude(sel_q, sel_w, keys, q_pos0, block) -> np.ndarray:
+    """Prefill analogue of score_magnitude: the largest term size over the tile's queries
+    that see each block, [B][nb_vis]."""
+    q = np.abs(np.asarray(sel_q, np.float64))
+    w = np.abs(np.asarray(sel_w, np.float64))
+    k = np.abs(np.asarray(keys, np.float64))
+    B, Tq = q.shape[0], q.shape[1]
+    nb_vis = -(-(q_pos0 + Tq) // block)
+    per_key = (w[:, :, None, None, :] * np.einsum("bqhi,bnjhi->bqnjh", q, k[:, :nb_vis])).sum(-1)
+    per_q = per_key.max(-1)
+    return per_q.max(axis=1)

@@ -1,0 +1,156 @@
+"""GPU parity of the prefill-tile variant: MFMA tile scoring, top-p over the visible
+blocks with the diagonal recency window, and causal block-sparse MFMA attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_spot_amd import _lib
+from block_sparse_long_spot_amd import workloads as W
+from oracle import spot_oracle as O
+from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
+                    assert_topp_unit, gpu_sets, np64, tile_score_magnitude)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    _lib.load()
+
+
+SCORE_CASES = [
+    # B, Tq, q_pos0, nb_cache, kpb, H, d_idx
+    (1, 128, 32640, 512, 1, 4, 64),
+    (2, 40, 1000, 20, 1, 4, 64),
+    (1, 17, 0, 1, 2, 2, 32),
+    (1, 128, 200, 6, 1, 1, 128),
+    (2, 100, 5000, 100, 3, 4, 64),
+    (1, 64, 4095, 70, 1, 8, 32),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_score_parity(case):
+    B, Tq, q_pos0, nb_cache, kpb, H, di = case
+    log(f"prefill score {case}")
+    g = torch.Generator().manual_seed(Tq + q_pos0)
+    sel_q = torch.randn(B, Tq, H, di, generator=g).bfloat16()
+    sel_w = torch.randn(B, Tq, H, generator=g)
+    sel_k = torch.randn(B, nb_cache, kpb, H, di, generator=g).bfloat16()
+    nb_vis = -(-(q_pos0 + Tq) // 64)
+    scores = torch.full((B, nb_vis), float("nan"), device=DEV)
+    _lib.spot_prefill_select_score(sel_q.to(DEV), sel_w.to(DEV), sel_k.to(DEV), scores, q_pos0,
+                                   block=64, kpb=kpb)
+    torch.cuda.synchronize()
+    ref = O.prefill_tile_score(np64(sel_q), np64(sel_w), np64(sel_k), q_pos0, 64)
+    mag = tile_score_magnitude(np64(sel_q), np64(sel_w), np64(sel_k), q_pos0, 64)
+    assert_scores_close(np64(scores), ref, mag)
+
+
+ATTN_CASES = [
+    # B, Hq, Hkv, Tq, q_pos0, L, pattern
+    (1, 32, 8, 128, 32640, 32768, "random"),
+    (1, 8, 2, 128, 1000, 1128, "all"),
+    (2, 8, 8, 40, 300, 400, "random"),
+    (1, 4, 2, 17, 0, 17, "all"),
+    (1, 16, 2, 100, 5000, 7000, "with_future"),
+    (2, 8, 1, 64, 64, 1000, "random"),
+    (1, 8, 4, 128, 700, 900, "diag_only"),
+    (1, 8, 2, 33, 2000, 2100, "empty"),
+]
+
+
+def _prefill_sets(pattern, B, q_pos0, Tq, L, g):
+    nb = -(-L // 64)
+    last = (q_pos0 + Tq - 1) // 64
+    sets = []
+    for b in range(B):
+        if pattern == "all":
+            s = list(range(last + 1))
+        elif pattern == "diag_only":
+            s = list(range(max(0, last - 3), last + 1))
+        elif pattern == "empty":
+            s = []
+        else:
+            pool = torch.randperm(last + 1, generator=g)[: max(1, (last + 1) // 3)].tolist()
+            s = set(pool) | set(range(max(0, last - 3), last + 1)) | {0}
+            if pattern == "with_future" and last + 1 < nb:
+                s |= {last + 1, nb - 1}       # blocks after the tile: fully masked
+            s = sorted(s)
+        sets.append(s)
+    return sets
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_attn_parity(case):
+    B, Hq, Hkv, Tq, q_pos0, L, pattern = case
+    log(f"prefill attn {case}")
+    g = torch.Generator().manual_seed(L + Tq)
+    Q = torch.randn(B, Hq, Tq, 128, generator=g).bfloat16()
+    K = torch.randn(B, Hkv, L, 128, generator=g).bfloat16()
+    V = torch.randn(B, Hkv, L, 128, generator=g).bfloat16()
+    sets = _prefill_sets(pattern, B, q_pos0, Tq, L, g)
+    K_max = max(1, max(len(s) for s in sets))
+    idx = torch.full((B, K_max), -1, dtype=torch.int32)
+    cnt = torch.zeros(B, dtype=torch.int32)
+    for b, s in enumerate(sets):
+        if s:
+            idx[b, : len(s)] = torch.tensor(s, dtype=torch.int32)
+        cnt[b] = len(s)
+    out = torch.full((B, Hq, Tq, 128), float("nan"), device=DEV).bfloat16()
+    scale = 1 / math.sqrt(128)
+    _lib.spot_prefill_attn(Q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), cnt.to(DEV), out, q_pos0,
+                           scale)
+    torch.cuda.synchronize()
+    ref = O.prefill_attention(np64(Q), np64(K), np64(V), sets, 64, scale, q_pos0)
+    assert_out_close(np64(out), ref, torch.bfloat16, tag=str(case))
+
+
+def test_prefill_tile_end_to_end():
+    """The 128-query tile at positions 32640..32767 of a 32K context."""
+    wl = W.WORKLOADS["c5_prefill_32k"]
+    inp = W.make_inputs(wl, device=DEV)
+    q_pos0, Tq, nb_vis = wl.q_pos0, wl.prefill_Tq, wl.nb
+    scores = torch.empty(wl.B, nb_vis, device=DEV)
+    _lib.spot_prefill_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"], scores, q_pos0)
+    K_max = nb_vis
+    idx = torch.empty(wl.B, K_max, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(wl.B, dtype=torch.int32, device=DEV)
+    _lib.spot_select_topp(scores, idx, cnt, None, wl.p, wl.K_min, K_max, wl.n_sink, wl.n_rec)
+    out = torch.empty(wl.B, wl.Hq, Tq, wl.d, dtype=torch.bfloat16, device=DEV)
+    scale = 1 / math.sqrt(wl.d)
+    _lib.spot_prefill_attn(inp["q"], inp["K"], inp["V"], idx, cnt, out, q_pos0, scale)
+    torch.cuda.synchronize()
+    sq, sw, sk = np64(inp["sel_q"]), np64(inp["sel_w"]), np64(inp["sel_k"])
+    ref_s = O.prefill_tile_score(sq, sw, sk, q_pos0, wl.block)
+    assert_scores_close(np64(scores), ref_s, tile_score_magnitude(sq, sw, sk, q_pos0, wl.block))
+    sets = gpu_sets(idx, cnt)
+    pf = float(np.float32(wl.p))
+    assert_selection_e2e(sets[0], ref_s[0], pf, wl.K_min, K_max, wl.n_sink, wl.n_rec, "c5")
+    assert_topp_unit(sets[0], np64(scores)[0], pf, wl.K_min, K_max, wl.n_sink, wl.n_rec, "c5u")
+    assert set(range(nb_vis - 4, nb_vis)) <= set(sets[0]) and 0 in sets[0]
+    log(f"c5: |S| = {len(sets[0])} of {nb_vis} blocks")
+    heads = {(0, h) for h in (0, 5, 17, 31)}
+    ref = O.prefill_attention(np64(inp["q"]), _KV(inp["K"]), _KV(inp["V"]), sets, wl.block,
+                              scale, q_pos0, heads=heads)
+    got = np64(out)
+    for (b, h) in heads:
+        assert_out_close(got[b, h], ref[b, h], torch.bfloat16, tag=f"c5 head {h}")
+
+
+class _KV:
+    def __init__(self, t):
+        self.t, self.shape = t, t.shape
+
+    def __getitem__(self, key):
+        b, g = key
+        return self.t[b, g].to("cpu", torch.float64).numpy()
