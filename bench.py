@@ -112,6 +112,71 @@ def time_flushed(inp, wl, bufs, reps, stream):
     return times
 
 
+def prefill_leg(steps, warmup, stream):
+    """The 128-query prefill tile at 32K: tile scoring, top-p, causal sparse attention.
+    Returns per-call µs and the attention's achieved TFLOP/s (algorithmic flops:
+    4 * d per visible (query, head, token) in the selected blocks)."""
+    wl = W.WORKLOADS["c5_prefill_32k"]
+    inp = W.make_inputs(wl, device="cuda")
+    q_pos0, Tq, nb_vis = wl.q_pos0, wl.prefill_Tq, wl.nb
+    scores = torch.empty(wl.B, nb_vis, device="cuda")
+    idx = torch.empty(wl.B, nb_vis, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(wl.B, dtype=torch.int32, device="cuda")
+    out = torch.empty(wl.B, wl.Hq, Tq, wl.d, dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(wl.d)
+
+    def run(ev=None):
+        if ev:
+            ev[0].record(stream)
+        spot.spot_prefill_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"], scores, q_pos0,
+                                       stream=stream)
+        if ev:
+            ev[1].record(stream)
+        spot.spot_select_topp(scores, idx, cnt, None, wl.p, wl.K_min, nb_vis, wl.n_sink,
+                              wl.n_rec, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        spot.spot_prefill_attn(inp["q"], inp["K"], inp["V"], idx, cnt, out, q_pos0, scale,
+                               stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for e in evs:
+            run(e)
+    torch.cuda.synchronize()
+    t = {k: statistics.fmean([e[i].elapsed_time(e[i + 1]) * 1e3 for e in evs])
+         for i, k in enumerate(["score", "topp", "attn"])}
+    sel = idx[0, : int(cnt[0])].cpu().tolist()
+    vis = 0
+    for i in range(Tq):
+        pos = q_pos0 + i
+        for blk in sel:
+            vis += max(0, min((blk + 1) * wl.block, pos + 1, wl.L) - blk * wl.block)
+    flops = 4.0 * wl.d * vis * wl.Hq
+    return {"workload": wl.name, "selected_blocks": len(sel), "visible_blocks": nb_vis,
+            "per_call_us_mean": {k: round(v, 3) for k, v in t.items()},
+            "attn_flops": flops,
+            "attn_TFLOPs": round(flops / (t["attn"] * 1e-6) / 1e12, 2),
+            "attn_frac_of_bf16_mfma_peak": round(flops / (t["attn"] * 1e-6) / 2.5e15, 4)}
+
+
+def calibration_copy():
+    """A plain 256 MiB device copy, outside every timed region: its FETCH_SIZE and
+    WRITE_SIZE counters scale the counters of the other kernels to bytes."""
+    n = 1 << 26
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n * 4
+
+
 def cpu_baseline(wl, inp, b_sample=1, heads_sample=None):
     """The fp64 oracle (scoring, dual top-p, dense masked attention) on a bounded
     sample: batch rows [0, b_sample), all heads, full L. Scaled to one whole step."""
@@ -163,6 +228,7 @@ def main():
     ap.add_argument("--flushed-reps", type=int, default=50)
     ap.add_argument("--extra-b1", action="store_true", default=True)
     ap.add_argument("--no-extra-b1", dest="extra_b1", action="store_false")
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false", default=True)
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -243,6 +309,10 @@ def main():
                                                  for k, v in p1.items()},
                             "note": "batch row 0 of the same inputs"}
         del inp1, bufs1
+    if a.prefill:
+        log("bench: prefill tile")
+        result["prefill"] = prefill_leg(max(10, a.steps // 4), 5, stream)
+    result["calibration_copy_bytes"] = calibration_copy()
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, inp, b_sample=1)

@@ -10,6 +10,7 @@ constexpr int kWave = 64;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 // bfloat16 is the upper half of a binary32: widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -42,6 +43,25 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
   o[2] = bf16_lo(a.y); o[3] = bf16_hi(a.y);
   o[4] = bf16_lo(a.z); o[5] = bf16_hi(a.z);
   o[6] = bf16_lo(a.w); o[7] = bf16_hi(a.w);
+}
+
+// The same for data read exactly once (non-temporal loads).
+__device__ __forceinline__ void load8_stream(const float* p, float* o) {
+  const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  const u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = __uint_as_float(a[i]);
+    o[4 + i] = __uint_as_float(b[i]);
+  }
+}
+__device__ __forceinline__ void load8_stream(const uint16_t* p, float* o) {
+  const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = bf16_lo(a[i]);
+    o[2 * i + 1] = bf16_hi(a[i]);
+  }
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }

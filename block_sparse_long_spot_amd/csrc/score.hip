@@ -46,8 +46,8 @@ __global__ __launch_bounds__(256) void select_score_kernel(
     if constexpr (KK == kKeyInt4) {
       const uint8_t* cp = static_cast<const uint8_t*>(sel_k) + (row * H + head) * (DIDX / 2) +
                           part * 16;
-      const uint4 c4 = *reinterpret_cast<const uint4*>(cp);
-      const uint32_t wd[4] = {c4.x, c4.y, c4.z, c4.w};
+      const u32x4_t c4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp));
+      const uint32_t wd[4] = {c4[0], c4[1], c4[2], c4[3]};
       float a = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void select_score_kernel(
       typedef typename std::conditional<KK == kKeyF32, float, uint16_t>::type KT;
       const KT* kp = static_cast<const KT*>(sel_k) + (row * H + head) * DIDX + part * CH;
       float kv[8];
-      load8(kp, kv);
+      load8_stream(kp, kv);
 #pragma unroll
       for (int n = 0; n < 8; ++n) dot = fmaf(qv[n], kv[n], dot);
     }
