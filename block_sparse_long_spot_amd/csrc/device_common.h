@@ -79,6 +79,57 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// ---- wave64 scans on the DPP network (gfx9 row_shr / row_bcast controls): each step
+// reads a neighbouring lane's register inside the VALU instruction, no LDS traffic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned long long dpp_or_zero(unsigned long long v) {
+  const uint32_t lo = dpp_or_zero<CTRL, ROW_MASK>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_or_zero<CTRL, ROW_MASK>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+// Inclusive prefix sum over the 64 lanes (lane i gets the sum of lanes 0..i).
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T x) {
+  x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8   (now a scan inside each row of 16)
+  x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x) {
+  // lanes without a valid source (or outside ROW_MASK) see their own value
+  const int xi = __float_as_int(x);
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, CTRL, ROW_MASK, 0xf, false)));
+}
+// Maximum over the 64 lanes, valid in lane 63 (a running maximum in lane order).
+__device__ __forceinline__ float wave_max_to_last(float x) {
+  x = dpp_max_step<0x111, 0xf>(x);
+  x = dpp_max_step<0x112, 0xf>(x);
+  x = dpp_max_step<0x114, 0xf>(x);
+  x = dpp_max_step<0x118, 0xf>(x);
+  x = dpp_max_step<0x142, 0xa>(x);
+  x = dpp_max_step<0x143, 0xc>(x);
+  return x;
+}
+template <typename T>
+__device__ __forceinline__ T lane_value(T x, int lane) {
+  if constexpr (sizeof(T) == 8) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
+    return static_cast<T>((static_cast<unsigned long long>(hi) << 32) | lo);
+  } else {
+    return static_cast<T>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
+  }
+}
+
 // Order-preserving map of a binary32 onto uint32 (larger float -> larger key).
 // -0.0 must be folded onto +0.0 by the caller.
 __device__ __forceinline__ uint32_t float_key(float f) {

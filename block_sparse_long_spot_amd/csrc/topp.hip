@@ -1,22 +1,25 @@
 // Dual top-p block selection (SpotAttention §2.3, Eq. 7 and Eq. 8).
 //
-// One work-group per query row. Every thread keeps EPT consecutive blocks in
-// registers: the score, an order-preserving 32-bit key of it, and the block's
-// softmax mass in 2^-38 fixed point (integer sums are exact, so nothing depends on
-// the order in which threads add).
+// One work-group per query row; latency-bound (a few thousand scores), so the design
+// minimises the chain of dependent steps: 7 work-group barriers, wave-level scans on
+// the DPP network, one 64-bit LDS atomic per block. Every thread keeps EPT consecutive
+// blocks in registers: the score, an order-preserving 32-bit key of it, and the
+// block's softmax mass exp(s - max) in 2^-29 fixed point (integer sums are exact, so
+// nothing depends on the order in which threads add).
 //
 //   1. reserved blocks R (sink prefix, recency suffix) are set aside;
-//   2. max and sum of exp(s - max) over the residual blocks (Eq. 7's softmax);
-//   3. one coarse histogram of count and mass over 2048 bins of width 1/64 in
-//      (max - s) (bin order = score order), turned into prefix sums. It locates the
-//      bin where the cumulative mass reaches p*Z (the nucleus cut) and, because the
-//      clamp k = clamp(k_p, K_min - r, K_max - r) is monotone, also decides whether
-//      k is already known or falls inside that same bin;
-//   4. only the bin that holds the k-th block needs an exact order: its blocks
-//      (usually a handful) are gathered and one wave ranks them by (score desc,
-//      index asc), accumulating mass in that order to finish k_p when needed. A bin
-//      with more than 64 blocks (dense ties) falls back to an exact radix select,
-//      11+11+10 bits of the key, restricted to that bin;
+//   2. max over the residual blocks, then each residual block's mass (Eq. 7);
+//   3. one coarse histogram over 2048 bins of width 1/64 in (max - s) (bin order =
+//      score order) holding (count << 44) | mass per bin, and its prefix sums. One pass
+//      over the prefix finds the bin where the cumulative mass reaches p*Z (the nucleus
+//      cut) and the bins of the two block counts the clamp
+//      k = clamp(k_p, K_min - r, K_max - r) can produce; as the clamp is monotone this
+//      decides whether k is already known or falls inside the cut bin;
+//   4. only the bin holding the k-th block needs an exact order: its blocks (usually a
+//      handful) are gathered and one wave ranks them by (score desc, index asc),
+//      accumulating mass in that order to finish k_p when needed. A bin with more than
+//      64 blocks (dense ties) falls back to an exact radix select, 11+11+10 bits of
+//      the key, restricted to that bin;
 //   5. blocks in earlier bins, the chosen ones of the boundary bin, and R form S; a
 //      block-wide scan writes it in ascending order.
 #include "device_common.h"
@@ -30,88 +33,72 @@ typedef unsigned long long u64;
 constexpr int kCoarseBins = 2048;
 constexpr float kBinsPerNat = 64.f;  // coarse bin width: 1/64 of a unit of log-mass
 constexpr int kRankMax = 64;         // boundary bins up to this size are ranked by one wave
+constexpr int kMassBits = 29;        // fixed point of a block's mass (<= 1.0)
+constexpr int kCntShift = 44;        // count field of a packed bin: 16384 blocks * 2^29 < 2^44
+constexpr u64 kMassMask = (1ull << kCntShift) - 1;
 
 template <int NT>
 struct ToppSmem {
-  uint32_t hc[kCoarseBins];          // histograms (coarse pass, then the fallback passes)
+  u64 hist[kCoarseBins];             // packed coarse histogram (count << 44) | mass
+  uint32_t hc[kCoarseBins];          // fallback radix histograms
   u64 hm[kCoarseBins];
-  uint32_t pc[kCoarseBins + 1];      // exclusive prefix over bins: count and mass above
-  u64 pm[kCoarseBins + 1];
   uint32_t gk[kRankMax];             // gathered boundary-bin blocks: key, index, mass
   int32_t gi[kRankMax];
   u64 gm[kRankMax];
   int32_t gsel[kRankMax];            // 1 if the gathered block is chosen
   int32_t ng;
-  int32_t found[3];                  // bins of the mass target and two count targets
+  // bins found by the prefix pass: [0] mass target, [1] low count target, [2] high
+  int32_t f_bin[3];
+  u64 f_pre[3];                      // packed prefix (blocks and mass above the bin)
+  u64 f_cnt[3];                      // blocks in the bin
   int32_t k_final;
   u64 inbin_mass;                    // mass of the chosen blocks of the boundary bin
-  u64 wa[NT / 64];
-  u64 wb[NT / 64];
+  u64 wt[NT / 64];                   // per-wave totals
+  u64 wt2[NT / 64];
   float wf[NT / 64];
   uint32_t r_digit;
   u64 r_cnt_above;
   u64 r_mass_above;
 };
 
+// Sum over the work-group (one barrier; `slot` must not be in use).
 template <int NT>
-__device__ float block_max(float v, ToppSmem<NT>& sh) {
+__device__ u64 block_sum(u64 v, u64* slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  if (lane == 0) sh.wf[wave] = v;
-  __syncthreads();
-  float r = sh.wf[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, sh.wf[w]);
-  __syncthreads();
-  return r;
-}
-
-template <int NT>
-__device__ u64 block_sum(u64 v, ToppSmem<NT>& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-  if (lane == 0) sh.wa[wave] = v;
+  const u64 w = lane_value(wave_incl_scan(v), 63);
+  if (lane == 0) slot[wave] = w;
   __syncthreads();
   u64 r = 0;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) r += sh.wa[w];
-  __syncthreads();
+  for (int i = 0; i < NT / 64; ++i) r += slot[i];
   return r;
 }
 
-// Exclusive prefix sum in thread order; also returns the total.
+// Exclusive prefix sum in thread order, and the total (one barrier).
 template <int NT>
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, ToppSmem<NT>& sh) {
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, u64* slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh.wa[wave] = x;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) slot[wave] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
-    const uint32_t t = static_cast<uint32_t>(sh.wa[w]);
-    if (w < wave) before += t;
+    const uint32_t t = static_cast<uint32_t>(slot[w]);
+    before += w < wave ? t : 0u;
     tot += t;
   }
-  __syncthreads();
   total = tot;
   return before + x - v;
 }
 
-// Radix select over the residual keys, from the largest key down.
+// Radix select over the active keys, from the largest key down (fallback path).
 // BY_MASS: stop where the cumulative mass reaches `target`; otherwise where the
 // cumulative count does. Outputs the selected key, the count and mass strictly above
 // it, and the count and mass of its tie group.
 template <int NT, int EPT, bool BY_MASS>
 __device__ void radix_select(const uint32_t (&key)[EPT], const u64 (&mass)[EPT],
-                             const bool (&res)[EPT], u64 target, ToppSmem<NT>& sh,
+                             const bool (&act)[EPT], u64 target, ToppSmem<NT>& sh,
                              uint32_t& tau, u64& cnt_above, u64& mass_above, u64& tie_cnt,
                              u64& tie_mass) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -136,7 +123,7 @@ __device__ void radix_select(const uint32_t (&key)[EPT], const u64 (&mass)[EPT],
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      if (res[e] && (key[e] & pmask) == prefix) {
+      if (act[e] && (key[e] & pmask) == prefix) {
         const uint32_t d = (key[e] >> shift) & dmask;
         atomicAdd(&sh.hc[d], 1u);
         if (BY_MASS) atomicAdd(&sh.hm[d], mass[e]);
@@ -163,16 +150,16 @@ __device__ void radix_select(const uint32_t (&key)[EPT], const u64 (&mass)[EPT],
       }
     }
     if (lane == 0) {
-      sh.wa[wave] = sc;
-      sh.wb[wave] = sm;
+      sh.wt[wave] = sc;
+      sh.wt2[wave] = sm;
     }
     __syncthreads();
     u64 hc_hi = 0, hm_hi = 0;  // totals of the waves holding higher bins
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
       if (w > wave) {
-        hc_hi += sh.wa[w];
-        hm_hi += sh.wb[w];
+        hc_hi += sh.wt[w];
+        hm_hi += sh.wt2[w];
       }
     }
     const u64 ec = sc - lc + hc_hi;  // count in bins above this thread's bins
@@ -208,15 +195,15 @@ __device__ void radix_select(const uint32_t (&key)[EPT], const u64 (&mass)[EPT],
   __syncthreads();
 }
 
-// exp(s - mx) in 2^-38 fixed point. s - mx and its split into an integer and a
+// exp(s - mx) in 2^-29 fixed point. s - mx and its split into an integer and a
 // fraction are exact in fp64; only the fractional power of two is evaluated in fp32
 // (about 1 ulp), so the mass carries a relative error near 1e-7.
 __device__ __forceinline__ u64 fixed_mass(float s, float mx) {
   const double t = (static_cast<double>(s) - static_cast<double>(mx)) * 1.4426950408889634;
   const double n = floor(t);
-  if (n < -80.0) return 0ull;
-  const float f = static_cast<float>(t - n);                 // in [0, 1)
-  const float v = ldexpf(exp2f(f), static_cast<int>(n) + 38);  // <= 2^38
+  if (n < -60.0) return 0ull;
+  const float f = static_cast<float>(t - n);                            // in [0, 1)
+  const float v = ldexpf(exp2f(f), static_cast<int>(n) + kMassBits);   // <= 2^29
   return static_cast<u64>(__float2ll_rn(v));
 }
 
@@ -228,6 +215,7 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
                                                          float p, int K_min, int K_max,
                                                          int n_sink, int n_rec) {
   constexpr int BPT = kCoarseBins / NT;
+  constexpr int NW = NT / 64;
   __shared__ ToppSmem<NT> sh;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -240,36 +228,57 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   // k as a function of the nucleus size: monotone in k_p
   auto clampk = [&](int x) { return min(max(x, lo), hi_cap); };
 
+  // ---- 1. scores into registers; clear the histogram
   float s[EPT];
   uint32_t key[EPT];
   bool valid[EPT], res[EPT];
+  if ((nb & 3) == 0 && (EPT & 3) == 0) {
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const int i = tid * EPT + e;
+      const float4 v4 = i < nb ? *reinterpret_cast<const float4*>(row + i)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      s[e] = v4.x;
+      s[e + 1] = v4.y;
+      s[e + 2] = v4.z;
+      s[e + 3] = v4.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = tid * EPT + e;
+      s[e] = i < nb ? row[i] : 0.f;
+    }
+  }
+  float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const int i = tid * EPT + e;
     valid[e] = i < nb;
-    float v = valid[e] ? row[i] : 0.f;
-    if (v == 0.f) v = 0.f;  // fold -0.0 onto +0.0
-    s[e] = v;
-    key[e] = float_key(v);
+    if (s[e] == 0.f) s[e] = 0.f;  // fold -0.0 onto +0.0
+    key[e] = float_key(s[e]);
     res[e] = valid[e] && i >= rs && i < nb - rr;
+    if (res[e]) mx = fmaxf(mx, s[e]);
   }
-  for (int i = tid; i < kCoarseBins; i += NT) {
-    sh.hc[i] = 0;
-    sh.hm[i] = 0;
-  }
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) sh.hist[tid * BPT + i] = 0;
   if (tid == 0) {
     sh.ng = 0;
-    sh.found[0] = sh.found[1] = sh.found[2] = 0;
     sh.inbin_mass = 0;
-  }
-
-  float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (res[e]) mx = fmaxf(mx, s[e]);
-  mx = block_max<NT>(mx, sh);  // also orders the clears above
-
-  // softmax mass in fixed point, coarse bin, histogram
+    for (int t = 0; t < 3; ++t) {
+      sh.f_bin[t] = 0;
+      sh.f_pre[t] = 0;
+      sh.f_cnt[t] = 0;
+    }
+  }
+  // ---- 2. residual max, masses, coarse bins, histogram
+  mx = wave_max_to_last(mx);
+  if (lane == 63) sh.wf[wave] = mx;
+  __syncthreads();  // barrier 1
+  mx = sh.wf[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, sh.wf[w]);
   u64 mass[EPT];
   int cb[EPT];
 #pragma unroll
@@ -279,111 +288,108 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
     if (res[e]) {
       mass[e] = fixed_mass(s[e], mx);
       cb[e] = static_cast<int>(fminf((mx - s[e]) * kBinsPerNat, kCoarseBins - 1.f));
-      atomicAdd(&sh.hc[cb[e]], 1u);
-      atomicAdd(&sh.hm[cb[e]], mass[e]);
+      atomicAdd(&sh.hist[cb[e]], (1ull << kCntShift) | mass[e]);
     }
   }
-  __syncthreads();
-  // exclusive prefix over bins in ascending bin order (= descending score)
-  {
-    const int b0 = tid * BPT;
-    u64 lc = 0, lm = 0;
+  __syncthreads();  // barrier 2
+  // ---- 3. prefix over the bins (ascending bin = descending score)
+  u64 hb[BPT];
+  u64 loc = 0;
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      lc += sh.hc[b0 + i];
-      lm += sh.hm[b0 + i];
-    }
-    u64 ic = lc, im = lm;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const u64 yc = __shfl_up(ic, o, 64);
-      const u64 ym = __shfl_up(im, o, 64);
-      if (lane >= o) {
-        ic += yc;
-        im += ym;
-      }
-    }
-    if (lane == 63) {
-      sh.wa[wave] = ic;
-      sh.wb[wave] = im;
-    }
-    __syncthreads();
-    u64 oc = 0, om = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w)
-      if (w < wave) {
-        oc += sh.wa[w];
-        om += sh.wb[w];
-      }
-    u64 rc = oc + ic - lc, rm = om + im - lm;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      sh.pc[b0 + i] = static_cast<uint32_t>(rc);
-      sh.pm[b0 + i] = rm;
-      rc += sh.hc[b0 + i];
-      rm += sh.hm[b0 + i];
-    }
-    if (tid == NT - 1) {
-      sh.pc[kCoarseBins] = static_cast<uint32_t>(rc);
-      sh.pm[kCoarseBins] = rm;
-    }
-    __syncthreads();
+  for (int i = 0; i < BPT; ++i) {
+    hb[i] = sh.hist[tid * BPT + i];
+    loc += hb[i];
   }
-  const u64 Z = sh.pm[kCoarseBins];
-
-  // decide k, or the bin where it is decided. One pass finds the bins of the mass
-  // target and of the two count targets the clamp can produce.
+  const u64 incl = wave_incl_scan(loc);
+  if (lane == 63) sh.wt[wave] = incl;
+  __syncthreads();  // barrier 3
+  u64 before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const u64 t = sh.wt[w];
+    before += w < wave ? t : 0ull;
+    total += t;
+  }
+  const u64 Z = total & kMassMask;
+  u64 T = 0;  // mass target of the nucleus cut
+  int tl = 0, th = 0;
   int k = 0;
-  int bk = -1;           // bin holding the k-th residual block in score order
-  bool need_kp = false;  // k still depends on the exact nucleus size inside bin bk
-  u64 T = 0;
   if (n_res > 0) {
-    int tl = min(max(lo, 1), hi_cap), th = hi_cap;  // count targets (0 = none)
     if (p >= 1.f || p <= 0.f) {
       k = clampk(p >= 1.f ? n_res : 0);
       tl = k;
-      th = 0;
     } else {
       T = static_cast<u64>(ceil(static_cast<double>(p) * static_cast<double>(Z)));
       if (T == 0) T = 1;
+      tl = min(max(lo, 1), hi_cap);
+      th = hi_cap;
     }
+  }
+  {
+    u64 P = before + incl - loc;  // packed prefix above this thread's first bin
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
-      const int bb = tid * BPT + i;
-      if (T > 0 && sh.pm[bb] < T && T <= sh.pm[bb + 1]) sh.found[0] = bb;
-      if (sh.pc[bb] < (uint32_t)tl && (uint32_t)tl <= sh.pc[bb + 1]) sh.found[1] = bb;
-      if (sh.pc[bb] < (uint32_t)th && (uint32_t)th <= sh.pc[bb + 1]) sh.found[2] = bb;
+      const int bin = tid * BPT + i;
+      const u64 pc = P >> kCntShift, pm = P & kMassMask;
+      const u64 c = hb[i] >> kCntShift, m = hb[i] & kMassMask;
+      if (T > 0 && pm < T && T <= pm + m) {
+        sh.f_bin[0] = bin;
+        sh.f_pre[0] = P;
+        sh.f_cnt[0] = c;
+      }
+      if (tl > 0 && pc < (u64)tl && (u64)tl <= pc + c) {
+        sh.f_bin[1] = bin;
+        sh.f_pre[1] = P;
+        sh.f_cnt[1] = c;
+      }
+      if (th > 0 && pc < (u64)th && (u64)th <= pc + c) {
+        sh.f_bin[2] = bin;
+        sh.f_pre[2] = P;
+        sh.f_cnt[2] = c;
+      }
+      P += hb[i];
     }
-    __syncthreads();
+  }
+  __syncthreads();  // barrier 4
+  // ---- decide k, or the bin where it is decided
+  int bk = -1;           // bin holding the k-th residual block in score order
+  int fs = 0;            // which found slot describes bin bk
+  bool need_kp = false;  // k still depends on the exact nucleus size inside bin bk
+  if (n_res > 0) {
     if (T == 0) {
-      if (k > 0) bk = sh.found[1];
+      if (k > 0) {
+        bk = sh.f_bin[1];
+        fs = 1;
+      }
     } else {
-      const int bm = sh.found[0];
-      const int A = static_cast<int>(sh.pc[bm]);
-      const int C = static_cast<int>(sh.pc[bm + 1]) - A;
-      const int k1 = clampk(A + 1), k2 = clampk(A + C);
+      const int A0 = static_cast<int>(sh.f_pre[0] >> kCntShift);
+      const int C0 = static_cast<int>(sh.f_cnt[0]);
+      const int k1 = clampk(A0 + 1), k2 = clampk(A0 + C0);
       if (k1 != k2) {
-        bk = bm;
+        bk = sh.f_bin[0];
         need_kp = true;
       } else {
         k = k1;
-        if (k > 0) bk = k == th ? sh.found[2] : (k == tl ? sh.found[1] : bm);
+        fs = k == th ? 2 : (k == tl ? 1 : 0);
+        if (k > 0) bk = sh.f_bin[fs];
       }
     }
   }
+  const int A = bk >= 0 ? static_cast<int>(sh.f_pre[fs] >> kCntShift) : 0;
+  const int C = bk >= 0 ? static_cast<int>(sh.f_cnt[fs]) : 0;
+  const u64 PM = bk >= 0 ? (sh.f_pre[fs] & kMassMask) : 0;
 
-  // exact order inside the boundary bin
+  // ---- 4. exact order inside the boundary bin
   uint32_t tau = 0;
   u64 take = 0;  // fallback: blocks of key tau to take, lowest index first
   int slot[EPT];
   bool fallback = false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) slot[e] = 0;
   if (bk >= 0) {
-    const int A = static_cast<int>(sh.pc[bk]);
-    const int C = static_cast<int>(sh.pc[bk + 1]) - A;
     if (C <= kRankMax) {
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        slot[e] = -1;
         if (cb[e] == bk) {
           const int sl = atomicAdd(&sh.ng, 1);
           slot[e] = sl;
@@ -392,42 +398,38 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
           sh.gm[sl] = mass[e];
         }
       }
-      __syncthreads();
+      __syncthreads();  // barrier 5
       if (wave == 0) {
         const bool act = lane < C;
         const uint32_t mk = act ? sh.gk[lane] : 0u;
         const int mi = act ? sh.gi[lane] : 0x7fffffff;
         const u64 mm = act ? sh.gm[lane] : 0ull;
-        const uint32_t mlo = static_cast<uint32_t>(mm), mhi = static_cast<uint32_t>(mm >> 32);
         int rank = 0;
         u64 cm = mm;  // mass of the blocks ranked at or before this one
         for (int j = 0; j < C; ++j) {  // j is uniform: broadcast block j from lane j
           const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
           const int ij = __builtin_amdgcn_readlane(mi, j);
-          const u64 gj = (static_cast<u64>(__builtin_amdgcn_readlane(mhi, j)) << 32) |
-                         __builtin_amdgcn_readlane(mlo, j);
-          const bool before = kj > mk || (kj == mk && ij < mi);
-          rank += before ? 1 : 0;
-          cm += before ? gj : 0ull;
+          const u64 gj = lane_value(mm, j);
+          const bool before_me = kj > mk || (kj == mk && ij < mi);
+          rank += before_me ? 1 : 0;
+          cm += before_me ? gj : 0ull;
         }
         int kk = k;
         if (need_kp) {
-          int cand = (act && sh.pm[bk] + cm >= T) ? A + rank + 1 : 0x7fffffff;
+          int cand = (act && PM + cm >= T) ? A + rank + 1 : 0x7fffffff;
 #pragma unroll
           for (int o = 1; o < 64; o <<= 1) cand = min(cand, __shfl_xor(cand, o, 64));
           kk = clampk(cand);
         }
         const bool chosen = act && rank < kk - A;
         if (act) sh.gsel[lane] = chosen ? 1 : 0;
-        u64 im = chosen ? mm : 0ull;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) im += __shfl_xor(im, o, 64);
+        const u64 im = lane_value(wave_incl_scan(chosen ? mm : 0ull), 63);
         if (lane == 0) {
           sh.k_final = kk;
           sh.inbin_mass = im;
         }
       }
-      __syncthreads();
+      __syncthreads();  // barrier 6
       k = sh.k_final;
     } else {
       // dense boundary bin: exact radix select over the keys of that bin only
@@ -438,9 +440,9 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
       u64 ca, ma, tc, tm;
       bool decided = false;
       if (need_kp) {
-        const u64 tgt = T - sh.pm[bk];  // > 0: bin bk holds the mass crossing
+        const u64 tgt = T - PM;  // > 0: bin bk holds the mass crossing
         radix_select<NT, EPT, true>(key, mass, act, tgt, sh, tau, ca, ma, tc, tm);
-        const u64 m_tau = tm / tc;      // every block of key tau has the same mass
+        const u64 m_tau = tm / tc;  // every block of key tau has the same mass
         u64 c = (tgt - ma + m_tau - 1) / m_tau;
         c = c < 1 ? 1 : (c > tc ? tc : c);
         const int kp = A + static_cast<int>(ca + c);
@@ -458,14 +460,15 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
     }
   }
 
-  // membership: earlier bins, the chosen blocks of bin bk, and the reserved set
+  // ---- 5. membership and ascending compaction
   uint32_t tie_rank = 0;
   if (fallback) {
-    uint32_t tl = 0;
+    uint32_t tl2 = 0;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) tl += (cb[e] == bk && key[e] == tau) ? 1u : 0u;
+    for (int e = 0; e < EPT; ++e) tl2 += (cb[e] == bk && key[e] == tau) ? 1u : 0u;
     uint32_t tt;
-    tie_rank = block_excl_scan<NT>(tl, tt, sh);
+    tie_rank = block_excl_scan<NT>(tl2, tt, sh.wt);
+    __syncthreads();
   }
   bool sel[EPT];
   uint32_t sel_local = 0;
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
     if (pick) mass_sel += mass[e];
   }
   uint32_t cnt;
-  uint32_t pos = block_excl_scan<NT>(sel_local, cnt, sh);
+  uint32_t pos = block_excl_scan<NT>(sel_local, cnt, sh.wt2);  // barrier 7
   int32_t* out = sel_idx + (size_t)b * K_max;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -501,7 +504,11 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   for (int j = static_cast<int>(cnt) + tid; j < K_max; j += NT) out[j] = -1;
   if (sel_mass != nullptr) {
     u64 ms = 0;
-    if (k > 0 && bk >= 0) ms = fallback ? block_sum<NT>(mass_sel, sh) : sh.pm[bk] + sh.inbin_mass;
+    if (fallback) {
+      ms = block_sum<NT>(mass_sel, sh.wt);
+    } else if (k > 0 && bk >= 0) {
+      ms = PM + sh.inbin_mass;
+    }
     if (tid == 0)
       sel_mass[b] = Z > 0 ? static_cast<float>(static_cast<double>(ms) / static_cast<double>(Z))
                           : 0.f;

@@ -391,3 +391,29 @@ def test_decode_step_bit_reproducible():
         outs.append((bufs.scores.cpu(), bufs.sel_idx.cpu(), bufs.out.cpu()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, reproduces the eager result bit for bit."""
+    wl = W.WORKLOADS["c2_32k_b4"]
+    inp = W.make_inputs(wl, device=DEV, seed=11)
+    eager = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+    decode_step(inp, wl, eager)
+    torch.cuda.synchronize()
+    ref = (eager.sel_idx.clone(), eager.sel_cnt.clone(), eager.out.clone())
+    bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        decode_step(inp, wl, bufs, stream=stream)
+    for i in range(4):
+        bufs.out.fill_(float("nan"))
+        bufs.sel_idx.fill_(12345)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        decode_step(inp, wl, eager)           # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(bufs.sel_idx, ref[0]) and torch.equal(bufs.sel_cnt, ref[1])
+        assert torch.equal(bufs.out, ref[2]), f"replay {i}"
