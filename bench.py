@@ -12,9 +12,11 @@ baseline is the fp64 oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -60,6 +62,24 @@ def byte_budget(wl, B, tokens):
     algorithmic = selk + B * wl.H_idx * (wl.d_idx * es + 4) + tokens * wl.Hkv * wl.d * 2 * es \
         + B * wl.Hq * wl.d * 2 * es
     return {"score": score, "topp": topp, "attn": attn, "step": algorithmic}
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_c3_128k_b8.md")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_long_spot_amd", "csrc", "attn.hip")
+
+
+def profiled_traffic():
+    """HBM bytes per sparse-attention call from the committed rocprofv3 counter summary,
+    or None when the attention source changed since those counters were taken."""
+    try:
+        fields = dict(re.findall(r"^(\w+): (\S+)$", open(PROFILE).read(), re.M))
+        digest = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if fields.get("source_sha256_16") != digest:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def time_steps(inp, wl, bufs, steps, warmup, stream):
@@ -236,9 +256,10 @@ def cpu_baseline(wl, inp, b_sample=1, heads_sample=None):
     B = inp["q"].shape[0]
     return {"value": dt * 1e6 * B / b_sample, "unit": "us", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"batch rows 0..{b_sample - 1} of {B} (all {wl.Hq} heads, L={wl.L}), "
-                      f"{dt:.2f} s measured, scaled x{B / b_sample:g} to one step; includes "
-                      "device-to-host copies of the sampled K/V rows"}
+            "sample": f"batch rows 0..{b_sample - 1} of {B} (all {wl.Hq} heads, L={wl.L}): "
+                      f"{dt:.2f} s measured, scaled x{B / b_sample:g} to one step; fp64 "
+                      "scoring, sort-based top-p and dense masked attention over all L keys, "
+                      "including the device-to-host copy of each K/V row it reads"}
 
 
 def main():
@@ -303,9 +324,9 @@ def main():
                    "selector_cache": wl.sel_k_dtype, "p": wl.p, "K_min": wl.K_min,
                    "K_max": wl.K_max, "n_sink": wl.n_sink, "n_rec": wl.n_rec,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "attn_mfma (spot_sparse_attn: split-K runs and their merge in one kernel)",
+        "roofline": {"bound": "hbm", "kernel": "spot_sparse_attn call: attn_mfma (split-K runs) + attn_combine (merge)",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(),
                      "bytes_per_launch": budget["attn"], "avg_launch_us": round(mean["attn"], 3)},
         "step_hbm": {"algorithmic_bytes": budget["step"],
                      "GBps": round(budget["step"] / (us_step * 1e-6) / 1e9, 1),
@@ -347,7 +368,7 @@ def main():
     result["calibration_copy_bytes"] = calibration_copy()
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, inp, b_sample=1)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, b_sample=wl.B)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -214,11 +214,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   const int nbl = (L + kBlk - 1) / kBlk;
   const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
   const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
-  // block of list entry j, or -1 for an entry outside [0, nbl) (ignored)
-  auto block_of = [&](int j) {
-    const int blk = sel_idx[(size_t)b * K_max + j];
-    return (blk < 0 || blk >= nbl) ? -1 : blk;
-  };
+  // This wave's list entries j0 + wave + i*NW, one per lane, read in one instruction
+  // (bps / NW <= 64); block i is then a register read, not a load on the critical path.
+  const int n_mine = (j1 - j0 - wave + NW - 1) / NW;
+  int my_blk = -1;
+  if (lane < n_mine) {
+    const int e = sel_idx[(size_t)b * K_max + j0 + wave + lane * NW];
+    my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
+  }
+  auto block_of = [&](int i) { return __builtin_amdgcn_readlane(my_blk, i); };
   // K rows of a block in the B-operand layout: lane (token row, k-group kg)
   auto load_k = [&](int blk, bf16x8_t (&kb)[4][KS]) {
     const int t0 = max(blk, 0) * kBlk;
@@ -334,25 +338,22 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Software pipeline over this wave's blocks (entries j0 + wave, + NW, ...): the next
-  // block's K loads are in flight while the current block is consumed.
-  int j = j0 + wave;
-  int blk = j < j1 ? block_of(j) : -1;
+  // Software pipeline over this wave's blocks: the next block's K loads are in flight
+  // while the current block is consumed.
+  int blk = n_mine > 0 ? block_of(0) : -1;
   bf16x8_t kb[4][KS];
-  if (j < j1) load_k(blk, kb);
-  while (j < j1) {
+  if (n_mine > 0) load_k(blk, kb);
+  for (int i = 0; i < n_mine; ++i) {
     u32x4_t vv[TPL];
     load_v(blk, vv);
-    const int jn = j + NW;
-    const int blkn = jn < j1 ? block_of(jn) : -1;
+    const int blkn = i + 1 < n_mine ? block_of(i + 1) : -1;
     bf16x8_t kn[4][KS];
-    if (jn < j1) load_k(blkn, kn);
+    if (i + 1 < n_mine) load_k(blkn, kn);
     if (blk >= 0) consume(blk, kb, vv);
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
       for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
-    j = jn;
     blk = blkn;
   }
 

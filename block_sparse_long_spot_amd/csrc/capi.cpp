@@ -152,7 +152,8 @@ int spot_prefill_attn(const void* q, const void* k_cache, const void* v_cache, i
   if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
   if ((long)q_pos0 + Tq > L) return SPOT_ERR_INVALID;
   const int G = Hq / Hkv;
-  if (kv_dtype != SPOT_BF16 || d != 128 || block != 64 || Tq > 128) return SPOT_ERR_UNSUPPORTED;
+  if (kv_dtype != SPOT_BF16 || d != 128 || block != 64 || Tq > 128 || K_max > 8192)
+    return SPOT_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
   if (B > kMaxGrid || Hq > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
   return from_hip(spot::launch_prefill_attn(q, k_cache, v_cache, sel_idx, sel_cnt, K_max, out, B,

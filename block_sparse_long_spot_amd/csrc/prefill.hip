@@ -28,14 +28,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- tile scoring
-// Wave = 16 blocks (columns) x all Tq queries (rows, 16 per MFMA row tile).
-template <int DIDX>
-__global__ __launch_bounds__(64) void prefill_score_kernel(
+// Work-group = 16 blocks (columns) x all Tq queries; its 4 waves take interleaved row
+// tiles of 16 queries and combine their column maxima through LDS. Per selector key,
+// a wave holds the key operands of every head in registers and issues the query
+// operands of a row tile together, so the MFMAs wait on one round of loads.
+template <int DIDX, int H>
+__global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
     const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int Tq, int q_pos0,
-    int nb_cache, int nb_vis, int kpb, int H, int block) {
+    int nb_cache, int nb_vis, int kpb, int block) {
   constexpr int KS = DIDX / 32;
-  const int lane = threadIdx.x;
+  constexpr int NWV = 4;
+  __shared__ float colmax[NWV][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int b = blockIdx.y;
   const int blk0 = blockIdx.x * 16;
@@ -46,21 +51,88 @@ __global__ __launch_bounds__(64) void prefill_score_kernel(
   const float* wb = sel_w + (size_t)b * Tq * H;
   float best = -INFINITY;  // max over (visible query, key j) for column blk0 + col
   for (int j = 0; j < kpb; ++j) {
+    bf16x8_t kop[H][KS];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const uint16_t* kp =
+          sel_k + ((((size_t)b * nb_cache + blk_c) * kpb + j) * H + h) * DIDX + kg * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kop[h][s] = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
+    }
+    for (int rt = wave; rt < n_rt; rt += NWV) {
+      const int qr = min(rt * 16 + col, Tq - 1);   // A-operand row of this lane
+      bf16x8_t qop[H][KS];
+      float wq[H][4];
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qop[h][s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wq[h][r] = wb[(size_t)min(rt * 16 + kg * 4 + r, Tq - 1) * H + h];
+      }
+      floatx4_t tot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        floatx4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[h][s], kop[h][s], c, 0, 0, 0);
+        // c[r] = S_h[query rt*16 + kg*4 + r][column col]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[r] += wq[h][r] * fmaxf(c[r], 0.f);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = rt * 16 + kg * 4 + r;
+        const bool vis = qi < Tq && (long)blk * block <= (long)q_pos0 + qi;
+        if (vis) best = fmaxf(best, tot[r]);
+      }
+    }
+  }
+  // lanes col, col+16, col+32, col+48 hold the same column; then across the waves
+  best = fmaxf(best, shfl_xor_f(best, 16));
+  best = fmaxf(best, shfl_xor_f(best, 32));
+  if (kg == 0) colmax[wave][col] = best;
+  __syncthreads();
+  if (wave == 0 && kg == 0 && blk < nb_vis) {
+    float m = colmax[0][col];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) m = fmaxf(m, colmax[w][col]);
+    scores[(size_t)b * nb_vis + blk] = m;
+  }
+}
+
+// Any H: heads looped at run time (slower path for selector head counts other than 4).
+template <int DIDX>
+__global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
+    const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
+    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int Tq, int q_pos0,
+    int nb_cache, int nb_vis, int kpb, int H, int block) {
+  constexpr int KS = DIDX / 32;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, kg = lane >> 4;
+  const int b = blockIdx.y;
+  const int blk = blockIdx.x * 16 + col;
+  const int blk_c = min(blk, nb_vis - 1);
+  const int n_rt = (Tq + 15) / 16;
+  const uint16_t* qb = sel_q + (size_t)b * Tq * H * DIDX;
+  const float* wb = sel_w + (size_t)b * Tq * H;
+  float best = -INFINITY;
+  for (int j = 0; j < kpb; ++j) {
     for (int rt = 0; rt < n_rt; ++rt) {
       floatx4_t tot = {0.f, 0.f, 0.f, 0.f};
       for (int h = 0; h < H; ++h) {
         const uint16_t* kp =
             sel_k + ((((size_t)b * nb_cache + blk_c) * kpb + j) * H + h) * DIDX + kg * 8;
-        const int qr = min(rt * 16 + col, Tq - 1);  // A-operand row of this lane
+        const int qr = min(rt * 16 + col, Tq - 1);
         const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
         floatx4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
-          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, c, 0, 0, 0);
-        }
-        // c[r] = S_h[query rt*16 + kg*4 + r][column col]
+        for (int s = 0; s < KS; ++s)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8_t*>(qp + s * 32),
+              *reinterpret_cast<const bf16x8_t*>(kp + s * 32), c, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qi = min(rt * 16 + kg * 4 + r, Tq - 1);
@@ -75,7 +147,6 @@ __global__ __launch_bounds__(64) void prefill_score_kernel(
       }
     }
   }
-  // lanes col, col+16, col+32, col+48 hold the same column
   best = fmaxf(best, shfl_xor_f(best, 16));
   best = fmaxf(best, shfl_xor_f(best, 32));
   if (kg == 0 && blk < nb_vis) scores[(size_t)b * nb_vis + blk] = best;
@@ -84,6 +155,7 @@ __global__ __launch_bounds__(64) void prefill_score_kernel(
 // ---------------------------------------------------------------- attention
 constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
 constexpr int kVPad = 68;   // V^T row stride in bf16 (128 B + 8 B)
+constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS)
 
 template <int G>
 __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
@@ -95,6 +167,7 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
   constexpr int NT = G * 64;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kKPad];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kVPad];
+  __shared__ int32_t sel_s[kMaxPrefillList];
 
   const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -123,25 +196,56 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
   const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
   const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
 
-  for (int j = 0; j < cnt; ++j) {
-    const int blk = sel_idx[(size_t)b * K_max + j];
-    if (blk < 0 || blk >= nbl || blk * kBlk > last_pos) continue;  // uniform
+  // the selected list, staged once in LDS (it is read block after block below)
+  for (int i = tid; i < cnt; i += NT) sel_s[i] = sel_idx[(size_t)b * K_max + i];
+  __syncthreads();
+  // next list entry at or after j whose block exists and is not after the whole tile
+  auto next_block = [&](int j, int& blk) {
+    for (; j < cnt; ++j) {
+      blk = sel_s[j];
+      if (blk >= 0 && blk < nbl && blk * kBlk <= last_pos) return j;
+    }
+    return cnt;
+  };
+  // K and V of one block pass through registers (kbuf, vbuf) on their way to LDS, so
+  // the next block's loads are in flight while the current one is consumed
+  constexpr int CPT = kBlk * (D / 8) / NT;  // 16-byte chunks per thread per tensor
+  u32x4_t kbuf[CPT], vbuf[CPT];
+  auto fetch = [&](int blk) {
     const int t0 = blk * kBlk;
-    // stage K (row-major) and V (transposed) of this block
-    for (int c = tid; c < kBlk * (D / 8); c += NT) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
       const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
       const int tok = min(t0 + t, L - 1);
-      const uint4 kv = *reinterpret_cast<const uint4*>(Kg + (size_t)tok * D + d0);
-      *reinterpret_cast<uint4*>(&Ks[t * kKPad + d0]) = kv;
-      const uint4 vv = *reinterpret_cast<const uint4*>(Vg + (size_t)tok * D + d0);
-      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+      kbuf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kg + (size_t)tok * D + d0));
+      vbuf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + d0));
+    }
+  };
+  auto stage = [&]() {  // K row-major, V transposed
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Vt[(d0 + 2 * i) * kVPad + t] = static_cast<uint16_t>(w4[i] & 0xffffu);
-        Vt[(d0 + 2 * i + 1) * kVPad + t] = static_cast<uint16_t>(w4[i] >> 16);
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      *reinterpret_cast<u32x4_t*>(&Ks[t * kKPad + d0]) = kbuf[i];
+      const uint32_t w4[4] = {vbuf[i][0], vbuf[i][1], vbuf[i][2], vbuf[i][3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(d0 + 2 * e) * kVPad + t] = static_cast<uint16_t>(w4[e] & 0xffffu);
+        Vt[(d0 + 2 * e + 1) * kVPad + t] = static_cast<uint16_t>(w4[e] >> 16);
       }
     }
+  };
+  int blk = 0;
+  int j = next_block(0, blk);
+  if (j < cnt) fetch(blk);
+  while (j < cnt) {  // j and blk are uniform across the work-group
+    stage();
     __syncthreads();
+    int blk_next = 0;
+    const int jn = next_block(j + 1, blk_next);
+    if (jn < cnt) fetch(blk_next);
+    const int t0 = blk * kBlk;
     // S'[token][query] for 4 tiles of 16 tokens
     floatx4_t sc[4];
 #pragma unroll
@@ -213,6 +317,8 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
       }
     }
     __syncthreads();
+    j = jn;
+    blk = blk_next;
   }
   // normalise: rows kg*4 + r need the l of those rows
 #pragma unroll
@@ -237,20 +343,27 @@ hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
   dim3 grid((nb_vis + 15) / 16, B);
   const uint16_t* q = static_cast<const uint16_t*>(sel_q);
   const uint16_t* k = static_cast<const uint16_t*>(sel_k);
-  switch (d_idx) {
-    case 32:
-      hipLaunchKernelGGL(prefill_score_kernel<32>, grid, dim3(64), 0, stream, q, sel_w, k,
-                         scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block);
-      break;
-    case 64:
-      hipLaunchKernelGGL(prefill_score_kernel<64>, grid, dim3(64), 0, stream, q, sel_w, k,
-                         scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block);
-      break;
-    default:
-      hipLaunchKernelGGL(prefill_score_kernel<128>, grid, dim3(64), 0, stream, q, sel_w, k,
-                         scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block);
-      break;
+#define SPOT_PS4(DI)                                                                         \
+  hipLaunchKernelGGL((prefill_score_kernel<DI, 4>), grid, dim3(256), 0, stream, q, sel_w, k, \
+                     scores, Tq, q_pos0, nb_cache, nb_vis, kpb, block)
+#define SPOT_PSA(DI)                                                                       \
+  hipLaunchKernelGGL((prefill_score_kernel_anyh<DI>), grid, dim3(64), 0, stream, q, sel_w, \
+                     k, scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block)
+  if (H == 4) {
+    switch (d_idx) {
+      case 32: SPOT_PS4(32); break;
+      case 64: SPOT_PS4(64); break;
+      default: SPOT_PS4(128); break;
+    }
+  } else {
+    switch (d_idx) {
+      case 32: SPOT_PSA(32); break;
+      case 64: SPOT_PSA(64); break;
+      default: SPOT_PSA(128); break;
+    }
   }
+#undef SPOT_PS4
+#undef SPOT_PSA
   return hipGetLastError();
 }
 

@@ -174,7 +174,7 @@ SPOT_API int spot_prefill_select_score(const void* sel_q, int q_dtype, const flo
  * tile and every head). Rows with no visible selected token get zeros.
  *   q    [B][Hq][Tq][d]; K, V [B][Hkv][L][d]; out [B][Hq][Tq][d]; kv_dtype SPOT_BF16;
  *        16-byte aligned.
- * Supported: d == 128, block == 64, 1 <= Tq <= 128, Hq/Hkv in {1, 2, 4, 8}.
+ * Supported: d == 128, block == 64, 1 <= Tq <= 128, K_max <= 8192, Hq/Hkv in {1, 2, 4, 8}.
  */
 SPOT_API int spot_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                                int kv_dtype, const int32_t* sel_idx, const int32_t* sel_cnt,
