@@ -273,6 +273,7 @@ def main():
     ap.add_argument("--extra-b1", action="store_true", default=True)
     ap.add_argument("--no-extra-b1", dest="extra_b1", action="store_false")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false", default=True)
+    ap.add_argument("--no-int4", dest="int4", action="store_false", default=True)
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -362,6 +363,27 @@ def main():
                                                  for k, v in p1.items()},
                             "note": "batch row 0 of the same inputs"}
         del inp1, bufs1
+    if a.int4 and wl.name == "c3_128k_b8":
+        log("bench: INT4 selector cache workload")
+        wl4 = W.WORKLOADS["c4_128k_b8_int4"]
+        del inp
+        torch.cuda.empty_cache()
+        inp4 = W.make_inputs(wl4, device="cuda")
+        bufs4 = DecodeBuffers(wl4.B, wl4.nb, wl4.Hq, wl4.d, wl4.K_max, dt)
+        w4, _, p4 = time_steps(inp4, wl4, bufs4, a.steps, a.warmup, stream)
+        g4, _ = time_graph(inp4, wl4, bufs4, a.steps, a.warmup, stream)
+        tok4 = selected_tokens(bufs4.sel_idx, bufs4.sel_cnt, wl4.L, wl4.block)
+        b4 = byte_budget(wl4, wl4.B, tok4)
+        result["int4_selector"] = {
+            "workload": wl4.name, "us_per_step_graph": round(g4, 3),
+            "us_per_step_stream": round(w4 * 1e6 / a.steps, 3),
+            "selected_blocks_mean": round(tok4 / wl4.block / wl4.B, 1),
+            "algorithmic_bytes": b4["step"],
+            "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in p4.items()},
+            "score_GBps": round(b4["score"] / (statistics.fmean(p4["score"]) * 1e-6) / 1e9, 1)}
+        del inp4, bufs4
+        torch.cuda.empty_cache()
+        inp = W.make_inputs(wl, device="cuda") if not a.no_cpu_baseline else None
     if a.prefill:
         log("bench: prefill tile")
         result["prefill"] = prefill_leg(max(10, a.steps // 4), 5, stream)
