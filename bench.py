@@ -208,6 +208,49 @@ def prefill_leg(steps, warmup, stream):
             "attn_frac_of_bf16_mfma_peak": round(flops / (t["attn"] * 1e-6) / 2.5e15, 4)}
 
 
+def page_geometry_selector(steps, warmup, stream):
+    """The paper's selector geometry (Appendix A, Table 3: per-token selector keys,
+    4 heads x 128 dims, block 16) at 128K, batch 1: scoring of 8192 blocks x 16 keys
+    (128 MiB of bf16 keys) plus dual top-p over them. Table 1 reports the selector at
+    1.55 ms per decode token over Qwen3-8B's 36 layers, i.e. about 43 us per layer, on
+    one NVIDIA B200 (context, not a target)."""
+    L, block, H, di = 131072, 16, 4, 128
+    nb, kpb = L // block, block
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(47)
+    sel_q = torch.randn(1, H, di, generator=gen, device="cuda").bfloat16()
+    sel_w = torch.randn(1, H, generator=gen, device="cuda").abs()
+    sel_k = torch.randn(1, nb, kpb, H, di, generator=gen, device="cuda").bfloat16()
+    scores = torch.empty(1, nb, device="cuda")
+    K_max = nb
+    idx = torch.empty(1, K_max, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for i in range(warmup + steps):
+            e = ev[i - warmup] if i >= warmup else None
+            if e:
+                e[0].record(stream)
+            spot.spot_select_score(sel_q, sel_w, sel_k, None, scores, kpb=kpb, stream=stream)
+            if e:
+                e[1].record(stream)
+            # Table 3 inference defaults: sink 128 tokens, recency 256, K_min 512 tokens
+            spot.spot_select_topp(scores, idx, cnt, None, 0.9, 512 // block, K_max,
+                                  128 // block, 256 // block, stream=stream)
+            if e:
+                e[2].record(stream)
+    torch.cuda.synchronize()
+    t_score = statistics.fmean([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
+    t_topp = statistics.fmean([e[1].elapsed_time(e[2]) * 1e3 for e in ev])
+    key_bytes = sel_k.numel() * 2
+    return {"geometry": "L 131072, block 16, 16 per-token keys per block, 4 x 128 bf16, batch 1",
+            "selector_key_bytes": key_bytes,
+            "score_us": round(t_score, 3), "topp_us": round(t_topp, 3),
+            "score_GBps": round(key_bytes / (t_score * 1e-6) / 1e9, 1),
+            "selected_blocks": int(cnt[0]),
+            "paper_selector_us_per_layer_B200": round(1550.0 / 36, 1)}
+
+
 def calibration_copy():
     """A plain 256 MiB device copy, outside every timed region: its FETCH_SIZE and
     WRITE_SIZE counters scale the counters of the other kernels to bytes."""
@@ -274,6 +317,8 @@ def main():
     ap.add_argument("--no-extra-b1", dest="extra_b1", action="store_false")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false", default=True)
     ap.add_argument("--no-int4", dest="int4", action="store_false", default=True)
+    ap.add_argument("--no-page-geometry", dest="page_geometry", action="store_false",
+                    default=True)
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -387,6 +432,10 @@ def main():
     if a.prefill:
         log("bench: prefill tile")
         result["prefill"] = prefill_leg(max(10, a.steps // 4), 5, stream)
+    if a.page_geometry:
+        log("bench: selector at the paper's page geometry")
+        result["page_geometry_selector"] = page_geometry_selector(max(10, a.steps // 4), 5,
+                                                                  stream)
     result["calibration_copy_bytes"] = calibration_copy()
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")

@@ -39,41 +39,74 @@ __global__ __launch_bounds__(256) void select_score_kernel(
   for (int c = 0; c < CH; c += 8) load8(qp + c, qv + c);
   const float wh = sel_w[(size_t)b * H + head];
 
-  float best = -INFINITY;
-  for (int j = 0; j < kpb; ++j) {
-    const size_t row = ((size_t)b * nb + blk_c) * kpb + j;
+  // score of selector key j of this lane group's block (all lanes of the group return it)
+  auto key_score = [&](int j, const u32x4_t& raw, const u32x4_t& raw2, uint16_t sh) {
     float dot = 0.f;
     if constexpr (KK == kKeyInt4) {
-      const uint8_t* cp = static_cast<const uint8_t*>(sel_k) + (row * H + head) * (DIDX / 2) +
-                          part * 16;
-      const u32x4_t c4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp));
-      const uint32_t wd[4] = {c4[0], c4[1], c4[2], c4[3]};
       float a = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           // nibble n of word k is element 8k+n; shift it to the top, sign-extend down
-          const int code = static_cast<int>(wd[k] << (28 - 4 * n)) >> 28;
+          const int code = static_cast<int>(raw[k] << (28 - 4 * n)) >> 28;
           a = fmaf(qv[k * 8 + n], static_cast<float>(code), a);
         }
       }
-      const uint16_t sh = sel_scale[(row * H + head) * (DIDX / 32) + part];
       dot = a * half_bits_to_f(sh);
-    } else {
-      typedef typename std::conditional<KK == kKeyF32, float, uint16_t>::type KT;
-      const KT* kp = static_cast<const KT*>(sel_k) + (row * H + head) * DIDX + part * CH;
-      float kv[8];
-      load8_stream(kp, kv);
+    } else if constexpr (KK == kKeyF32) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) dot = fmaf(qv[n], kv[n], dot);
+      for (int n = 0; n < 4; ++n) {
+        dot = fmaf(qv[n], __uint_as_float(raw[n]), dot);
+        dot = fmaf(qv[4 + n], __uint_as_float(raw2[n]), dot);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        dot = fmaf(qv[2 * n], bf16_lo(raw[n]), dot);
+        dot = fmaf(qv[2 * n + 1], bf16_hi(raw[n]), dot);
+      }
     }
 #pragma unroll
     for (int o = 1; o < LPH; o <<= 1) dot += shfl_xor_f(dot, o);
     float c = wh * fmaxf(dot, 0.f);
     // every lane of a head now holds that head's term; add one copy per head
     for (int o = LPH; o < LPR; o <<= 1) c += shfl_xor_f(c, o);
-    best = fmaxf(best, c);
+    return c;
+  };
+  // this lane's 16-byte chunk (two for fp32 keys) of key j
+  auto load_key = [&](int j, u32x4_t& raw, u32x4_t& raw2, uint16_t& sh) {
+    const size_t row = ((size_t)b * nb + blk_c) * kpb + j;
+    if constexpr (KK == kKeyInt4) {
+      const uint8_t* cp = static_cast<const uint8_t*>(sel_k) + (row * H + head) * (DIDX / 2) +
+                          part * 16;
+      raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp));
+      sh = sel_scale[(row * H + head) * (DIDX / 32) + part];
+    } else {
+      typedef typename std::conditional<KK == kKeyF32, float, uint16_t>::type KT;
+      const KT* kp = static_cast<const KT*>(sel_k) + (row * H + head) * DIDX + part * CH;
+      raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp));
+      if constexpr (KK == kKeyF32)
+        raw2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + 4));
+    }
+  };
+
+  // keys of a block are read four at a time so their loads overlap (per-token keys)
+  float best = -INFINITY;
+  int j = 0;
+  for (; j + 4 <= kpb; j += 4) {
+    u32x4_t r[4], r2[4];
+    uint16_t sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_key(j + u, r[u], r2[u], sc[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) best = fmaxf(best, key_score(j + u, r[u], r2[u], sc[u]));
+  }
+  for (; j < kpb; ++j) {
+    u32x4_t r, r2;
+    uint16_t sc;
+    load_key(j, r, r2, sc);
+    best = fmaxf(best, key_score(j, r, r2, sc));
   }
   if (valid && gl == 0) scores[(size_t)b * nb + blk] = best;
 }

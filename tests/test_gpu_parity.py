@@ -417,3 +417,28 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(bufs.sel_idx, ref[0]) and torch.equal(bufs.sel_cnt, ref[1])
         assert torch.equal(bufs.out, ref[2]), f"replay {i}"
+
+
+def test_page_geometry_scoring_sampled():
+    """The paper's selector geometry (per-token keys, 16 per block, 4 heads x 128) at a
+    128K context, batch 1: sampled blocks against the oracle, then the top-p rule on the
+    GPU's own scores."""
+    nb, kpb, H, di = 8192, 16, 4, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    sel_q = torch.randn(1, H, di, generator=g, device=DEV).bfloat16()
+    sel_w = torch.randn(1, H, generator=g, device=DEV).abs()
+    sel_k = torch.randn(1, nb, kpb, H, di, generator=g, device=DEV).bfloat16()
+    scores = torch.empty(1, nb, device=DEV)
+    _lib.spot_select_score(sel_q, sel_w, sel_k, None, scores, kpb=kpb)
+    idx = torch.empty(1, nb, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+    _lib.spot_select_topp(scores, idx, cnt, None, 0.9, 32, nb, 8, 16)
+    torch.cuda.synchronize()
+    pick = torch.tensor([0, 1, 2, 777, 4096, 8190, 8191] + list(range(3000, 3064)))
+    keys = np64(sel_k[:, pick])
+    ref = O.select_score(np64(sel_q), np64(sel_w), keys)
+    assert_scores_close(np64(scores)[:, pick.numpy()], ref,
+                        score_magnitude(np64(sel_q), np64(sel_w), keys))
+    s = gpu_sets(idx, cnt)[0]
+    assert_topp_unit(s, np64(scores)[0], float(np.float32(0.9)), 32, nb, 8, 16, tag="page")
