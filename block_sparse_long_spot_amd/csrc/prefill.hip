@@ -8,11 +8,12 @@
 //
 // Attention: one work-group per (16-query row tile, KV head); wave w computes query
 // head g*G + w, so the G heads of a KV group share every K/V block the work-group
-// stages in LDS (K row-major, V transposed). Per selected block:
+// stages in LDS (K and V row-major, 16-byte writes). Per selected block:
 //   S' = K . Q^T   (tokens x queries; A = K from LDS, B = Q from registers)
 // whose accumulator layout gives each lane 8 scores of one query row. Those become,
 // after the online softmax and a bf16 conversion, the A operand of
-//   O += P . V     (B = V^T read from LDS in the same token order),
+//   O += P . V     (B = V read with gfx950's transposing LDS load, ds_read_b64_tr_b16,
+//                   in the same token order),
 // so P never leaves registers. Causal and L masks are applied per element.
 #include "device_common.h"
 #include "spot_internal.h"
@@ -22,6 +23,15 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBlk = 64;
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+// An LDS address of this kernel's shared arrays as the LDS-space pointer the
+// transposing read takes.
+__device__ __forceinline__ lds_s16x4_t* lds_s16x4(const uint16_t* p) {
+  return (lds_s16x4_t*)((__attribute__((address_space(3))) uint16_t*)p);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f_to_bf16_rne(lo)) | (static_cast<uint32_t>(f_to_bf16_rne(hi)) << 16);
@@ -154,7 +164,6 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
 
 // ---------------------------------------------------------------- attention
 constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
-constexpr int kVPad = 68;   // V^T row stride in bf16 (128 B + 8 B)
 constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS)
 
 template <int G>
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
   constexpr int D = 128;
   constexpr int NT = G * 64;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kVPad];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBlk * kKPad];
   __shared__ int32_t sel_s[kMaxPrefillList];
 
   const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -222,18 +231,13 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
       vbuf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + d0));
     }
   };
-  auto stage = [&]() {  // K row-major, V transposed
+  auto stage = [&]() {  // K and V row-major
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
       *reinterpret_cast<u32x4_t*>(&Ks[t * kKPad + d0]) = kbuf[i];
-      const uint32_t w4[4] = {vbuf[i][0], vbuf[i][1], vbuf[i][2], vbuf[i][3]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(d0 + 2 * e) * kVPad + t] = static_cast<uint16_t>(w4[e] & 0xffffu);
-        Vt[(d0 + 2 * e + 1) * kVPad + t] = static_cast<uint16_t>(w4[e] >> 16);
-      }
+      *reinterpret_cast<u32x4_t*>(&Vs[t * kKPad + d0]) = vbuf[i];
     }
   };
   int blk = 0;
@@ -304,14 +308,18 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
       const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* vp = &Vt[(dt * 16 + row) * kVPad + 32 * s + 4 * kg];
+        // transposing LDS reads: source lane `row` of each 16-lane group points at V row
+        // 32s + 4kg + row/4, dims dt*16 + 4*(row%4); lane `row` then receives
+        // V[32s + 4kg + k][dt*16 + row] for k = 0..3 (and the same 16 tokens later)
+        const uint16_t* vp = &Vs[(32 * s + 4 * kg + row / 4) * kKPad + dt * 16 + 4 * (row % 4)];
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(vp));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(vp + 16 * kKPad));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
         u32x4 vb;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        vb[0] = lo.x;
-        vb[1] = lo.y;
-        vb[2] = hi.x;
-        vb[3] = hi.y;
+        vb[0] = l2[0];
+        vb[1] = l2[1];
+        vb[2] = h2[0];
+        vb[3] = h2[1];
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb),
                                                         o[dt], 0, 0, 0);
       }
