@@ -269,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float bm = fmaxf(fmaxf(z[0][r], z[1][r]), fmaxf(z[2][r], z[3][r]));
-      bm = group_max<16>(bm);
+      bm = row16_max(bm);
       const float mn = fmaxf(mrow[r], bm);
       alpha[r] = exp2f(mrow[r] - mn);
       float rs = 0.f;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
         z[T][r] = exp2f(z[T][r] - mn);
         rs += z[T][r];
       }
-      rs = group_sum<16>(rs);
+      rs = row16_sum(rs);
       lrow[r] = lrow[r] * alpha[r] + rs;
       mrow[r] = mn;
     }

@@ -130,6 +130,28 @@ __device__ __forceinline__ T lane_value(T x, int lane) {
   }
 }
 
+// Sum / maximum over each row of 16 lanes (lanes 16r .. 16r+15), result in every lane
+// of the row, by rotations inside the row on the DPP network (row_ror:8,4,2,1).
+template <int CTRL>
+__device__ __forceinline__ float dpp_rot(float x) {
+  const int xi = __float_as_int(x);
+  return __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_rot<0x128>(x);
+  x += dpp_rot<0x124>(x);
+  x += dpp_rot<0x122>(x);
+  x += dpp_rot<0x121>(x);
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_rot<0x128>(x));
+  x = fmaxf(x, dpp_rot<0x124>(x));
+  x = fmaxf(x, dpp_rot<0x122>(x));
+  x = fmaxf(x, dpp_rot<0x121>(x));
+  return x;
+}
+
 // Order-preserving map of a binary32 onto uint32 (larger float -> larger key).
 // -0.0 must be folded onto +0.0 by the caller.
 __device__ __forceinline__ uint32_t float_key(float f) {
