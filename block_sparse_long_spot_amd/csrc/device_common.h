@@ -152,6 +152,36 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// Sum over aligned groups of W lanes (W a power of two <= 64), result in every lane of
+// the group, for values already summed over aligned groups of FROM lanes (every lane of
+// such a group holds the same value; FROM = 1 for arbitrary values). Inside a row of 16
+// the steps run on the DPP network (quad_perm swaps, then row half-mirror and mirror,
+// which pair each lane with one in the other half of its group of 8 or 16); across rows
+// they are shuffles.
+template <int W, int FROM = 1>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  if constexpr (FROM <= 1 && W >= 2) x += dpp_rot<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (FROM <= 2 && W >= 4) x += dpp_rot<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (FROM <= 4 && W >= 8) x += dpp_rot<0x141>(x);   // row_half_mirror
+  if constexpr (FROM <= 8 && W >= 16) x += dpp_rot<0x140>(x);  // row_mirror
+  if constexpr (FROM <= 16 && W >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (FROM <= 32 && W >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+// The same with the group size 2^log2w chosen at run time (uniform across the wave).
+template <int FROM>
+__device__ __forceinline__ float group_sum_dpp_rt(float x, int log2w) {
+  switch (log2w) {
+    case 0: return x;
+    case 1: return group_sum_dpp<2, FROM>(x);
+    case 2: return group_sum_dpp<4, FROM>(x);
+    case 3: return group_sum_dpp<8, FROM>(x);
+    case 4: return group_sum_dpp<16, FROM>(x);
+    case 5: return group_sum_dpp<32, FROM>(x);
+    default: return group_sum_dpp<64, FROM>(x);
+  }
+}
+
 // Order-preserving map of a binary32 onto uint32 (larger float -> larger key).
 // -0.0 must be folded onto +0.0 by the caller.
 __device__ __forceinline__ uint32_t float_key(float f) {

@@ -6,8 +6,8 @@
 // split into 16-byte chunks, one per lane, so a wave reads whole rows with
 // contiguous 16-byte loads: 8 elements per lane for fp32/bf16 keys (fp32 takes two
 // loads), 32 INT4 codes per lane for the quantised cache (exactly one fp16 scale
-// group). Lanes of one head reduce their partial dots with cross-lane adds, apply
-// ReLU and the head weight, then lanes of one row add the heads.
+// group). Lanes of one head reduce their partial dots with cross-lane adds (DPP inside
+// a row of 16 lanes), apply ReLU and the head weight, then lanes of one row add the heads.
 #include "device_common.h"
 #include "spot_internal.h"
 
@@ -67,12 +67,9 @@ __global__ __launch_bounds__(256) void select_score_kernel(
         dot = fmaf(qv[2 * n + 1], bf16_hi(raw[n]), dot);
       }
     }
-#pragma unroll
-    for (int o = 1; o < LPH; o <<= 1) dot += shfl_xor_f(dot, o);
-    float c = wh * fmaxf(dot, 0.f);
-    // every lane of a head now holds that head's term; add one copy per head
-    for (int o = LPH; o < LPR; o <<= 1) c += shfl_xor_f(c, o);
-    return c;
+    dot = group_sum_dpp<LPH>(dot);
+    // every lane of a head now holds that head's term; add the heads of the row
+    return group_sum_dpp_rt<LPH>(wh * fmaxf(dot, 0.f), lpr_log2);
   };
   // this lane's 16-byte chunk (two for fp32 keys) of key j
   auto load_key = [&](int j, u32x4_t& raw, u32x4_t& raw2, uint16_t& sh) {
