@@ -103,8 +103,9 @@ SPOT_API int spot_select_score(const void* sel_q, int q_dtype, const float* sel_
  *            skip). 0 when k = 0 or B_res is empty.
  * Errors: SPOT_ERR_INVALID when p is not finite, n_sink/n_rec/K_min < 0, or
  * K_max < r (the reserved set would not fit). Supported: 1 <= nb <= 16384.
- * Masses are accumulated exactly in 2^-38 fixed point from double-precision
- * exponentials, so the result does not depend on thread scheduling.
+ * Each block's mass exp(s - max) is rounded to 2^-29 fixed point (relative error near
+ * 1e-7) and masses are summed as integers, exactly, so the result does not depend on
+ * thread scheduling.
  */
 SPOT_API int spot_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
                               float* sel_mass, int B, int nb, float p, int K_min, int K_max,
