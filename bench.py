@@ -233,6 +233,24 @@ def prefill_leg(steps, warmup, stream):
             "attn_frac_of_bf16_mfma_peak": round(flops / (t["attn"] * 1e-6) / 2.5e15, 4)}
 
 
+def static_topk_leg(inp, wl, steps, warmup, stream):
+    """Static top-K (Eq. 6) with K = half the blocks, no reserved blocks: the paper's
+    K = 0.5L decode rows (Table 1), on the same 128K batch-8 inputs. Four times the
+    attention bytes of the top-p headline."""
+    K = wl.nb // 2
+    ws = wl.with_(p=0.0, K_min=K, K_max=K, n_sink=0, n_rec=0)
+    bufs = DecodeBuffers(ws.B, ws.nb, ws.Hq, ws.d, ws.K_max, inp["q"].dtype)
+    us, _ = time_back_to_back(lambda: decode_step(inp, ws, bufs, stream=stream), steps,
+                              warmup, stream)
+    _, _, per = time_steps(inp, ws, bufs, max(10, steps // 10), warmup, stream)
+    tok = selected_tokens(bufs.sel_idx, bufs.sel_cnt, ws.L, ws.block)
+    bb = byte_budget(ws, ws.B, tok)
+    return {"K_blocks": K, "us_per_step": round(us, 3), "algorithmic_bytes": bb["step"],
+            "GBps": round(bb["step"] / (us * 1e-6) / 1e9, 1),
+            "frac": round(bb["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in per.items()}}
+
+
 def page_geometry_selector(steps, warmup, stream):
     """The paper's selector geometry (Appendix A, Table 3: per-token selector keys,
     4 heads x 128 dims, block 16) at 128K, batch 1: scoring of 8192 blocks x 16 keys
@@ -342,6 +360,7 @@ def main():
     ap.add_argument("--no-extra-b1", dest="extra_b1", action="store_false")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false", default=True)
     ap.add_argument("--no-int4", dest="int4", action="store_false", default=True)
+    ap.add_argument("--no-static", dest="static", action="store_false", default=True)
     ap.add_argument("--no-page-geometry", dest="page_geometry", action="store_false",
                     default=True)
     a = ap.parse_args()
@@ -453,6 +472,9 @@ def main():
                                                  for k, v in p1.items()},
                             "note": "batch row 0 of the same inputs"}
         del inp1, bufs1
+    if a.static and wl.name == "c3_128k_b8":
+        log("bench: static top-K at half the context")
+        result["static_topk_half"] = static_topk_leg(inp, wl, a.steps, a.warmup, stream)
     if a.int4 and wl.name == "c3_128k_b8":
         log("bench: INT4 selector cache workload")
         wl4 = W.WORKLOADS["c4_128k_b8_int4"]

@@ -96,6 +96,8 @@ SPOT_API int spot_select_score(const void* sel_q, int q_dtype, const float* sel_
  *   k     = min(max(k_p, K_min - r, 0), K_max - r, |B_res|)   (|S| in [K_min, K_max]);
  *   S     = R u (first k of the order), written in ascending block order.
  * If B_res is empty, S is every block.
+ * Static top-K (Eq. 6: the K highest-scoring blocks, no reserved blocks) is the case
+ * p <= 0, n_sink = n_rec = 0, K_min = K_max = K.
  *   scores   fp32 [B][nb]; 4-byte aligned.
  *   sel_idx  out int32 [B][K_max]: S ascending, then -1 up to K_max; 4-byte aligned.
  *   sel_cnt  out int32 [B]: |S|.

@@ -140,6 +140,11 @@ TOPP_CASES = [
     (10, "normal", 0.9, 0, 10, 6, 6),           # empty residual
     (20, "normal", -0.5, 3, 20, 1, 1),          # p <= 0: floor only
     (20, "normal", 1.7, 0, 8, 1, 1),            # p >= 1: cap binds
+    # static top-K (Eq. 6): p <= 0, no reserved blocks, K_min = K_max = K
+    (2048, "zipf", 0.0, 1024, 1024, 0, 0),
+    (2048, "ties", 0.0, 1024, 1024, 0, 0),
+    (8192, "normal", 0.0, 4096, 4096, 0, 0),
+    (300, "tiebin65", 0.0, 25, 25, 0, 0),       # K-th block inside a dense tied bin
 ]
 
 
@@ -165,6 +170,27 @@ def test_select_topp_parity(case):
         sel, info = O.select_topp_row(row, pf, K_min, K_max, n_sink, n_rec)
         if sets[b] == sel and info["n_res"] > 0:
             assert abs(masses[b] - info["mass"]) <= 1e-6, (masses[b], info["mass"])
+
+
+@pytest.mark.parametrize("nb,K,kind", [(2048, 1024, "zipf"), (2048, 1024, "ties"),
+                                       (777, 100, "flat"), (16384, 8192, "normal")])
+def test_static_topk_matches_sort(nb, K, kind):
+    """Eq. 6 directly: the K largest scores, ties to the lower block index, by a full
+    sort of the GPU's input scores (no top-p machinery on the reference side)."""
+    B = 3
+    g = cpu_gen(nb + K)
+    x = _topp_rows(kind, B, nb, g).float().contiguous()
+    scores = x.to(DEV)
+    idx = torch.empty(B, K, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(B, dtype=torch.int32, device=DEV)
+    _lib.spot_select_topp(scores, idx, cnt, None, 0.0, K, K, 0, 0)
+    torch.cuda.synchronize()
+    xs = x.numpy().astype(np.float32)
+    for b in range(B):
+        order = np.lexsort((np.arange(nb), -xs[b].astype(np.float64)))
+        want = sorted(order[:K].tolist())
+        assert int(cnt[b]) == K
+        assert idx[b].cpu().tolist() == want, f"row {b}"
 
 
 def test_select_topp_deterministic():
@@ -370,6 +396,17 @@ def test_workload_full_size(name, big_inputs):
             assert wl.K_min <= len(s) <= wl.K_max
         else:
             assert len(s) == wl.K_max     # the Zipf(1.1) nucleus is far above the cap
+
+
+def test_workload_static_topk_half(big_inputs):
+    """Static top-K at half the context (Eq. 6; the paper's K = 0.5L decode rows) on the
+    128K batch-8 inputs: 1024 of 2048 blocks per query, sampled outputs."""
+    base = W.WORKLOADS["c3_128k_b8"]
+    inp = big_inputs(base.name)
+    wl = base.with_(p=0.0, K_min=base.nb // 2, K_max=base.nb // 2, n_sink=0, n_rec=0)
+    rows = [(b, (7 * b + 1) % wl.Hq) for b in range(wl.B)]
+    bufs, sets = run_e2e(wl, inp, check_rows=rows, tag="c3-static-half")
+    assert all(len(s) == wl.nb // 2 for s in sets)
 
 
 def test_workload_budgets_vary(big_inputs):
