@@ -1,16 +1,23 @@
 // Decode attention over the selected KV blocks (SpotAttention §2.3: the layer attends
 // only to keys in blocks of S_q, one S_q per query shared by every head).
 //
-// Split-K: the selected-block list of one (query, KV head) "unit" is cut into runs of
-// `bps` blocks; a work-group reduces one run with an online softmax for the G query
-// heads that share the KV head (GQA) and stores (m, l, acc) per head; runs past the
-// end of the list store an empty marker. attn_combine then merges the runs of every
+// Split-K: the selected-block list of one (query, KV head) "unit" is cut into runs; a
+// work-group reduces one run with an online softmax for the G query heads that share
+// the KV head (GQA) and stores (m, l, acc) per head; runs past the end of the list
+// store an empty marker. The MFMA path cuts runs from each row's actual count, so a
+// list far shorter than K_max still spreads over every work-group. attn_combine then merges the runs of every
 // (query, head) in run order (deterministic). Merging across work-groups inside one
 // kernel would need an agent-scope release/acquire per work-group, which on this
 // multi-XCD part is an L2 writeback plus invalidate; a second small kernel is cheaper.
 //
+// Block sizes 16, 32, 64 and 128 tokens. The unit of work of a wave is a 64-token
+// chunk made of four 16-token tiles, each with its own start token: the four tiles of
+// one 64-token block, two 32-token blocks, four 16-token blocks (the paper's page
+// size) or half a 128-token block. Run lengths are chosen in tokens, so every block
+// size moves the same bytes per work-group.
+//
 // HBM-bound (about 4 flop per byte in bf16 with G = 4). Two run kernels:
-//  * attn_mfma (bf16, d in {64,128}): each wave owns whole 64-token blocks.
+//  * attn_mfma (bf16, d in {64,128}): each wave owns whole 64-token chunks.
 //    q.K^T runs on the MFMA units (v_mfma_f32_16x16x32_bf16, the G heads padded to
 //    16 rows): every lane loads 16 contiguous bytes of a K row straight into the
 //    B-operand layout, no LDS staging and no bf16->fp32 conversion. K and V are read
@@ -20,7 +27,7 @@
 //    VALU: each lane owns 8 head dims of a set of tokens, reading V rows with
 //    coalesced 16-byte loads, and probabilities come through a per-wave LDS tile.
 //  * attn_generic (fp32 or bf16, any supported shape): one wave per run;
-//    lane = token for q.K^T, lane = head dim for P.V.
+//    lane = token for q.K^T (64 tokens of a block at a time), lane = head dim for P.V.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
 #include "device_common.h"
 #include "spot_internal.h"
@@ -29,7 +36,7 @@ namespace spot {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBlk = 64;  // tokens per KV block
+constexpr int kChunk = 64;  // tokens a wave consumes at a time (four 16-token tiles)
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f(x); }
@@ -69,7 +76,7 @@ __global__ __launch_bounds__(64) void attn_generic(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, int K_max,
     float* __restrict__ ws_acc, float2* __restrict__ ws_ml, int Hq, int Hkv, int L,
-    float qscale, int bps, int nsplit) {
+    float qscale, int block, int bps, int nsplit) {
   constexpr int DPL = D / 64;  // head dims per lane in P.V
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int cnt = min(max(sel_cnt[b], 0), K_max);
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(64) void attn_generic(
   const int j1 = min(j0 + bps, cnt);
   const int lane = threadIdx.x;
   __shared__ float qs[G][D];
-  __shared__ float ps[kBlk][G];
+  __shared__ float ps[kChunk][G];
   for (int i = lane; i < G * D; i += 64) {
     const int h = i / D, dd = i % D;
     qs[h][dd] = to_f(q[((size_t)b * Hq + g * G + h) * D + dd]) * qscale;
@@ -95,14 +102,18 @@ __global__ __launch_bounds__(64) void attn_generic(
 #pragma unroll
     for (int c = 0; c < DPL; ++c) acc[h][c] = 0.f;
   }
-  const int nbl = (L + kBlk - 1) / kBlk;
+  const int nbl = (L + block - 1) / block;
   const T* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
   const T* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
   for (int j = j0; j < j1; ++j) {
     const int blk = sel_idx[(size_t)b * K_max + j];
     if (blk < 0 || blk >= nbl) continue;
-    const int tok = blk * kBlk + lane;
-    const bool tv = tok < L;
+    // 64 tokens of the block at a time; at least one of them is < L
+    for (int c0 = 0; c0 < block && blk * block + c0 < L; c0 += kChunk) {
+    const int t0 = blk * block + c0;
+    const int ntok = min(min(kChunk, block - c0), L - t0);
+    const int tok = t0 + lane;
+    const bool tv = lane < ntok;
     const T* kr = Kg + (size_t)(tv ? tok : L - 1) * D;
     float z[G];
 #pragma unroll
@@ -129,9 +140,8 @@ __global__ __launch_bounds__(64) void attn_generic(
       m[h] = mn;
     }
     __syncthreads();
-    const int tend = min(kBlk, L - blk * kBlk);
-    for (int t = 0; t < tend; ++t) {
-      const T* vr = Vg + (size_t)(blk * kBlk + t) * D + lane * DPL;
+    for (int t = 0; t < ntok; ++t) {
+      const T* vr = Vg + (size_t)(t0 + t) * D + lane * DPL;
 #pragma unroll
       for (int c = 0; c < DPL; ++c) {
         const float v = to_f(vr[c]);
@@ -140,6 +150,7 @@ __global__ __launch_bounds__(64) void attn_generic(
       }
     }
     __syncthreads();
+    }
   }
   __shared__ float racc[G][D];
   __shared__ float rm[G], rl[G];
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(64) void attn_generic(
 }
 
 // ---------------------------------------------------------------- MFMA pass 1 (bf16)
-template <int D, int G, int NW>
+template <int D, int G, int NW, int BS>
 __global__ __launch_bounds__(NW * 64) void attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
@@ -166,23 +177,33 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   constexpr int KS = D / 32;   // MFMA k-steps over the head dim
   constexpr int DC = D / 8;    // lanes covering one V row (8 dims each)
   constexpr int TG = 64 / DC;  // token groups in P.V
-  constexpr int TPL = DC;      // tokens per lane per block in P.V (= 64 / TG)
+  constexpr int TPL = DC;      // tokens per lane per chunk in P.V (= 64 / TG)
   constexpr int NG = (G + 3) / 4;  // 16-lane groups that hold real heads in S
+  constexpr int TPB = BS / 16;                    // 16-token tiles per block
+  constexpr int EPC = BS >= kChunk ? 1 : kChunk / BS;  // list entries per chunk
+  constexpr int CPE = BS >= kChunk ? BS / kChunk : 1;  // chunks per list entry
   static_assert(G <= 8, "at most 8 query heads per KV head");
+  static_assert(BS == 16 || BS == 32 || BS == 64 || BS == 128, "block of 16 to 128 tokens");
+  static_assert(16 % TG == 0, "a lane's P.V tokens of one step lie in one tile");
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int cnt = min(max(sel_cnt[b], 0), K_max);
-  const int j0 = split * bps;
+  // Runs are cut from this row's actual count, spread over all nsplit work-groups
+  // (whole chunks for small blocks); `bps` is the split plan's maximum, sized for
+  // K_max, and cnt <= K_max keeps every run within it.
+  int run = (cnt + nsplit - 1) / nsplit;
+  run = min((run + EPC - 1) / EPC * EPC, bps);
+  const int j0 = split * run;
   if (j0 >= cnt) {
     store_empty_run<G, NW * 64>(b, g, split, Hq, nsplit, ws_ml);
     return;
   }
-  const int j1 = min(j0 + bps, cnt);
+  const int j1 = min(j0 + run, cnt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;  // MFMA operand coordinates
   const int dc = lane % DC, tg = lane / DC;   // P.V coordinates
 
-  __shared__ __attribute__((aligned(16))) float Ps[NW][kBlk][G < 4 ? 4 : G];
+  __shared__ __attribute__((aligned(16))) float Ps[NW][kChunk][G < 4 ? 4 : G];
   __shared__ float mm[NW][G], ll[NW][G];
   __shared__ float accs[NW][G][D];
 
@@ -211,43 +232,72 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
 
-  const int nbl = (L + kBlk - 1) / kBlk;
+  const int nbl = (L + BS - 1) / BS;
   const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
   const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
-  // This wave's list entries j0 + wave + i*NW, one per lane, read in one instruction
-  // (bps / NW <= 64); block i is then a register read, not a load on the critical path.
-  const int n_mine = (j1 - j0 - wave + NW - 1) / NW;
+  // This wave's chunks are wave + i*NW. The list entries they use are read once, one
+  // per lane (at most 64 per wave; the split plan keeps runs within that), so a
+  // chunk's tile starts are register reads, not loads on the critical path.
+  //   BS >= 64: lane i holds the entry of chunk i;
+  //   BS <  64: lane i*EPC + u holds entry u of chunk i.
+  const int n_ent = j1 - j0;
+  const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
+  const int n_mine = (n_chunks - wave + NW - 1) / NW;
   int my_blk = -1;
-  if (lane < n_mine) {
-    const int e = sel_idx[(size_t)b * K_max + j0 + wave + lane * NW];
-    my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
+  {
+    const int i = lane / EPC, u = lane % EPC;
+    const int e_rel = BS >= kChunk ? (wave + i * NW) / CPE : (wave + i * NW) * EPC + u;
+    if (i < n_mine && e_rel < n_ent) {
+      const int e = sel_idx[(size_t)b * K_max + j0 + e_rel];
+      my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
+    }
   }
-  auto block_of = [&](int i) { return __builtin_amdgcn_readlane(my_blk, i); };
-  // K rows of a block in the B-operand layout: lane (token row, k-group kg)
-  auto load_k = [&](int blk, bf16x8_t (&kb)[4][KS]) {
-    const int t0 = max(blk, 0) * kBlk;
+  // first token of each 16-token tile of chunk i, or -1 for a tile with no block
+  auto tile_starts = [&](int i, int (&st)[4]) {
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const int tok = min(t0 + T * 16 + row, L - 1);
+      if constexpr (BS >= kChunk) {
+        const int blk = __builtin_amdgcn_readlane(my_blk, i);
+        const int off = ((wave + i * NW) % CPE) * kChunk + T * 16;
+        st[T] = blk < 0 ? -1 : blk * BS + off;
+      } else {
+        const int blk = __builtin_amdgcn_readlane(my_blk, i * EPC + T / TPB);
+        st[T] = blk < 0 ? -1 : blk * BS + (T % TPB) * 16;
+      }
+    }
+  };
+  // a chunk with no token below L is skipped (its scores would all be -inf)
+  auto any_token = [&](const int (&st)[4]) {
+    bool a = false;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) a = a || (st[T] >= 0 && st[T] < L);
+    return a;
+  };
+  // K rows of a chunk in the B-operand layout: lane (token row, k-group kg)
+  auto load_k = [&](const int (&st)[4], bf16x8_t (&kb)[4][KS]) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int tok = st[T] < 0 ? 0 : min(st[T] + row, L - 1);
       const uint16_t* kp = Kg + (size_t)tok * D + kg * 8;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         kb[T][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kp + s * 32));
     }
   };
-  // V rows of a block: lane (dim chunk dc, token group tg), whole rows per instruction
-  auto load_v = [&](int blk, u32x4_t (&vv)[TPL]) {
-    const int t0 = max(blk, 0) * kBlk;
+  // V rows of a chunk: lane (dim chunk dc, token group tg), whole rows per instruction;
+  // chunk token i*TG + tg lies in tile (i*TG)/16
+  auto load_v = [&](const int (&st)[4], u32x4_t (&vv)[TPL]) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      const int tok = min(t0 + i * TG + tg, L - 1);
+      const int T = (i * TG) / 16;
+      const int tok = st[T] < 0 ? 0 : min(st[T] + (i * TG) % 16 + tg, L - 1);
       vv[i] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + dc * 8));
     }
   };
-  // online-softmax update of this wave's state with one block
-  auto consume = [&](int blk, const bf16x8_t (&kb)[4][KS], const u32x4_t (&vv)[TPL]) {
-    const int t0 = blk * kBlk;
+  // online-softmax update of this wave's state with one chunk
+  auto consume = [&](const int (&st)[4], const bf16x8_t (&kb)[4][KS],
+                     const u32x4_t (&vv)[TPL]) {
     // S[head][token] for the 4 tiles of 16 tokens
     floatx4_t sa[4];
 #pragma unroll
@@ -261,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     float z[4][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const bool tv = t0 + T * 16 + row < L;
+      const bool tv = st[T] >= 0 && st[T] + row < L;
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[T][r] = tv ? sa[T][r] * qscale : -INFINITY;
     }
@@ -338,23 +388,30 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Software pipeline over this wave's blocks: the next block's K loads are in flight
-  // while the current block is consumed.
-  int blk = n_mine > 0 ? block_of(0) : -1;
+  // Software pipeline over this wave's chunks: the next chunk's K loads are in flight
+  // while the current chunk is consumed.
+  int st[4] = {-1, -1, -1, -1};
   bf16x8_t kb[4][KS];
-  if (n_mine > 0) load_k(blk, kb);
+  if (n_mine > 0) {
+    tile_starts(0, st);
+    load_k(st, kb);
+  }
   for (int i = 0; i < n_mine; ++i) {
     u32x4_t vv[TPL];
-    load_v(blk, vv);
-    const int blkn = i + 1 < n_mine ? block_of(i + 1) : -1;
+    load_v(st, vv);
+    int stn[4] = {-1, -1, -1, -1};
     bf16x8_t kn[4][KS];
-    if (i + 1 < n_mine) load_k(blkn, kn);
-    if (blk >= 0) consume(blk, kb, vv);
+    if (i + 1 < n_mine) {
+      tile_starts(i + 1, stn);
+      load_k(stn, kn);
+    }
+    if (any_token(st)) consume(st, kb, vv);
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+    for (int T = 0; T < 4; ++T) {
+      st[T] = stn[T];
 #pragma unroll
       for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
-    blk = blkn;
+    }
   }
 
   // sum the token groups: lanes dc, dc + DC, ... hold the same head dims
@@ -467,37 +524,67 @@ Ws carve(void* workspace, int B, int Hq, int d, int nsplit) {
 template <typename T, int D, int G>
 hipError_t launch_generic(const void* q, const void* k, const void* v, const int32_t* sel_idx,
                           const int32_t* sel_cnt, int K_max, Ws ws, void* out, int B, int Hq,
-                          int Hkv, int L, float qscale, AttnSplit sp, hipStream_t stream) {
+                          int Hkv, int L, int block, float qscale, AttnSplit sp,
+                          hipStream_t stream) {
   dim3 grid(sp.nsplit, Hkv, B);
   hipLaunchKernelGGL((attn_generic<T, D, G>), grid, dim3(64), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k),
                      static_cast<const T*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml, Hq, Hkv,
-                     L, qscale, sp.blocks_per_split, sp.nsplit);
+                     L, qscale, block, sp.blocks_per_split, sp.nsplit);
   return hipGetLastError();
 }
 
 constexpr int kMfmaWaves = 4;
 
-template <int D, int G>
-hipError_t launch_mfma(const void* q, const void* k, const void* v, const int32_t* sel_idx,
-                       const int32_t* sel_cnt, int K_max, Ws ws, void* out, int B, int Hq,
-                       int Hkv, int L, float qscale, AttnSplit sp, hipStream_t stream) {
+template <int D, int G, int BS>
+hipError_t launch_mfma_bs(const void* q, const void* k, const void* v, const int32_t* sel_idx,
+                          const int32_t* sel_cnt, int K_max, Ws ws, int B, int Hq, int Hkv,
+                          int L, float qscale, AttnSplit sp, hipStream_t stream) {
+  // the kernel keeps a wave's list entries one per lane: at most 64 of them
+  const int entries_per_chunk = BS >= kChunk ? 1 : kChunk / BS;
+  const long chunks = BS >= kChunk ? (long)sp.blocks_per_split * (BS / kChunk)
+                                   : (sp.blocks_per_split + entries_per_chunk - 1) /
+                                         entries_per_chunk;
+  if ((chunks + kMfmaWaves - 1) / kMfmaWaves * entries_per_chunk > 64)
+    return hipErrorInvalidValue;
   dim3 grid(sp.nsplit, Hkv, B);
-  hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves>), grid, dim3(kMfmaWaves * 64), 0, stream,
+  hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves, BS>), grid, dim3(kMfmaWaves * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml, Hq,
                      Hkv, L, qscale, sp.blocks_per_split, sp.nsplit);
   return hipGetLastError();
 }
 
+template <int D, int G>
+hipError_t launch_mfma(const void* q, const void* k, const void* v, const int32_t* sel_idx,
+                       const int32_t* sel_cnt, int K_max, Ws ws, void* out, int B, int Hq,
+                       int Hkv, int L, int block, float qscale, AttnSplit sp,
+                       hipStream_t stream) {
+  switch (block) {
+    case 16:
+      return launch_mfma_bs<D, G, 16>(q, k, v, sel_idx, sel_cnt, K_max, ws, B, Hq, Hkv, L,
+                                      qscale, sp, stream);
+    case 32:
+      return launch_mfma_bs<D, G, 32>(q, k, v, sel_idx, sel_cnt, K_max, ws, B, Hq, Hkv, L,
+                                      qscale, sp, stream);
+    case 128:
+      return launch_mfma_bs<D, G, 128>(q, k, v, sel_idx, sel_cnt, K_max, ws, B, Hq, Hkv, L,
+                                       qscale, sp, stream);
+    default:
+      return launch_mfma_bs<D, G, 64>(q, k, v, sel_idx, sel_cnt, K_max, ws, B, Hq, Hkv, L,
+                                      qscale, sp, stream);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
                     const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, Ws ws,
-                    void* out, int B, int Hq, int Hkv, int L, float qscale, AttnSplit sp,
-                    hipStream_t stream) {
+                    void* out, int B, int Hq, int Hkv, int L, int block, float qscale,
+                    AttnSplit sp, hipStream_t stream) {
   const int G = Hq / Hkv;
   hipError_t e;
-#define SPOT_ARGS q, k, v, sel_idx, sel_cnt, K_max, ws, out, B, Hq, Hkv, L, qscale, sp, stream
+#define SPOT_ARGS \
+  q, k, v, sel_idx, sel_cnt, K_max, ws, out, B, Hq, Hkv, L, block, qscale, sp, stream
   if (std::is_same<T, uint16_t>::value && fast) {
     switch (G) {
       case 1: e = launch_mfma<D, 1>(SPOT_ARGS); break;
@@ -522,21 +609,20 @@ hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
 
 }  // namespace
 
-AttnSplit attn_split_plan(int B, int Hkv, int K_max, bool bf16_fast_path) {
+AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path) {
   AttnSplit sp;
   const long units = (long)B * Hkv;
   if (!bf16_fast_path) {
     sp.blocks_per_split = 4;
   } else {
-    // the longest run (<= 64 blocks) that still gives >= 256 work-groups
-    int bps = 4;
-    for (int c = 64; c >= 4; c >>= 1) {
-      if (units * ((K_max + c - 1) / c) >= 256) {
-        bps = c;
-        break;
-      }
+    // the longest run (<= 4096 tokens, i.e. 64 chunks: at most 16 per wave, and at
+    // most 64 list entries per wave) that still gives >= 256 work-groups
+    int bps = 0;
+    for (int tokens = 4096; tokens >= 256 && bps == 0; tokens >>= 1) {
+      const int c = tokens / block;
+      if (units * ((K_max + c - 1) / c) >= 256) bps = c;
     }
-    sp.blocks_per_split = bps;
+    sp.blocks_per_split = bps > 0 ? bps : 256 / block;
   }
   sp.nsplit = (K_max + sp.blocks_per_split - 1) / sp.blocks_per_split;
   return sp;
@@ -550,20 +636,20 @@ size_t attn_workspace_bytes(int B, int Hq, int d, int K_max) {
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,
                               int K_max, void* out, void* workspace, int B, int Hq, int Hkv,
-                              int d, int L, float sm_scale, hipStream_t stream) {
+                              int d, int L, int block, float sm_scale, hipStream_t stream) {
   const bool fast = bf16;
-  const AttnSplit sp = attn_split_plan(B, Hkv, K_max, fast);
+  const AttnSplit sp = attn_split_plan(B, Hkv, K_max, block, fast);
   const Ws ws = carve(workspace, B, Hq, d, sp.nsplit);
   const float qscale = sm_scale * kLog2e;
   if (bf16)
     return d == 64 ? launch_d<uint16_t, 64>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
-                                            ws, out, B, Hq, Hkv, L, qscale, sp, stream)
+                                            ws, out, B, Hq, Hkv, L, block, qscale, sp, stream)
                    : launch_d<uint16_t, 128>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,
-                                             ws, out, B, Hq, Hkv, L, qscale, sp, stream);
+                                             ws, out, B, Hq, Hkv, L, block, qscale, sp, stream);
   return d == 64 ? launch_d<float, 64>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max, ws,
-                                       out, B, Hq, Hkv, L, qscale, sp, stream)
+                                       out, B, Hq, Hkv, L, block, qscale, sp, stream)
                  : launch_d<float, 128>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max, ws,
-                                        out, B, Hq, Hkv, L, qscale, sp, stream);
+                                        out, B, Hq, Hkv, L, block, qscale, sp, stream);
 }
 
 }  // namespace spot

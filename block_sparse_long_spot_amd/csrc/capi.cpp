@@ -111,12 +111,12 @@ int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, in
     return SPOT_ERR_INVALID;
   const int G = Hq / Hkv;
   if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;
-  if (block != 64) return SPOT_ERR_UNSUPPORTED;
+  if (block != 16 && block != 32 && block != 64 && block != 128) return SPOT_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
   if (B > kMaxGrid || Hkv > kMaxGrid || (long)B * Hq > 2147483647L) return SPOT_ERR_UNSUPPORTED;
   return from_hip(spot::launch_sparse_attn(q, k_cache, v_cache, kv_dtype == SPOT_BF16, sel_idx,
                                            sel_cnt, K_max, out, workspace, B, Hq, Hkv, d, L,
-                                           sm_scale, as_stream(stream)));
+                                           block, sm_scale, as_stream(stream)));
 }
 
 int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,

@@ -25,13 +25,13 @@ struct AttnSplit {
   int blocks_per_split;
   int nsplit;
 };
-AttnSplit attn_split_plan(int B, int Hkv, int K_max, bool bf16_fast_path);
+AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path);
 size_t attn_workspace_bytes(int B, int Hq, int d, int K_max);
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,
                               int K_max, void* out, void* workspace, int B, int Hq, int Hkv,
-                              int d, int L, float sm_scale, hipStream_t stream);
+                              int d, int L, int block, float sm_scale, hipStream_t stream);
 
 hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
                                        const void* sel_k, float* scores, int B, int Tq,

@@ -72,7 +72,10 @@ class Workload:
 
 # The five workloads: a small fp32 case, the Qwen3-8B-shaped layer at 32K, the
 # same layer at 128K (batch 1 and 8), the 128K batch-8 case with an INT4 selector
-# cache, and a 128-query prefill tile at 32K.
+# cache, and a 128-query prefill tile at 32K. A sixth uses the paper's own selector
+# geometry and inference settings (Appendix A, Table 3): 16-token blocks, one selector
+# key per token (4 heads x 128), sink 128 tokens, recency 256 tokens, a K_min floor of
+# 512 tokens, dual top-p at p = 0.9 and no cap on |S|.
 WORKLOADS = {
     "c1_small_f32": Workload(
         "c1_small_f32", B=1, Hq=8, Hkv=2, d=64, L=4096, block=64, H_idx=4, d_idx=32, kpb=1,
@@ -98,6 +101,10 @@ WORKLOADS = {
         "c5_prefill_32k", B=1, Hq=32, Hkv=8, d=128, L=32768, block=64, H_idx=4, d_idx=64,
         kpb=1, dtype="bf16", sel_k_dtype="bf16", p=0.95, K_min=0, K_max=512, n_sink=1,
         n_rec=4, structure="none", prefill_Tq=128, seed=46),
+    "page_128k_b1": Workload(
+        "page_128k_b1", B=1, Hq=32, Hkv=8, d=128, L=131072, block=16, H_idx=4, d_idx=128,
+        kpb=16, dtype="bf16", sel_k_dtype="bf16", p=0.9, K_min=32, K_max=8192, n_sink=8,
+        n_rec=16, structure="zipf", zipf_s=1.1, seed=47),
 }
 
 

@@ -138,7 +138,8 @@ SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max
  * Split-K: each work-group reduces a run of selected blocks of one (b, KV head) with an
  * online softmax; a second kernel merges the runs of every (b, head) in run order, so
  * the result is deterministic.
- * Supported: d in {64, 128}; block == 64; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
+ * Supported: d in {64, 128}; block in {16, 32, 64, 128} tokens (16 is the paper's page
+ * size, Appendix A Table 3); Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
  */
 SPOT_API int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               int kv_dtype, const int32_t* sel_idx, const int32_t* sel_cnt,

@@ -101,7 +101,8 @@ def test_sparse_attn_validation(lib):
     assert attn(lib, L=0) == INVALID
     assert attn(lib, sm_scale=float("nan")) == INVALID
     assert attn(lib, d=96) == UNSUPPORTED
-    assert attn(lib, block=16) == UNSUPPORTED
+    assert attn(lib, block=48) == UNSUPPORTED
+    assert attn(lib, block=256) == UNSUPPORTED
     assert attn(lib, Hq=48, Hkv=3) == UNSUPPORTED           # 16 heads per KV head
     ws = _lib.spot_sparse_attn_workspace_bytes(8, 32, 128, 256)
     assert ws == 8 * 32 * 256 * 130 * 4      # fp32 partial results and (m, l) per run

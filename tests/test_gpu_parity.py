@@ -246,13 +246,43 @@ def _sets_for(pattern, B, nb, K_max, g):
 @pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_sparse_attn_parity(case):
     B, Hq, Hkv, d, L, K_max, dt, pattern = case
-    log(f"attn case {case}")
-    g = cpu_gen(L + d + K_max)
+    _attn_case(B, Hq, Hkv, d, L, 64, K_max, dt, pattern, tag=str(case))
+
+
+ATTN_BLOCK_CASES = [
+    # B, Hq, Hkv, d, L, block, K_max, dtype, pattern
+    (1, 32, 8, 128, 4096, 16, 200, "bf16", "random"),
+    (2, 8, 2, 64, 1000, 16, 40, "bf16", "ragged_last"),     # last block of 8 tokens
+    (2, 8, 2, 128, 777, 32, 13, "bf16", "ragged_last"),
+    (2, 16, 4, 128, 5000, 128, 30, "bf16", "random"),
+    (1, 8, 8, 64, 300, 128, 3, "bf16", "all"),              # a chunk wholly past L
+    (3, 32, 8, 128, 2048, 16, 64, "bf16", "invalid_entries"),
+    (3, 8, 2, 128, 1024, 32, 8, "bf16", "empty_rows"),
+    (2, 8, 1, 128, 3000, 16, 7, "bf16", "random"),          # G = 8
+    (2, 8, 2, 64, 1500, 16, 50, "f32", "random"),
+    (2, 8, 2, 128, 1000, 128, 6, "f32", "ragged_last"),
+    (2, 4, 4, 64, 900, 32, 20, "f32", "random"),
+    # longest runs of the split plan: 16 chunks per wave (64 list entries at block 16)
+    (4, 8, 8, 64, 32768, 16, 2048, "bf16", "random"),
+    (8, 8, 8, 64, 16384, 32, 512, "bf16", "random"),
+    (8, 8, 8, 64, 16384, 128, 128, "bf16", "all"),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_BLOCK_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_sparse_attn_block_sizes(case):
+    B, Hq, Hkv, d, L, block, K_max, dt, pattern = case
+    _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag=str(case), dirty_ws=True)
+
+
+def _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag, dirty_ws=False):
+    log(f"attn case {tag}")
+    g = cpu_gen(L + d + K_max + (block if block != 64 else 0))
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     q = torch.randn(B, Hq, d, generator=g).to(tdt)
     K = torch.randn(B, Hkv, L, d, generator=g).to(tdt)
     V = torch.randn(B, Hkv, L, d, generator=g).to(tdt)
-    nb = -(-L // 64)
+    nb = -(-L // block)
     sets = _sets_for(pattern, B, nb, K_max, g)
     idx = torch.full((B, K_max), -1, dtype=torch.int32)
     cnt = torch.zeros(B, dtype=torch.int32)
@@ -268,14 +298,16 @@ def test_sparse_attn_parity(case):
             idx[b, 0] = -1
     scale = 1.0 / math.sqrt(d)
     out = torch.full((B, Hq, d), float("nan"), device=DEV).to(tdt)
-    ws = torch.zeros(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
-                     device=DEV)
+    # workspace contents on entry do not matter: optionally start from all-NaN bytes
+    ws = torch.full((_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max),),
+                    255 if dirty_ws else 0, dtype=torch.uint8, device=DEV)
     idx_d, cnt_d = idx.to(DEV), cnt.to(DEV)
-    _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx_d, cnt_d, out, ws, scale)
+    _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx_d, cnt_d, out, ws, scale,
+                          block=block)
     torch.cuda.synchronize()
     used = [[int(x) for x in idx[b, : int(cnt[b])]] for b in range(B)]
-    ref = O.sparse_attention(np64(q), np64(K), np64(V), used, 64, scale)
-    assert_out_close(np64(out), ref, tdt, tag=str(case))
+    ref = O.sparse_attention(np64(q), np64(K), np64(V), used, block, scale)
+    assert_out_close(np64(out), ref, tdt, tag=tag)
 
 
 def test_sparse_attn_deterministic():
@@ -407,6 +439,19 @@ def test_workload_static_topk_half(big_inputs):
     rows = [(b, (7 * b + 1) % wl.Hq) for b in range(wl.B)]
     bufs, sets = run_e2e(wl, inp, check_rows=rows, tag="c3-static-half")
     assert all(len(s) == wl.nb // 2 for s in sets)
+
+
+def test_workload_page_geometry(big_inputs):
+    """The paper's own geometry end to end at 128K: 16-token blocks, 16 per-token
+    selector keys per block (4 heads x 128), Table 3's sink / recency / K_min, p = 0.9
+    with no cap. Every score and the whole selection against the oracle, sampled heads
+    of the output."""
+    wl = W.WORKLOADS["page_128k_b1"]
+    inp = big_inputs(wl.name)
+    rows = [(0, 0), (0, 13), (0, 31)]
+    bufs, sets = run_e2e(wl, inp, check_rows=rows, tag=wl.name)
+    n = len(sets[0])
+    assert wl.K_min <= n < wl.nb // 2, n
 
 
 def test_workload_budgets_vary(big_inputs):
