@@ -15,8 +15,10 @@ Zipf structure.
 Layouts (row-major, innermost last):
   sel_q  [B][H_idx][d_idx]           (decode)   or [B][Tq][H_idx][d_idx] (prefill)
   sel_w  [B][H_idx] fp32             (decode)   or [B][Tq][H_idx]        (prefill)
-  sel_k  [B][nb][kpb][H_idx][d_idx]  fp32/bf16, or INT4 codes
-         [B][nb][kpb][H_idx][d_idx/2] uint8 + fp16 scales [B][nb][kpb][H_idx][d_idx/32]
+  sel_k  [B][nb][kpb][H_idx][d_idx]  fp32/bf16, int8 or float8_e4m3fn codes (with one
+         fp32 scale [1]), or 4-bit codes [B][nb][kpb][H_idx][d_idx/2] uint8 with
+         scales [B][nb][kpb][H_idx][d_idx/32]: fp16 for INT4, E8M0 bytes for FP4
+  sel_q  may be quantised the same ways (Workload.sel_q_dtype)
   q      [B][Hq][d]                  (decode)   or [B][Hq][Tq][d]        (prefill)
   K, V   [B][Hkv][L][d]
 """
@@ -41,7 +43,7 @@ class Workload:
     d_idx: int
     kpb: int
     dtype: str            # "f32" or "bf16": q, K, V, selector query and selector keys
-    sel_k_dtype: str      # "f32", "bf16" or "int4"
+    sel_k_dtype: str      # "f32", "bf16", "int8", "fp8", "int4" or "fp4"
     p: float
     K_min: int
     K_max: int
@@ -53,6 +55,7 @@ class Workload:
     zipf_spread: Optional[tuple] = None   # (s_lo, s_hi) across the batch
     prefill_Tq: int = 0   # > 0: a prefill tile of Tq queries ending at position L-1
     seed: int = 42
+    sel_q_dtype: Optional[str] = None     # quantised selector query (None: dtype)
 
     @property
     def nb(self) -> int:
@@ -139,6 +142,62 @@ def quantize_int4_g32(x: torch.Tensor):
     return codes.contiguous(), scale16.contiguous()
 
 
+def quantize_int8_tensor(x: torch.Tensor):
+    """Symmetric INT8 with one fp32 scale for the whole tensor: scale = amax / 127,
+    code = clamp(round_half_even(x / scale), -127, 127). 8 bits per element. Returns
+    (codes int8, scale float32 [1])."""
+    amax = x.float().abs().amax()
+    scale = (amax / 127.0).clamp_min(torch.finfo(torch.float32).tiny).reshape(1)
+    codes = torch.round(x.float() / scale).clamp(-127, 127).to(torch.int8)
+    return codes.contiguous(), scale.float().contiguous()
+
+
+def quantize_fp8_e4m3_tensor(x: torch.Tensor):
+    """FP8 E4M3 with one fp32 scale for the whole tensor: scale = amax / 448 (the
+    largest finite E4M3 value), codes = x / scale rounded by torch's float8_e4m3fn
+    cast (done on the CPU). 8 bits per element. Returns (codes float8_e4m3fn,
+    scale float32 [1])."""
+    amax = x.float().abs().amax()
+    scale = (amax / 448.0).clamp_min(torch.finfo(torch.float32).tiny).reshape(1)
+    codes = (x.float() / scale).cpu().to(torch.float8_e4m3fn).to(x.device)
+    return codes.contiguous(), scale.float().contiguous()
+
+
+_FP4_MAGS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_fp4_e2m1_g32(x: torch.Tensor):
+    """FP4 E2M1 with one E8M0 (power-of-two) scale per 32 consecutive elements of the
+    last axis: scale = 2^ceil(log2(amax / 6)) so that |x| / scale <= 6, code = the
+    nearest E2M1 value of x / scale (sign in bit 3), two codes per byte with the even
+    element in the low nibble. 4 + 8/32 = 4.25 bits per element. Returns (codes uint8
+    [..., n/2], scales uint8 [..., n/32] holding the biased exponent)."""
+    *lead, n = x.shape
+    assert n % 32 == 0
+    xg = x.float().reshape(*lead, n // 32, 32)
+    amax = xg.abs().amax(dim=-1)
+    e = torch.ceil(torch.log2(torch.where(amax > 0, amax / 6.0, torch.ones_like(amax))))
+    e = e.clamp(-127, 127)
+    scale = torch.pow(2.0, e).unsqueeze(-1)
+    y = (xg / scale).abs()
+    mags = torch.tensor(_FP4_MAGS, device=x.device)
+    mids = (mags[1:] + mags[:-1]) / 2
+    mag_code = torch.bucketize(y, mids)                    # index of the nearest magnitude
+    sign = ((xg < 0) & (mag_code > 0)).to(torch.int64) << 3
+    nib = (mag_code | sign).reshape(*lead, n).to(torch.uint8)
+    codes = nib[..., 0::2] | (nib[..., 1::2] << 4)
+    scales = (e + 127).to(torch.uint8)
+    return codes.contiguous(), scales.contiguous()
+
+
+def quantize_selector(x: torch.Tensor, fmt: str):
+    """Encode x in one of the selector-cache formats; returns (codes, scale or None)."""
+    if fmt in ("f32", "bf16"):
+        return x.to(_tdtype(fmt)).contiguous(), None
+    return {"int4": quantize_int4_g32, "int8": quantize_int8_tensor,
+            "fp8": quantize_fp8_e4m3_tensor, "fp4": quantize_fp4_e2m1_g32}[fmt](x)
+
+
 def make_inputs(wl: Workload, device="cpu", seed: Optional[int] = None,
                 B: Optional[int] = None) -> dict:
     """Draw one batch of inputs for workload ``wl`` on ``device``.
@@ -212,13 +271,10 @@ def make_inputs(wl: Workload, device="cpu", seed: Optional[int] = None,
             noise = noise - proj * qh
             keys = (t / wsum).view(n_res, 1, 1, 1) * (qh / qn2) + noise
             sel_k[b, residual.to(device)] = keys
-    out = {"sel_q": sel_q.to(dt), "sel_w": sel_w, "q": q.to(dt), "K": K, "V": V,
-           "planted": planted}
-    if wl.sel_k_dtype == "int4":
-        codes, scales = quantize_int4_g32(sel_k)
-        out["sel_k"] = codes
-        out["sel_k_scale"] = scales
+    out = {"sel_w": sel_w, "q": q.to(dt), "K": K, "V": V, "planted": planted}
+    if wl.sel_q_dtype is None:
+        out["sel_q"], out["sel_q_scale"] = sel_q.to(dt), None
     else:
-        out["sel_k"] = sel_k.to(_tdtype(wl.sel_k_dtype))
-        out["sel_k_scale"] = None
+        out["sel_q"], out["sel_q_scale"] = quantize_selector(sel_q, wl.sel_q_dtype)
+    out["sel_k"], out["sel_k_scale"] = quantize_selector(sel_k, wl.sel_k_dtype)
     return out

@@ -62,6 +62,68 @@ def dequant_int4_g32(codes, scales):
 
 
 # ---------------------------------------------------------------------------
+# The other selector-cache precisions of §5.3 and Appendix G (Table 9): INT8 and FP8
+# at 0.500x the BF16 footprint (so no per-group scale: one scale for the tensor), and
+# FP4 microscale at group 32. The FP4 scale is read as an 8-bit power of two (E8M0):
+# §5.3 prints 1.20 GiB for FP4 against 1.27 GiB for INT4 from the same 4.50 GiB, i.e.
+# 4.25 bits per element, one byte of scale per 32 elements.
+# ---------------------------------------------------------------------------
+def dequant_int8(codes, scale):
+    """Decode INT8 codes (two's complement) with one scale for the whole tensor:
+    value = code * scale, exactly. codes int8 [...]; scale a float32 number."""
+    c = np.asarray(codes).astype(np.int8).astype(np.float64)
+    return c * float(np.float32(scale))
+
+
+def decode_fp8_e4m3(codes):
+    """FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; subnormals
+    at exponent 0; no infinities; exponent and mantissa all ones is NaN): float64."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** (1 - 7), (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (b & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def dequant_fp8_e4m3(codes, scale):
+    """FP8 E4M3 codes times one scale for the whole tensor, exactly."""
+    return decode_fp8_e4m3(codes) * float(np.float32(scale))
+
+
+def decode_fp4_e2m1(nibbles):
+    """FP4 E2M1 (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent 0
+    is subnormal): the 16 codes are +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}. float64."""
+    n = np.asarray(nibbles).astype(np.int64) & 0xF
+    sign = np.where(n & 0x8, -1.0, 1.0)
+    e = (n >> 1) & 0x3
+    m = (n & 0x1).astype(np.float64)
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * 2.0 ** (e - 1.0))
+    return sign * mag
+
+
+def decode_e8m0(codes):
+    """E8M0 scale: 2 ** (code - 127); code 255 is NaN. float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(c == 255, np.nan, 2.0 ** (c - 127.0))
+
+
+def dequant_fp4_e2m1_g32(codes, scales):
+    """FP4 E2M1 codes, two per byte (element 2i in the low nibble), with one E8M0 scale
+    byte per 32 elements: value = fp4 * 2 ** (scale - 127), exactly.
+    codes uint8 [..., n/2]; scales uint8 [..., n/32]. Returns float64 [..., n]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n = codes.shape[-1] * 2
+    vals = np.empty(codes.shape[:-1] + (n,), dtype=np.float64)
+    vals[..., 0::2] = decode_fp4_e2m1(codes & 0x0F)
+    vals[..., 1::2] = decode_fp4_e2m1(codes >> 4)
+    scale_per_elem = np.repeat(decode_e8m0(scales), 32, axis=-1)
+    assert scale_per_elem.shape == vals.shape
+    return vals * scale_per_elem
+
+
+# ---------------------------------------------------------------------------
 # Selector scoring (§2.1 score formula; §2.3 per-block maximum).
 # ---------------------------------------------------------------------------
 def select_score(sel_q, sel_w, sel_k):

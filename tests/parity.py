@@ -26,11 +26,28 @@ def np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def decode_selector(codes, scale) -> np.ndarray:
+    """A selector tensor in any of the library's formats, decoded by the oracle to
+    float64 (the format follows from the dtypes, as in the binding)."""
+    if codes.dtype == torch.int8:
+        return O.dequant_int8(codes.cpu().numpy(), scale.cpu().numpy()[0])
+    if codes.dtype == torch.float8_e4m3fn:
+        return O.dequant_fp8_e4m3(codes.view(torch.uint8).cpu().numpy(),
+                                  scale.cpu().numpy()[0])
+    if codes.dtype == torch.uint8 and scale.dtype == torch.float16:
+        return O.dequant_int4_g32(codes.cpu().numpy(), scale.cpu().numpy())
+    if codes.dtype == torch.uint8 and scale.dtype == torch.uint8:
+        return O.dequant_fp4_e2m1_g32(codes.cpu().numpy(), scale.cpu().numpy())
+    assert scale is None
+    return np64(codes)
+
+
 def decoded_keys(inp) -> np.ndarray:
-    k = inp["sel_k"]
-    if k.dtype == torch.uint8:
-        return O.dequant_int4_g32(k.cpu().numpy(), inp["sel_k_scale"].cpu().numpy())
-    return np64(k)
+    return decode_selector(inp["sel_k"], inp.get("sel_k_scale"))
+
+
+def decoded_query(inp) -> np.ndarray:
+    return decode_selector(inp["sel_q"], inp.get("sel_q_scale"))
 
 
 def score_magnitude(sel_q, sel_w, keys) -> np.ndarray:

@@ -16,7 +16,8 @@ from block_sparse_long_spot_amd import workloads as W
 from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
 from oracle import spot_oracle as O
 from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
-                    assert_topp_unit, decoded_keys, gpu_sets, np64, score_magnitude)
+                    assert_topp_unit, decoded_keys, decoded_query, gpu_sets, np64,
+                    score_magnitude)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -339,9 +340,10 @@ def run_e2e(wl, inp_dev, check_rows=None, tag=""):
     torch.cuda.synchronize()
     log(f"{tag}: GPU step done")
     keys = decoded_keys(inp_dev)
-    ref_scores = O.select_score(np64(inp_dev["sel_q"]), np64(inp_dev["sel_w"]), keys)
+    qdec = decoded_query(inp_dev)
+    ref_scores = O.select_score(qdec, np64(inp_dev["sel_w"]), keys)
     assert_scores_close(np64(bufs.scores), ref_scores,
-                        score_magnitude(np64(inp_dev["sel_q"]), np64(inp_dev["sel_w"]), keys))
+                        score_magnitude(qdec, np64(inp_dev["sel_w"]), keys))
     sets = gpu_sets(bufs.sel_idx, bufs.sel_cnt)
     pf = float(np.float32(wl.p))
     for b in range(B):

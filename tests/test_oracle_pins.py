@@ -110,6 +110,107 @@ def test_int4_group_scale_and_quantizer_roundtrip():
     np.testing.assert_allclose(scales.float().numpy(), (g / 7).half().float().numpy())
 
 
+# ----------------------------------------------------------------------------- int8, fp8, fp4
+def test_int8_every_code_value():
+    codes = np.arange(-128, 128, dtype=np.int64).astype(np.int8)
+    v = O.dequant_int8(codes, np.float32(0.375))
+    np.testing.assert_array_equal(v, np.arange(-128, 128) * 0.375)
+
+
+def test_fp8_e4m3_matches_torch_on_every_code():
+    # library routine: torch's float8_e4m3fn (the OCP E4M3 format) widened to float32
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    got = O.decode_fp8_e4m3(codes)
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all() and nan.sum() == 2     # 0x7F and 0xFF
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+
+
+def test_fp8_e4m3_closed_forms():
+    d = O.decode_fp8_e4m3
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0
+    assert d(0x7E) == 448.0                    # largest finite value
+    assert d(0x08) == 2.0 ** -6                # smallest normal
+    assert d(0x01) == 2.0 ** -9                # smallest subnormal
+    assert d(0x07) == 7 * 2.0 ** -9            # largest subnormal
+    assert O.dequant_fp8_e4m3(np.array([0x40], np.uint8), 0.5)[0] == 1.0   # 2 * 0.5
+
+
+def test_e8m0_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().double().numpy()
+    got = O.decode_e8m0(codes)
+    assert np.isnan(got[255]) and np.isnan(want[255])
+    np.testing.assert_array_equal(got[:255], want[:255])
+    assert got[127] == 1.0 and got[130] == 8.0 and got[0] == 2.0 ** -127
+
+
+def test_fp4_e2m1_code_table():
+    # E2M1: the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, sign in bit 3
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = O.decode_fp4_e2m1(np.arange(16))
+    np.testing.assert_array_equal(got[:8], mags)
+    np.testing.assert_array_equal(got[8:], [-m for m in mags])
+    # every magnitude is (1 + m/2) * 2^(e-1) for e >= 1, m/2 for e = 0
+    for n in range(8):
+        e, m = n >> 1, n & 1
+        assert got[n] == ((1 + m / 2) * 2.0 ** (e - 1) if e else m / 2)
+
+
+def test_fp4_g32_nibble_order_and_scale():
+    codes = np.zeros((2, 16), np.uint8)
+    codes[0, 0] = 0x7A                 # element 0: 0xA = -1.0, element 1: 0x7 = 6.0
+    codes[1, 15] = 0x91                # element 30: 0x1 = 0.5, element 31: 0x9 = -0.5
+    scales = np.array([[129], [125]], np.uint8)        # 2^2 and 2^-2
+    v = O.dequant_fp4_e2m1_g32(codes, scales)
+    assert v.shape == (2, 32)
+    assert v[0, 0] == -4.0 and v[0, 1] == 24.0 and (v[0, 2:] == 0).all()
+    assert v[1, 30] == 0.125 and v[1, 31] == -0.125 and (v[1, :30] == 0).all()
+
+
+def test_quantizers_roundtrip_within_format_step():
+    from block_sparse_long_spot_amd.workloads import (quantize_fp4_e2m1_g32,
+                                                       quantize_fp8_e4m3_tensor,
+                                                       quantize_int8_tensor)
+    x = torch.randn(3, 4, 64, generator=torch.Generator().manual_seed(9))
+    xd = x.double().numpy()
+    c8, s8 = quantize_int8_tensor(x)
+    assert c8.dtype == torch.int8 and s8.numel() == 1
+    v = O.dequant_int8(c8.numpy(), s8.numpy()[0])
+    assert np.abs(v - xd).max() <= 0.5 * float(s8[0]) * (1 + 1e-6)
+    cf, sf = quantize_fp8_e4m3_tensor(x)
+    assert cf.dtype == torch.float8_e4m3fn and sf.numel() == 1
+    v = O.dequant_fp8_e4m3(cf.view(torch.uint8).numpy(), sf.numpy()[0])
+    # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 above the subnormal range
+    big = np.abs(xd) > 2.0 ** -6 * float(sf[0])
+    assert (np.abs(v - xd)[big] <= 2.0 ** -4 * np.abs(xd)[big] * (1 + 1e-6)).all()
+    c4, s4 = quantize_fp4_e2m1_g32(x)
+    assert c4.shape == (3, 4, 32) and s4.shape == (3, 4, 2) and s4.dtype == torch.uint8
+    v = O.dequant_fp4_e2m1_g32(c4.numpy(), s4.numpy())
+    scale = np.repeat(O.decode_e8m0(s4.numpy()), 32, -1)
+    # each group's largest magnitude fits under 6 * scale, and the error is at most half
+    # the widest gap between neighbouring E2M1 values (2 * scale, between 4 and 6)
+    assert (np.abs(xd) <= 6 * scale * (1 + 1e-9)).all()
+    assert (np.abs(v - xd) <= 1.0 * scale * (1 + 1e-9)).all()
+
+
+def test_8bit_and_fp4_footprints_match_pages_figures():
+    fig = json.load(open(GOLDEN))
+    n = 1024
+    assert 8 * n / (16 * n) == fig["int8_fraction_of_bf16"]["value"]
+    assert 8 * n / (16 * n) == fig["fp8_fraction_of_bf16"]["value"]
+    # FP4: 4-bit codes plus one E8M0 byte per group of 32 = 4.25 bits per element, which
+    # is what the printed 1.20 GiB (from 4.50 GiB of BF16) implies; a 16-bit group scale
+    # (4.5 bits) would print INT4's 1.27 GiB instead
+    grp = fig["fp4_group"]["value"]
+    bits = 8 * (n // 2 + n // grp) / n
+    bf16 = fig["selector_cache_gib_bf16_128k"]["value"]
+    assert bits == 4.25
+    assert round(bf16 * bits / 16, 2) == fig["selector_cache_gib_fp4_128k"]["value"]
+    assert round(bf16 * 4.5 / 16, 2) != fig["selector_cache_gib_fp4_128k"]["value"]
+
+
 def test_int4_bytes_match_pages_figures():
     fig = json.load(open(GOLDEN))
     n = 1024
