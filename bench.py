@@ -118,7 +118,7 @@ def time_steps(inp, wl, bufs, steps, warmup, stream):
             ev[i][0].record(stream)
             spot.spot_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"],
                                    inp.get("sel_k_scale"), bufs.scores, kpb=wl.kpb,
-                                   stream=stream)
+                                   stream=stream, sel_q_scale=inp.get("sel_q_scale"))
             ev[i][1].record(stream)
             spot.spot_select_topp(bufs.scores, bufs.sel_idx, bufs.sel_cnt, bufs.sel_mass, wl.p,
                                   wl.K_min, wl.K_max, wl.n_sink, wl.n_rec, stream=stream)
@@ -280,6 +280,37 @@ def page_geometry_step(steps, warmup, stream):
            "score_GBps": round(bb["score"] / (mean["score"] * 1e-6) / 1e9, 1),
            "paper_selector_us_per_layer_B200": round(1550.0 / 36, 1)}
     del inp, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def selector_formats_leg(steps, warmup, stream):
+    """Scoring alone at the paper's page geometry (128K context, 16 per-token keys per
+    16-token block, 4 heads x 128, batch 1) with the key cache in each precision of
+    §5.3 / Table 9: µs per call (events around back-to-back calls) and key bytes per
+    second. Table 1 reports the paper's selector slower at INT4 (1.91 ms) and FP4
+    (2.51 ms) than at BF16 (1.55 ms) on one B200, from dequantisation overhead."""
+    wl = W.WORKLOADS["page_128k_b1"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(48)
+    shape_k = (1, wl.nb, wl.kpb, wl.H_idx, wl.d_idx)
+    raw = torch.randn(*shape_k, generator=gen, device="cuda")
+    sel_q = torch.randn(1, wl.H_idx, wl.d_idx, generator=gen, device="cuda").bfloat16()
+    sel_w = torch.randn(1, wl.H_idx, generator=gen, device="cuda").abs()
+    scores = torch.empty(1, wl.nb, device="cuda")
+    res = {"geometry": "L 131072, block 16, 16 keys per block, 4 x 128, batch 1, bf16 query"}
+    for fmt in ("bf16", "int8", "fp8", "int4", "fp4"):
+        codes, scale = W.quantize_selector(raw, fmt)
+        nbytes = codes.numel() * codes.element_size() + (
+            scale.numel() * scale.element_size() if scale is not None and scale.numel() > 1
+            else 0)
+        us, _ = time_back_to_back(
+            lambda: spot.spot_select_score(sel_q, sel_w, codes, scale, scores, kpb=wl.kpb,
+                                           stream=stream), steps, warmup, stream)
+        res[fmt] = {"us": round(us, 3), "key_bytes": nbytes,
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del codes, scale
+    del raw
     torch.cuda.empty_cache()
     return res
 
@@ -495,6 +526,8 @@ def main():
     if a.page_geometry:
         log("bench: selector at the paper's page geometry")
         result["page_geometry"] = page_geometry_step(max(10, a.steps // 4), 20, stream)
+        log("bench: selector cache formats at the paper's page geometry")
+        result["selector_formats"] = selector_formats_leg(max(10, a.steps // 4), 20, stream)
     result["calibration_copy_bytes"] = calibration_copy()
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libspot.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "spot.h")
 
 SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_DEVICE = 0, -1, -2, -3
-SPOT_F32, SPOT_BF16, SPOT_INT4_G32 = 0, 1, 2
+SPOT_F32, SPOT_BF16, SPOT_INT4_G32, SPOT_INT8, SPOT_FP8_E4M3, SPOT_FP4_E2M1_G32 = range(6)
+ABI_VERSION = 2
 
 _lib = None
 
@@ -40,7 +41,7 @@ def load() -> ctypes.CDLL:
                            "`python -m block_sparse_long_spot_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.spot_select_score.argtypes = [vp, i, vp, vp, vp, i, vp, i, i, i, i, i, vp]
+    lib.spot_select_score.argtypes = [vp, i, vp, vp, vp, vp, i, vp, i, i, i, i, i, vp]
     lib.spot_select_score.restype = i
     lib.spot_select_topp.argtypes = [vp, vp, vp, vp, i, i, f, i, i, i, i, vp]
     lib.spot_select_topp.restype = i
@@ -59,6 +60,9 @@ def load() -> ctypes.CDLL:
     lib.spot_status_string.restype = ctypes.c_char_p
     lib.spot_abi_version.argtypes = []
     lib.spot_abi_version.restype = i
+    if lib.spot_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI {lib.spot_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -101,20 +105,47 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def spot_select_score(sel_q, sel_w, sel_k, sel_k_scale, scores, kpb: int = 1, stream=None):
-    """scores[B][nb] <- selector block scores. sel_k is [B][nb][kpb][H][d_idx] (fp32/bf16)
-    or INT4 codes uint8 [B][nb][kpb][H][d_idx/2] with sel_k_scale fp16 [..][d_idx/32]."""
-    B, H, d_idx = sel_q.shape
+def selector_format(codes: torch.Tensor, scale: Optional[torch.Tensor]):
+    """The C ABI format code of a selector tensor and how many elements one stored
+    element of its last axis holds, from the torch dtypes:
+      float32 / bfloat16, no scale               -> SPOT_F32 / SPOT_BF16
+      int8 codes, float32 scale [1]              -> SPOT_INT8
+      float8_e4m3fn codes, float32 scale [1]     -> SPOT_FP8_E4M3
+      uint8 (two 4-bit codes), float16 scales    -> SPOT_INT4_G32
+      uint8 (two 4-bit codes), uint8 E8M0 scales -> SPOT_FP4_E2M1_G32"""
+    dt = codes.dtype
+    if dt in (torch.float32, torch.bfloat16):
+        if scale is not None:
+            raise ValueError("fp32/bf16 selector tensors take no scale")
+        return _dtype_code(codes), 1
+    if scale is None:
+        raise ValueError(f"a {dt} selector tensor needs its scale tensor")
+    if dt in (torch.int8, torch.float8_e4m3fn):
+        if scale.dtype != torch.float32 or scale.numel() != 1:
+            raise ValueError("INT8 / FP8 selector tensors take one float32 scale")
+        return (SPOT_INT8 if dt == torch.int8 else SPOT_FP8_E4M3), 1
+    if dt == torch.uint8 and scale.dtype == torch.float16:
+        return SPOT_INT4_G32, 2
+    if dt == torch.uint8 and scale.dtype == torch.uint8:
+        return SPOT_FP4_E2M1_G32, 2
+    raise ValueError(f"unsupported selector format {dt} with scale {scale.dtype}")
+
+
+def spot_select_score(sel_q, sel_w, sel_k, sel_k_scale, scores, kpb: int = 1, stream=None,
+                      sel_q_scale=None):
+    """scores[B][nb] <- selector block scores. sel_q [B][H][d_idx] and sel_k
+    [B][nb][kpb][H][d_idx] in any selector format (see selector_format; 4-bit formats
+    store d_idx/2 bytes per row), each with its scale tensor or None."""
+    B, H = sel_w.shape
+    q_fmt, q_per = selector_format(sel_q, sel_q_scale)
+    k_fmt, k_per = selector_format(sel_k, sel_k_scale)
+    d_idx = sel_q.shape[-1] * q_per
+    assert sel_q.shape == (B, H, d_idx // q_per) and sel_k.shape[-1] * k_per == d_idx
     nb = scores.shape[1]
-    if sel_k.dtype == torch.uint8:
-        k_dtype = SPOT_INT4_G32
-        assert sel_k_scale is not None and sel_k_scale.dtype == torch.float16
-    else:
-        k_dtype = _dtype_code(sel_k)
     assert scores.dtype == torch.float32 and sel_w.dtype == torch.float32
-    st = load().spot_select_score(_ptr(sel_q), _dtype_code(sel_q), _ptr(sel_w), _ptr(sel_k),
-                                  _ptr(sel_k_scale), k_dtype, _ptr(scores), B, nb, kpb, H,
-                                  d_idx, _stream(stream))
+    st = load().spot_select_score(_ptr(sel_q), q_fmt, _ptr(sel_q_scale), _ptr(sel_w),
+                                  _ptr(sel_k), _ptr(sel_k_scale), k_fmt, _ptr(scores), B, nb,
+                                  kpb, H, d_idx, _stream(stream))
     _check("spot_select_score", st)
 
 

@@ -19,24 +19,48 @@ int from_hip(hipError_t e) {
 
 constexpr int kMaxGrid = 65535;  // grid.y / grid.z limit used by the launchers
 
-// Common validation of a selector-cache description; returns SPOT_OK or an error.
-int check_selector(const void* sel_q, int q_dtype, const float* sel_w, const void* sel_k,
-                   const void* sel_k_scale, int k_dtype, int H_idx, int d_idx, int kpb) {
+// A selector tensor in one of the spot_dtype formats with its scale array: the format
+// must be known, quantised formats need their scale (aligned to its element) and the
+// group formats need d_idx % 32 == 0; fp32/bf16 take no scale.
+int check_format(int fmt, const void* scale, int d_idx) {
+  switch (fmt) {
+    case SPOT_F32:
+    case SPOT_BF16:
+      return scale ? SPOT_ERR_INVALID : SPOT_OK;
+    case SPOT_INT8:
+    case SPOT_FP8_E4M3:
+      return scale && aligned(scale, 4) ? SPOT_OK : SPOT_ERR_INVALID;
+    case SPOT_INT4_G32:
+      return scale && aligned(scale, 2) && d_idx % 32 == 0 ? SPOT_OK : SPOT_ERR_INVALID;
+    case SPOT_FP4_E2M1_G32:
+      return scale && d_idx % 32 == 0 ? SPOT_OK : SPOT_ERR_INVALID;
+    default:
+      return SPOT_ERR_INVALID;
+  }
+}
+
+// elements of d_idx one 16-byte load of a key row holds, per format
+int key_chunk(int fmt) {
+  switch (fmt) {
+    case SPOT_INT8:
+    case SPOT_FP8_E4M3: return 16;
+    case SPOT_INT4_G32:
+    case SPOT_FP4_E2M1_G32: return 32;
+    default: return 8;
+  }
+}
+
+// Common validation of a selector description; returns SPOT_OK or an error.
+int check_selector(const void* sel_q, int q_dtype, const void* sel_q_scale, const float* sel_w,
+                   const void* sel_k, const void* sel_k_scale, int k_dtype, int H_idx,
+                   int d_idx, int kpb) {
   if (!sel_q || !sel_w || !sel_k) return SPOT_ERR_INVALID;
-  if (q_dtype != SPOT_F32 && q_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
-  if (k_dtype != SPOT_F32 && k_dtype != SPOT_BF16 && k_dtype != SPOT_INT4_G32)
-    return SPOT_ERR_INVALID;
   if (H_idx <= 0 || d_idx <= 0 || kpb <= 0) return SPOT_ERR_INVALID;
   if (!aligned(sel_q, 16) || !aligned(sel_w, 4) || !aligned(sel_k, 16)) return SPOT_ERR_INVALID;
-  if (k_dtype == SPOT_INT4_G32) {
-    if (!sel_k_scale || !aligned(sel_k_scale, 2)) return SPOT_ERR_INVALID;
-    if (d_idx % 32 != 0) return SPOT_ERR_INVALID;
-  } else if (sel_k_scale) {
-    return SPOT_ERR_INVALID;
-  }
+  if (check_format(q_dtype, sel_q_scale, d_idx) != SPOT_OK) return SPOT_ERR_INVALID;
+  if (check_format(k_dtype, sel_k_scale, d_idx) != SPOT_OK) return SPOT_ERR_INVALID;
   if (d_idx != 32 && d_idx != 64 && d_idx != 128) return SPOT_ERR_UNSUPPORTED;
-  const int ch = k_dtype == SPOT_INT4_G32 ? 32 : 8;
-  const int lpr = H_idx * (d_idx / ch);
+  const int lpr = H_idx * (d_idx / key_chunk(k_dtype));
   if (!pow2(H_idx) || lpr > 64) return SPOT_ERR_UNSUPPORTED;
   return SPOT_OK;
 }
@@ -45,7 +69,7 @@ int check_selector(const void* sel_q, int q_dtype, const float* sel_w, const voi
 
 extern "C" {
 
-int spot_abi_version(void) { return 1; }
+int spot_abi_version(void) { return 2; }
 
 const char* spot_status_string(int status) {
   switch (status) {
@@ -57,15 +81,16 @@ const char* spot_status_string(int status) {
   }
 }
 
-int spot_select_score(const void* sel_q, int q_dtype, const float* sel_w, const void* sel_k,
-                      const void* sel_k_scale, int k_dtype, float* scores, int B, int nb,
-                      int kpb, int H_idx, int d_idx, void* stream) {
+int spot_select_score(const void* sel_q, int q_dtype, const void* sel_q_scale,
+                      const float* sel_w, const void* sel_k, const void* sel_k_scale,
+                      int k_dtype, float* scores, int B, int nb, int kpb, int H_idx, int d_idx,
+                      void* stream) {
   if (B <= 0 || nb <= 0 || !scores || !aligned(scores, 4)) return SPOT_ERR_INVALID;
-  const int c = check_selector(sel_q, q_dtype, sel_w, sel_k, sel_k_scale, k_dtype, H_idx,
-                               d_idx, kpb);
+  const int c = check_selector(sel_q, q_dtype, sel_q_scale, sel_w, sel_k, sel_k_scale, k_dtype,
+                               H_idx, d_idx, kpb);
   if (c != SPOT_OK) return c;
   if (B > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
-  return from_hip(spot::launch_select_score(sel_q, q_dtype == SPOT_BF16, sel_w, sel_k,
+  return from_hip(spot::launch_select_score(sel_q, q_dtype, sel_q_scale, sel_w, sel_k,
                                             sel_k_scale, k_dtype, scores, B, nb, kpb, H_idx,
                                             d_idx, as_stream(stream)));
 }
@@ -125,8 +150,8 @@ int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w
                               int H_idx, int d_idx, int block, void* stream) {
   if (B <= 0 || Tq <= 0 || q_pos0 < 0 || nb_cache <= 0 || block <= 0) return SPOT_ERR_INVALID;
   if (!scores || !aligned(scores, 4)) return SPOT_ERR_INVALID;
-  const int c = check_selector(sel_q, q_dtype, sel_w, sel_k, sel_k_scale, k_dtype, H_idx,
-                               d_idx, kpb);
+  const int c = check_selector(sel_q, q_dtype, nullptr, sel_w, sel_k, sel_k_scale, k_dtype,
+                               H_idx, d_idx, kpb);
   if (c != SPOT_OK) return c;
   const long nb_vis = ((long)q_pos0 + Tq + block - 1) / block;
   if (nb_vis > nb_cache) return SPOT_ERR_INVALID;

@@ -7,13 +7,13 @@
 
 namespace spot {
 
-// Key storage kinds for the selector cache.
-enum KeyKind { kKeyF32 = 0, kKeyBF16 = 1, kKeyInt4 = 2 };
+// Selector element formats (the values of the C ABI's spot_dtype codes).
+enum Fmt { kF32 = 0, kBF16 = 1, kInt4 = 2, kInt8 = 3, kFp8 = 4, kFp4 = 5 };
 
-hipError_t launch_select_score(const void* sel_q, bool q_bf16, const float* sel_w,
-                               const void* sel_k, const void* sel_k_scale, int key_kind,
-                               float* scores, int B, int nb, int kpb, int H, int d_idx,
-                               hipStream_t stream);
+hipError_t launch_select_score(const void* sel_q, int q_fmt, const void* sel_q_scale,
+                               const float* sel_w, const void* sel_k, const void* sel_k_scale,
+                               int k_fmt, float* scores, int B, int nb, int kpb, int H,
+                               int d_idx, hipStream_t stream);
 
 hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
                               float* sel_mass, int B, int nb, float p, int K_min, int K_max,

@@ -25,7 +25,8 @@ class DecodeBuffers:
 def decode_step(inp: dict, wl, bufs: DecodeBuffers, stream=None):
     """Score every block, select each query's block set, attend over it."""
     _lib.spot_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"], inp.get("sel_k_scale"),
-                           bufs.scores, kpb=wl.kpb, stream=stream)
+                           bufs.scores, kpb=wl.kpb, stream=stream,
+                           sel_q_scale=inp.get("sel_q_scale"))
     _lib.spot_select_topp(bufs.scores, bufs.sel_idx, bufs.sel_cnt, bufs.sel_mass, wl.p,
                           wl.K_min, wl.K_max, wl.n_sink, wl.n_rec, stream=stream)
     _lib.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx, bufs.sel_cnt, bufs.out,

@@ -50,39 +50,55 @@ enum spot_status {
   SPOT_ERR_DEVICE = -3
 };
 
+/* Element formats. The quantised ones (§5.3 and Appendix G, Table 9: the selector's
+ * queries and key cache at INT8, INT4, FP8 and FP4) are selector-only. */
 enum spot_dtype {
-  SPOT_F32 = 0,      /* IEEE binary32 */
-  SPOT_BF16 = 1,     /* bfloat16 */
-  SPOT_INT4_G32 = 2  /* selector keys only: 4-bit two's-complement codes, two per byte
-                        (even element in the low nibble), plus one IEEE binary16 scale
-                        per 32 consecutive elements of d_idx: value = code * scale.
-                        4.5 bits per element (§5.3 and Appendix G, Table 9). */
+  SPOT_F32 = 0,           /* IEEE binary32 */
+  SPOT_BF16 = 1,          /* bfloat16 */
+  SPOT_INT4_G32 = 2,      /* 4-bit two's-complement codes, two per byte (even element in
+                             the low nibble), one IEEE binary16 scale per 32 consecutive
+                             elements of d_idx: value = code * scale. 4.5 bits/element. */
+  SPOT_INT8 = 3,          /* 8-bit two's-complement codes with ONE fp32 scale for the
+                             whole tensor: value = code * scale. 8 bits/element (the
+                             paper's 0.500x of BF16 leaves no room for group scales). */
+  SPOT_FP8_E4M3 = 4,      /* FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+                             bits, subnormals, no infinities) with ONE fp32 scale for the
+                             whole tensor: value = fp8 * scale. 8 bits/element. */
+  SPOT_FP4_E2M1_G32 = 5   /* FP4 E2M1 codes (values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), two
+                             per byte (even element in the low nibble), one E8M0 byte per
+                             32 elements of d_idx (scale 2^(byte - 127)): value = fp4 *
+                             scale. 4.25 bits/element, the footprint §5.3 prints. */
 };
 
 /*
  * spot_select_score — selector block scores (§2.1 score formula, §2.3 block maximum).
  *
  *   scores[b][blk] = max_{j < kpb} sum_{h < H_idx} sel_w[b][h] * ReLU( sum_i
- *                    sel_q[b][h][i] * sel_k[b][blk][j][h][i] )
+ *                    q[b][h][i] * k[b][blk][j][h][i] )
  *
- * No 1/sqrt(d_idx) factor (the paper's formula has none; temperature 1, Table 3).
- *   sel_q        [B][H_idx][d_idx], q_dtype SPOT_F32 or SPOT_BF16; 16-byte aligned.
+ * where q and k are the decoded values of sel_q and sel_k. No 1/sqrt(d_idx) factor (the
+ * paper's formula has none; temperature 1, Table 3). Each of sel_q and sel_k is in one
+ * of the spot_dtype formats, with its scale array:
+ *   SPOT_F32, SPOT_BF16        elements [..][d_idx]; scale pointer NULL;
+ *   SPOT_INT8, SPOT_FP8_E4M3   codes [..][d_idx]; scale -> one fp32 (4-byte aligned);
+ *   SPOT_INT4_G32              codes uint8 [..][d_idx/2]; scales fp16 [..][d_idx/32]
+ *                              (2-byte aligned);
+ *   SPOT_FP4_E2M1_G32          codes uint8 [..][d_idx/2]; scales E8M0 bytes [..][d_idx/32].
+ *   sel_q        [B][H_idx][..] in q_dtype, with sel_q_scale; 16-byte aligned.
  *   sel_w        [B][H_idx] fp32 mixing weights (any sign); 4-byte aligned.
- *   sel_k        k_dtype SPOT_F32 / SPOT_BF16: [B][nb][kpb][H_idx][d_idx];
- *                k_dtype SPOT_INT4_G32: codes uint8 [B][nb][kpb][H_idx][d_idx/2];
- *                16-byte aligned.
- *   sel_k_scale  SPOT_INT4_G32 only: fp16 [B][nb][kpb][H_idx][d_idx/32], 2-byte
- *                aligned; must be NULL for the other key types.
+ *   sel_k        [B][nb][kpb][H_idx][..] in k_dtype, with sel_k_scale; 16-byte aligned.
  *   scores       out fp32 [B][nb]; 4-byte aligned.
  *   kpb          selector keys per block (1 = one pooled key per block; the paper's
  *                per-token form is kpb = block size).
- * Supported: d_idx in {32, 64, 128}; H_idx a power of two with H_idx*d_idx/8 <= 64
- * (fp32/bf16 keys) or H_idx*d_idx/32 <= 64 (INT4 keys).
+ * Errors: SPOT_ERR_INVALID for an unknown format, a missing scale of a quantised format,
+ * or a scale given for fp32/bf16.
+ * Supported: d_idx in {32, 64, 128}; H_idx a power of two with H_idx*d_idx/c <= 64,
+ * c = 8 (fp32/bf16 keys), 16 (INT8/FP8 keys) or 32 (INT4/FP4 keys).
  */
-SPOT_API int spot_select_score(const void* sel_q, int q_dtype, const float* sel_w,
-                               const void* sel_k, const void* sel_k_scale, int k_dtype,
-                               float* scores, int B, int nb, int kpb, int H_idx, int d_idx,
-                               void* stream);
+SPOT_API int spot_select_score(const void* sel_q, int q_dtype, const void* sel_q_scale,
+                               const float* sel_w, const void* sel_k, const void* sel_k_scale,
+                               int k_dtype, float* scores, int B, int nb, int kpb, int H_idx,
+                               int d_idx, void* stream);
 
 /*
  * spot_select_topp — dual top-p block selection (§2.3, Eq. 7 and Eq. 8).
@@ -158,8 +174,8 @@ SPOT_API int spot_sparse_attn(const void* q, const void* k_cache, const void* v_
  *                    max_{j<kpb} sum_h sel_w[b][i][h] * ReLU(sel_q[b][i][h] . sel_k[b][blk][j][h])
  * for blk < nb_vis. Computed as one matrix product per selector head on the MFMA units.
  *   sel_q   [B][Tq][H_idx][d_idx] (q_dtype), sel_w fp32 [B][Tq][H_idx];
- *   sel_k   [B][nb_cache][kpb][H_idx][d_idx] (k_dtype SPOT_F32 or SPOT_BF16; 16-byte
- *           aligned), sel_k_scale must be NULL;
+ *   sel_k   [B][nb_cache][kpb][H_idx][d_idx] (16-byte aligned), sel_k_scale must be
+ *           NULL;
  *   scores  out fp32 [B][nb_vis] (row stride nb_vis).
  * Errors: SPOT_ERR_INVALID when nb_vis > nb_cache or q_pos0 < 0.
  * Supported: d_idx in {32, 64, 128}; bf16 queries and keys; 1 <= Tq <= 128.

@@ -11,6 +11,7 @@ from block_sparse_long_spot_amd import _lib
 
 INVALID, UNSUPPORTED = _lib.SPOT_ERR_INVALID, _lib.SPOT_ERR_UNSUPPORTED
 F32, BF16, INT4 = _lib.SPOT_F32, _lib.SPOT_BF16, _lib.SPOT_INT4_G32
+INT8, FP8, FP4 = _lib.SPOT_INT8, _lib.SPOT_FP8_E4M3, _lib.SPOT_FP4_E2M1_G32
 
 
 @pytest.fixture(scope="module")
@@ -38,12 +39,13 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "SPOT_OK"
     for s in (INVALID, UNSUPPORTED, _lib.SPOT_ERR_DEVICE, 12345):
         assert isinstance(_lib.status_string(s), str) and _lib.status_string(s)
-    assert lib.spot_abi_version() == 1
+    assert lib.spot_abi_version() == 2
 
 
 def score(lib, **kw):
-    a = dict(sel_q=fake(), q_dtype=BF16, sel_w=fake(), sel_k=fake(), sel_k_scale=None,
-             k_dtype=BF16, scores=fake(), B=1, nb=8, kpb=1, H_idx=4, d_idx=64, stream=None)
+    a = dict(sel_q=fake(), q_dtype=BF16, sel_q_scale=None, sel_w=fake(), sel_k=fake(),
+             sel_k_scale=None, k_dtype=BF16, scores=fake(), B=1, nb=8, kpb=1, H_idx=4,
+             d_idx=64, stream=None)
     a.update(kw)
     return lib.spot_select_score(*a.values())
 
@@ -54,14 +56,22 @@ def test_select_score_validation(lib):
     assert score(lib, B=0) == INVALID
     assert score(lib, nb=-1) == INVALID
     assert score(lib, kpb=0) == INVALID
-    assert score(lib, q_dtype=INT4) == INVALID
+    assert score(lib, q_dtype=INT4) == INVALID                      # quantised q, no scale
+    assert score(lib, q_dtype=6) == INVALID
+    assert score(lib, sel_q_scale=fake()) == INVALID                # scale with a bf16 query
     assert score(lib, k_dtype=7) == INVALID
     assert score(lib, k_dtype=INT4) == INVALID                      # missing scales
     assert score(lib, sel_k_scale=fake()) == INVALID                # scales with bf16 keys
     assert score(lib, k_dtype=INT4, sel_k_scale=fake(), d_idx=48) == INVALID
+    assert score(lib, k_dtype=FP4, sel_k_scale=fake(), d_idx=48) == INVALID
+    assert score(lib, k_dtype=INT8, sel_k_scale=fake(0x10002)) == INVALID   # fp32 scale
+    assert score(lib, k_dtype=INT4, sel_k_scale=fake(0x10001)) == INVALID   # fp16 scales
     assert score(lib, d_idx=96) == UNSUPPORTED
     assert score(lib, H_idx=3) == UNSUPPORTED
     assert score(lib, H_idx=16, d_idx=64) == UNSUPPORTED            # 128 lanes per key row
+    # 16 (8-bit formats) or 32 (4-bit formats) elements per lane: 128 lanes again
+    assert score(lib, H_idx=32, d_idx=64, k_dtype=INT8, sel_k_scale=fake()) == UNSUPPORTED
+    assert score(lib, H_idx=64, d_idx=64, k_dtype=FP4, sel_k_scale=fake()) == UNSUPPORTED
 
 
 def topp(lib, **kw):

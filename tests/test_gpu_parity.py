@@ -16,8 +16,8 @@ from block_sparse_long_spot_amd import workloads as W
 from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
 from oracle import spot_oracle as O
 from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
-                    assert_topp_unit, decoded_keys, decoded_query, gpu_sets, np64,
-                    score_magnitude)
+                    assert_topp_unit, decode_selector, decoded_keys, decoded_query,
+                    gpu_sets, np64, score_magnitude)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,7 +40,7 @@ def cpu_gen(seed):
 
 # ------------------------------------------------------------------ spot_select_score
 SCORE_CASES = [
-    # B, nb, kpb, H, d_idx, q dtype, key kind
+    # B, nb, kpb, H, d_idx, query format, key format
     (1, 64, 1, 4, 32, "f32", "f32"),
     (3, 333, 1, 4, 64, "bf16", "bf16"),
     (2, 1000, 1, 4, 64, "f32", "bf16"),
@@ -54,32 +54,41 @@ SCORE_CASES = [
     (1, 100, 1, 2, 128, "bf16", "int4"),
     (1, 31, 1, 16, 32, "f32", "int4"),
     (2, 2048, 1, 4, 64, "bf16", "bf16"),
+    # 8-bit and FP4 key caches, and quantised queries (§5.3, Appendix G)
+    (2, 257, 1, 4, 64, "bf16", "int8"),
+    (2, 65, 5, 4, 64, "int8", "int8"),
+    (1, 40, 1, 16, 32, "bf16", "int8"),
+    (2, 300, 1, 4, 64, "bf16", "fp8"),
+    (2, 65, 3, 4, 64, "fp8", "fp8"),
+    (1, 70, 1, 8, 128, "f32", "fp8"),
+    (2, 257, 1, 4, 64, "bf16", "fp4"),
+    (1, 100, 1, 2, 128, "f32", "fp4"),
+    (1, 130, 16, 4, 128, "fp4", "fp4"),
+    (1, 40, 1, 64, 32, "bf16", "fp4"),
+    (2, 77, 1, 4, 64, "int4", "int4"),
+    (1, 31, 1, 16, 32, "fp8", "f32"),
+    (2, 50, 2, 4, 64, "int4", "bf16"),
+    (2, 2048, 1, 4, 64, "bf16", "fp4"),
 ]
 
 
 @pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_select_score_parity(case):
-    B, nb, kpb, H, di, qd, kk = case
+    B, nb, kpb, H, di, qf, kf = case
     log(f"score case {case}")
-    g = cpu_gen(nb * 7 + kpb)
-    qt = torch.float32 if qd == "f32" else torch.bfloat16
-    sel_q = torch.randn(B, H, di, generator=g).to(qt)
+    g = cpu_gen(nb * 7 + kpb + len(qf) + 3 * len(kf))
+    sel_q, q_scale = W.quantize_selector(torch.randn(B, H, di, generator=g), qf)
     sel_w = torch.randn(B, H, generator=g)            # signed weights
-    keys = torch.randn(B, nb, kpb, H, di, generator=g)
-    if kk == "int4":
-        codes, scales = W.quantize_int4_g32(keys)
-        inp = {"sel_k": codes, "sel_k_scale": scales}
-    else:
-        inp = {"sel_k": keys.to(torch.float32 if kk == "f32" else torch.bfloat16),
-               "sel_k_scale": None}
+    sel_k, k_scale = W.quantize_selector(torch.randn(B, nb, kpb, H, di, generator=g), kf)
+    dev = lambda t: None if t is None else t.to(DEV)
     scores = torch.full((B, nb), float("nan"), device=DEV)
-    _lib.spot_select_score(sel_q.to(DEV), sel_w.to(DEV), inp["sel_k"].to(DEV),
-                           None if inp["sel_k_scale"] is None else inp["sel_k_scale"].to(DEV),
-                           scores, kpb=kpb)
+    _lib.spot_select_score(dev(sel_q), sel_w.to(DEV), dev(sel_k), dev(k_scale), scores, kpb=kpb,
+                           sel_q_scale=dev(q_scale))
     torch.cuda.synchronize()
-    keys = decoded_keys(inp)
-    ref = O.select_score(np64(sel_q), np64(sel_w), keys)
-    assert_scores_close(np64(scores), ref, score_magnitude(np64(sel_q), np64(sel_w), keys))
+    qdec = decode_selector(sel_q, q_scale)
+    keys = decode_selector(sel_k, k_scale)
+    ref = O.select_score(qdec, np64(sel_w), keys)
+    assert_scores_close(np64(scores), ref, score_magnitude(qdec, np64(sel_w), keys))
 
 
 # ------------------------------------------------------------------ spot_select_topp
@@ -454,6 +463,19 @@ def test_workload_page_geometry(big_inputs):
     bufs, sets = run_e2e(wl, inp, check_rows=rows, tag=wl.name)
     n = len(sets[0])
     assert wl.K_min <= n < wl.nb // 2, n
+
+
+@pytest.mark.parametrize("kf,qf", [("int8", None), ("fp8", "fp8"), ("fp4", None),
+                                   ("fp4", "fp4"), ("int4", "int4")])
+def test_workload_selector_formats(kf, qf):
+    """The 128K layer (batch 2) with the selector key cache, and optionally the selector
+    query, stored in the other precisions of §5.3 / Table 9: all scores, the selection
+    and sampled outputs against the oracle on the same codes."""
+    wl = W.WORKLOADS["c3_128k_b8"].with_(B=2, sel_k_dtype=kf, sel_q_dtype=qf,
+                                         name=f"c3_128k_b2_{kf}_{qf}")
+    inp = W.make_inputs(wl, device=DEV)
+    bufs, sets = run_e2e(wl, inp, check_rows=[(0, 3), (1, 30)], tag=wl.name)
+    assert all(wl.K_min <= len(s) <= wl.K_max for s in sets)
 
 
 def test_workload_budgets_vary(big_inputs):
