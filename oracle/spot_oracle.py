@@ -124,6 +124,95 @@ def dequant_fp4_e2m1_g32(codes, scales):
 
 
 # ---------------------------------------------------------------------------
+# Quantisation of new selector keys into the cache formats (the write side of
+# §5.3: the selector is trained in BF16 and quantised at inference). Where a float
+# decides an integer code, the decision is taken in float32, as the kernel takes it:
+# the quotient x / scale is a correctly rounded float32 division, then rounded to the
+# nearest integer, ties to even.
+# ---------------------------------------------------------------------------
+def _f32_quotient(x, s):
+    return (np.asarray(x, np.float32) / np.float32(s)).astype(np.float32)
+
+
+def quantize_int4_g32(x):
+    """Per group of 32: scale = fp16(amax / 7) (float32 quotient, rounded to fp16 to
+    nearest even); code = clamp(rne(x / scale), -8, 7), 0 when the scale is 0; two
+    codes per byte, element 2i in the low nibble. x float32 [..., n]. Returns (codes
+    uint8 [..., n/2], scales float16 [..., n/32])."""
+    x = np.asarray(x, np.float32)
+    *lead, n = x.shape
+    g = x.reshape(*lead, n // 32, 32)
+    amax = np.abs(g).max(axis=-1)
+    scale = (amax / np.float32(7)).astype(np.float32).astype(np.float16)
+    sf = scale.astype(np.float32)[..., None]
+    safe = np.where(sf > 0, sf, np.float32(1))
+    q = np.rint(_f32_quotient(g, 1) / safe).astype(np.float32)
+    q = np.where(sf > 0, np.clip(q, -8, 7), 0).astype(np.int64).reshape(*lead, n)
+    nib = (q & 0xF).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)), scale
+
+
+def fp4_group_exponent(amax):
+    """The smallest integer e with amax <= 6 * 2^e (exact: from the binary exponent of
+    amax), clamped to [-127, 127]; -127 for amax = 0."""
+    amax = np.asarray(amax, np.float64)
+    m, k = np.frexp(amax)                       # amax = m * 2^k, m in [0.5, 1)
+    e = np.where(m <= 0.75, k - 3, k - 2)
+    e = np.where(amax > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def e2m1_nearest(y):
+    """Code (0..7) of the E2M1 magnitude nearest to |y| <= 6, ties to the even code."""
+    a = np.abs(np.asarray(y, np.float64))
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    d = np.abs(a[..., None] - mags)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                    # one or two nearest codes
+    even = cand & (np.arange(8) % 2 == 0)
+    return np.where(even.any(-1), even.argmax(-1), cand.argmax(-1)).astype(np.int64)
+
+
+def quantize_fp4_e2m1_g32(x):
+    """Per group of 32: scale 2^e with e = fp4_group_exponent(amax); code = nearest
+    E2M1 value of x / 2^e (exact division by a power of two), ties to the even code,
+    sign bit 3 = the sign of x (a negative value that rounds to zero is -0, as in IEEE
+    rounding); E8M0 byte = e + 127. Returns (codes uint8 [..., n/2], scales uint8
+    [..., n/32])."""
+    x = np.asarray(x, np.float32)
+    *lead, n = x.shape
+    g = x.reshape(*lead, n // 32, 32).astype(np.float64)
+    e = fp4_group_exponent(np.abs(g).max(axis=-1))
+    y = g / (2.0 ** e)[..., None]
+    mag = e2m1_nearest(y)
+    code = (mag | np.where(np.signbit(y), 8, 0)).reshape(*lead, n)
+    nib = code.astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)), (e + 127).astype(np.uint8)
+
+
+def quantize_int8(x, scale):
+    """code = clamp(rne(x / scale), -127, 127) with the cache's fixed float32 scale."""
+    q = np.rint(_f32_quotient(x, scale))
+    return np.clip(q, -127, 127).astype(np.int8)
+
+
+def quantize_fp8_e4m3(x, scale):
+    """y = x / scale (float32), saturated to [-448, 448]; the magnitude goes to the
+    nearest E4M3 magnitude, ties to the even code, and the sign bit is the sign of y
+    (a negative value that rounds to zero is -0, as in IEEE rounding). Returns the
+    code bytes (uint8)."""
+    y = np.clip(_f32_quotient(x, scale).astype(np.float64), -448.0, 448.0)
+    codes = np.arange(0x7F, dtype=np.uint8)               # the finite magnitudes
+    vals = decode_fp8_e4m3(codes)
+    d = np.abs(np.abs(y)[..., None] - vals)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    pref = cand & ((codes & 1) == 0)
+    pick = np.where(pref.any(-1), pref.argmax(-1), cand.argmax(-1))
+    return (codes[pick] | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
 # Selector scoring (§2.1 score formula; §2.3 per-block maximum).
 # ---------------------------------------------------------------------------
 def select_score(sel_q, sel_w, sel_k):

@@ -195,6 +195,89 @@ def test_quantizers_roundtrip_within_format_step():
     assert (np.abs(v - xd) <= 1.0 * scale * (1 + 1e-9)).all()
 
 
+# ----------------------------------------------------------------------------- quantise-on-append
+def test_quantize_fp8_matches_torch_cast_including_ties():
+    # library routine: torch's float8_e4m3fn cast rounds to nearest, ties to even
+    vals = O.decode_fp8_e4m3(np.arange(256, dtype=np.uint8))
+    fin = np.sort(np.unique(vals[~np.isnan(vals)]))
+    mids = (fin[1:] + fin[:-1]) / 2                       # every tie between neighbours
+    rng = np.random.default_rng(1)
+    y = np.concatenate([fin, mids, rng.uniform(-448, 448, 2000),
+                        rng.uniform(-0.02, 0.02, 2000)]).astype(np.float32)
+    y = np.concatenate([y, -y, np.array([0.0, -0.0], np.float32)])
+    got = O.quantize_fp8_e4m3(y, np.float32(1.0))
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, want)               # signed zeros included
+    # saturation instead of NaN above the largest finite value
+    big = O.quantize_fp8_e4m3(np.array([500.0, -1e6], np.float32), 1.0)
+    assert list(O.decode_fp8_e4m3(big)) == [448.0, -448.0]
+
+
+def test_quantize_int8_rounding_and_clamp():
+    s = np.float32(0.5)
+    x = np.array([0.0, 0.25, 0.75, -0.25, 1.0, 63.4, 63.5, 100.0, -100.0], np.float32)
+    # quotients 0, 0.5, 1.5, -0.5, 2, 126.8, 127, 200, -200: ties to even, clamp to 127
+    np.testing.assert_array_equal(O.quantize_int8(x, s), [0, 0, 2, 0, 2, 127, 127, 127, -127])
+    k = np.arange(-127, 128)
+    np.testing.assert_array_equal(O.quantize_int8((k * 0.375).astype(np.float32), 0.375), k)
+
+
+def test_quantize_int4_roundtrip_and_recipe():
+    from block_sparse_long_spot_amd.workloads import quantize_int4_g32 as recipe
+    x = torch.randn(5, 4, 64, generator=torch.Generator().manual_seed(11))
+    c, sc = O.quantize_int4_g32(x.numpy())
+    v = O.dequant_int4_g32(c, sc)
+    step = np.repeat(sc.astype(np.float64), 32, -1)
+    assert (np.abs(v - x.double().numpy()) <= 0.5 * step * (1 + 1e-6)).all()
+    # an independent torch implementation of the same definition gives the same bytes
+    c2, s2 = recipe(x)
+    np.testing.assert_array_equal(c, c2.numpy())
+    np.testing.assert_array_equal(sc, s2.numpy())
+    # an all-zero group: scale 0, codes 0
+    cz, sz = O.quantize_int4_g32(np.zeros((1, 32), np.float32))
+    assert (cz == 0).all() and (sz == 0).all()
+
+
+def test_fp4_group_exponent_is_minimal():
+    rng = np.random.default_rng(2)
+    a = np.concatenate([rng.uniform(1e-3, 1e3, 500), 6.0 * 2.0 ** np.arange(-5, 6),
+                        4.5 * 2.0 ** np.arange(-5, 6), [0.75, 1.5, 3.0, 6.0001]])
+    e = O.fp4_group_exponent(a)
+    assert (a <= 6.0 * 2.0 ** e).all()                 # fits
+    assert (a > 6.0 * 2.0 ** (e - 1)).all()            # and one step smaller would not
+    assert O.fp4_group_exponent(0.0) == -127
+
+
+def test_e2m1_nearest_ties_to_even():
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    np.testing.assert_array_equal(O.e2m1_nearest(mids), [0, 2, 2, 4, 4, 6, 6])
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    np.testing.assert_array_equal(O.e2m1_nearest(np.array(mags)), np.arange(8))
+    np.testing.assert_array_equal(O.e2m1_nearest(np.array([0.26, 1.24, 5.01])), [1, 2, 7])
+
+
+def test_quantize_fp4_roundtrip_and_idempotence():
+    x = torch.randn(6, 128, generator=torch.Generator().manual_seed(12)).numpy()
+    c, sc = O.quantize_fp4_e2m1_g32(x)
+    v = O.dequant_fp4_e2m1_g32(c, sc)
+    scale = np.repeat(O.decode_e8m0(sc), 32, -1)
+    assert (np.abs(v - x) <= 1.0 * scale).all()           # half the widest gap (4 -> 6)
+    # re-quantising decoded values returns the same bytes when each group's largest
+    # magnitude decodes to 6 * scale
+    gmax = np.abs(v).reshape(6, 4, 32).max(-1)
+    full = np.isclose(gmax, 6 * O.decode_e8m0(sc))
+    c2, s2 = O.quantize_fp4_e2m1_g32(v.astype(np.float32))
+    assert full.any()
+    for r in range(6):
+        for gi in range(4):
+            if full[r, gi]:
+                assert s2[r, gi] == sc[r, gi]
+                np.testing.assert_array_equal(c2[r, 16 * gi:16 * gi + 16], c[r, 16 * gi:16 * gi + 16])
+    # a negative value that rounds to zero keeps its sign (-0, code 8)
+    cz, _ = O.quantize_fp4_e2m1_g32(np.array([[-0.01, 0.01] + [6.0] * 30], np.float32))
+    assert cz[0, 0] == 0x08
+
+
 def test_8bit_and_fp4_footprints_match_pages_figures():
     fig = json.load(open(GOLDEN))
     n = 1024
