@@ -298,7 +298,10 @@ def selector_formats_leg(steps, warmup, stream):
     sel_q = torch.randn(1, wl.H_idx, wl.d_idx, generator=gen, device="cuda").bfloat16()
     sel_w = torch.randn(1, wl.H_idx, generator=gen, device="cuda").abs()
     scores = torch.empty(1, wl.nb, device="cuda")
-    res = {"geometry": "L 131072, block 16, 16 keys per block, 4 x 128, batch 1, bf16 query"}
+    res = {"geometry": "L 131072, block 16, 16 keys per block, 4 x 128, batch 1, bf16 query",
+           "quantize": "spot_quantize_selector over the whole bf16 cache (131072 rows of "
+                       "512): bytes read + written per second"}
+    rows_bf16 = raw.reshape(-1, wl.H_idx * wl.d_idx).bfloat16().contiguous()
     for fmt in ("bf16", "int8", "fp8", "int4", "fp4"):
         codes, scale = W.quantize_selector(raw, fmt)
         nbytes = codes.numel() * codes.element_size() + (
@@ -309,7 +312,19 @@ def selector_formats_leg(steps, warmup, stream):
                                            stream=stream), steps, warmup, stream)
         res[fmt] = {"us": round(us, 3), "key_bytes": nbytes,
                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        if fmt != "bf16":
+            c2 = codes.view(torch.uint8).reshape(rows_bf16.shape[0], -1)
+            s2 = scale.reshape(rows_bf16.shape[0], -1) if scale.numel() > 1 else None
+            ts = scale if scale.numel() == 1 else None
+            qus, _ = time_back_to_back(
+                lambda: spot.spot_quantize_selector(rows_bf16, fmt, c2, scales=s2,
+                                                    tensor_scale=ts, stream=stream),
+                steps, warmup, stream)
+            moved = rows_bf16.numel() * 2 + nbytes
+            res[fmt]["quantize_us"] = round(qus, 3)
+            res[fmt]["quantize_GBps"] = round(moved / (qus * 1e-6) / 1e9, 1)
         del codes, scale
+    del rows_bf16
     del raw
     torch.cuda.empty_cache()
     return res

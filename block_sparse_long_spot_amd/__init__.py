@@ -6,12 +6,17 @@ see include/spot.h for the contract of each.
 from ._lib import (  # noqa: F401
     SPOT_BF16,
     SPOT_F32,
+    SPOT_FP4_E2M1_G32,
+    SPOT_FP8_E4M3,
     SPOT_INT4_G32,
+    SPOT_INT8,
     SpotError,
     load,
+    selector_format,
     spot_abi_version,
     spot_prefill_attn,
     spot_prefill_select_score,
+    spot_quantize_selector,
     spot_select_score,
     spot_select_topp,
     spot_sparse_attn,

@@ -43,6 +43,8 @@ def load() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.spot_select_score.argtypes = [vp, i, vp, vp, vp, vp, i, vp, i, i, i, i, i, vp]
     lib.spot_select_score.restype = i
+    lib.spot_quantize_selector.argtypes = [vp, i, i, i, i, vp, vp, vp, vp]
+    lib.spot_quantize_selector.restype = i
     lib.spot_select_topp.argtypes = [vp, vp, vp, vp, i, i, f, i, i, i, i, vp]
     lib.spot_select_topp.restype = i
     lib.spot_sparse_attn_workspace_bytes.argtypes = [i, i, i, i]
@@ -147,6 +149,23 @@ def spot_select_score(sel_q, sel_w, sel_k, sel_k_scale, scores, kpb: int = 1, st
                                   _ptr(sel_k), _ptr(sel_k_scale), k_fmt, _ptr(scores), B, nb,
                                   kpb, H, d_idx, _stream(stream))
     _check("spot_select_score", st)
+
+
+_FORMATS = {"int4": SPOT_INT4_G32, "fp4": SPOT_FP4_E2M1_G32, "int8": SPOT_INT8,
+            "fp8": SPOT_FP8_E4M3}
+
+
+def spot_quantize_selector(src, fmt: str, codes, scales=None, tensor_scale=None,
+                           stream=None):
+    """Encode src [n_rows][row_len] (fp32/bf16, row_len % 32 == 0) into codes (uint8
+    [n_rows][row_len/2] for "int4"/"fp4", [n_rows][row_len] int8 / float8_e4m3fn for
+    "int8"/"fp8") and, for the group formats, scales [n_rows][row_len/32] (fp16 for
+    "int4", uint8 E8M0 for "fp4"); the 8-bit formats read the cache's fp32 scale [1]."""
+    n_rows, row_len = src.shape
+    st = load().spot_quantize_selector(_ptr(src), _dtype_code(src), n_rows, row_len,
+                                       _FORMATS[fmt], _ptr(codes), _ptr(scales),
+                                       _ptr(tensor_scale), _stream(stream))
+    _check("spot_quantize_selector", st)
 
 
 def spot_select_topp(scores, sel_idx, sel_cnt, sel_mass, p: float, K_min: int, K_max: int,

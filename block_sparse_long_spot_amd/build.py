@@ -29,7 +29,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
-SOURCES = ["capi.cpp", "score.hip", "topp.hip", "attn.hip", "prefill.hip"]
+SOURCES = ["capi.cpp", "score.hip", "topp.hip", "attn.hip", "prefill.hip", "quant.hip"]
 
 
 def _compile(src: str) -> str:

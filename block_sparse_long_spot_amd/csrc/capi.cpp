@@ -114,6 +114,34 @@ int spot_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt, fl
                                            K_max, n_sink, n_rec, as_stream(stream)));
 }
 
+int spot_quantize_selector(const void* src, int src_dtype, int n_rows, int row_len, int fmt,
+                           void* codes, void* scales, const float* tensor_scale,
+                           void* stream) {
+  if (!src || !codes || n_rows <= 0 || row_len <= 0 || row_len % 32 != 0)
+    return SPOT_ERR_INVALID;
+  if (src_dtype != SPOT_F32 && src_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
+  if (!aligned(src, 16) || !aligned(codes, 16)) return SPOT_ERR_INVALID;
+  switch (fmt) {
+    case SPOT_INT4_G32:
+      if (!scales || !aligned(scales, 2) || tensor_scale) return SPOT_ERR_INVALID;
+      break;
+    case SPOT_FP4_E2M1_G32:
+      if (!scales || tensor_scale) return SPOT_ERR_INVALID;
+      break;
+    case SPOT_INT8:
+    case SPOT_FP8_E4M3:
+      if (scales || !tensor_scale || !aligned(tensor_scale, 4)) return SPOT_ERR_INVALID;
+      break;
+    default:
+      return SPOT_ERR_INVALID;
+  }
+  const long n_groups = (long)n_rows * (row_len / 32);
+  if (n_groups > 255L * 2147483647L) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_quantize_selector(src, src_dtype == SPOT_BF16, fmt, codes,
+                                                 scales, tensor_scale, n_groups,
+                                                 as_stream(stream)));
+}
+
 size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max) {
   if (B <= 0 || Hq <= 0 || d <= 0 || K_max <= 0) return 0;
   return spot::attn_workspace_bytes(B, Hq, d, K_max);

@@ -15,6 +15,10 @@ hipError_t launch_select_score(const void* sel_q, int q_fmt, const void* sel_q_s
                                int k_fmt, float* scores, int B, int nb, int kpb, int H,
                                int d_idx, hipStream_t stream);
 
+hipError_t launch_quantize_selector(const void* src, bool src_bf16, int fmt, void* codes,
+                                    void* scales, const float* tensor_scale, long n_groups,
+                                    hipStream_t stream);
+
 hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
                               float* sel_mass, int B, int nb, float p, int K_min, int K_max,
                               int n_sink, int n_rec, hipStream_t stream);

@@ -130,6 +130,38 @@ SPOT_API int spot_select_topp(const float* scores, int32_t* sel_idx, int32_t* se
                               int n_sink, int n_rec, void* stream);
 
 /*
+ * spot_quantize_selector — encode selector keys into a quantised cache format: the
+ * write side of §5.3 (the selector is trained in BF16 and its key cache quantised at
+ * inference), e.g. to append the new token's selector key to the cache (point codes
+ * and scales at its row).
+ *
+ * Rows are split into groups of 32 consecutive elements:
+ *   SPOT_INT4_G32      scale = fp16(amax / 7) (fp32 quotient, rounded to nearest even);
+ *                      code = clamp(rne(x / scale), -8, 7); all codes 0 when scale = 0.
+ *   SPOT_FP4_E2M1_G32  scale = 2^e, e the smallest integer with amax <= 6 * 2^e, clamped
+ *                      to [-127, 127] (-127 when amax = 0), stored as the byte e + 127;
+ *                      code = the E2M1 value nearest to x / 2^e, ties to the even code.
+ *   SPOT_INT8          code = clamp(rne(x / s), -127, 127) with the cache's fixed scale s.
+ *   SPOT_FP8_E4M3      y = clamp(x / s, -448, 448); code = the E4M3 value nearest to y,
+ *                      ties to the even code.
+ * x / scale is a correctly rounded fp32 division; rne rounds to nearest, ties to even;
+ * sign bits follow x (a negative value rounding to zero gives -0 in FP8 and FP4).
+ *   src           [n_rows][row_len] in src_dtype (SPOT_F32 or SPOT_BF16); 16-byte aligned.
+ *   row_len       a multiple of 32 (row_len = H_idx * d_idx for one selector key).
+ *   codes         out [n_rows][row_len / 2] (4-bit formats) or [n_rows][row_len] bytes
+ *                 (8-bit formats); 16-byte aligned.
+ *   scales        out, group formats only: [n_rows][row_len / 32] fp16 (INT4, 2-byte
+ *                 aligned) or E8M0 bytes (FP4); must be NULL for the 8-bit formats.
+ *   tensor_scale  in, 8-bit formats only: the cache's one fp32 scale s (device, 4-byte
+ *                 aligned); must be NULL for the group formats.
+ * Errors: SPOT_ERR_INVALID for a bad pointer, size or format, or a scale argument that
+ * does not match the format.
+ */
+SPOT_API int spot_quantize_selector(const void* src, int src_dtype, int n_rows, int row_len,
+                                    int fmt, void* codes, void* scales,
+                                    const float* tensor_scale, void* stream);
+
+/*
  * spot_sparse_attn_workspace_bytes — size of the workspace spot_sparse_attn needs for
  * these sizes (split-K partial results). Returns 0 for non-positive sizes.
  */

@@ -26,7 +26,7 @@ def fake(addr=0x10000):
 
 def test_exports_match_header(lib):
     declared = _lib.declared_symbols()
-    assert len(declared) == 8
+    assert len(declared) == 9
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -72,6 +72,31 @@ def test_select_score_validation(lib):
     # 16 (8-bit formats) or 32 (4-bit formats) elements per lane: 128 lanes again
     assert score(lib, H_idx=32, d_idx=64, k_dtype=INT8, sel_k_scale=fake()) == UNSUPPORTED
     assert score(lib, H_idx=64, d_idx=64, k_dtype=FP4, sel_k_scale=fake()) == UNSUPPORTED
+
+
+def quant(lib, **kw):
+    a = dict(src=fake(), src_dtype=BF16, n_rows=4, row_len=256, fmt=INT4, codes=fake(),
+             scales=fake(), tensor_scale=None, stream=None)
+    a.update(kw)
+    return lib.spot_quantize_selector(*a.values())
+
+
+def test_quantize_selector_validation(lib):
+    assert quant(lib, src=None) == INVALID
+    assert quant(lib, codes=None) == INVALID
+    assert quant(lib, n_rows=0) == INVALID
+    assert quant(lib, row_len=48) == INVALID                        # not whole groups
+    assert quant(lib, src_dtype=INT8) == INVALID
+    assert quant(lib, fmt=BF16) == INVALID                          # not a quantised format
+    assert quant(lib, src=fake(0x10008)) == INVALID
+    assert quant(lib, codes=fake(0x10004)) == INVALID
+    assert quant(lib, scales=None) == INVALID                       # INT4 writes scales
+    assert quant(lib, scales=fake(0x10001)) == INVALID              # fp16 scales misaligned
+    assert quant(lib, tensor_scale=fake()) == INVALID               # no tensor scale for INT4
+    assert quant(lib, fmt=FP4, scales=None) == INVALID
+    assert quant(lib, fmt=INT8, scales=None) == INVALID             # INT8 reads the tensor scale
+    assert quant(lib, fmt=FP8, scales=None, tensor_scale=fake(0x10002)) == INVALID
+    assert quant(lib, fmt=FP8, tensor_scale=fake()) == INVALID      # group scales given
 
 
 def topp(lib, **kw):
