@@ -408,3 +408,31 @@ def prefill_attention(Q, K, V, sels, block, sm_scale, q_pos0, heads=None):
                 den = w.sum(axis=1, keepdims=True)
                 out[b, hq] = np.where(has, (w @ Vg) / np.where(den > 0, den, 1.0), 0.0)
     return out
+
+
+def prefill_sequence(sel_q, sel_w, sel_k, Q, K, V, Tq, q_pos0, block, sm_scale, p, K_min,
+                     K_max, n_sink, n_rec):
+    """Sparse prefill of a whole sequence of T queries (positions q_pos0 .. q_pos0+T-1)
+    cut into consecutive tiles of Tq queries (the last one shorter): for each tile, the
+    tile block scores over its visible blocks (§2.1), dual top-p over them with the
+    recency window ending at the tile's diagonal (§2.3, Eq. 7-8), and causal attention
+    over the selected blocks. The three steps are the single-tile functions above,
+    applied tile after tile.
+
+    sel_q [B][T][H][d_idx], sel_w [B][T][H], sel_k [B][nb][kpb][H][d_idx] (decoded),
+    Q [B][Hq][T][d], K, V [B][Hkv][L][d]. Returns (out float64 [B][Hq][T][d], per tile:
+    the scores [B][nb_vis] and the selected sets)."""
+    Q = np.asarray(Q)
+    B, Hq, T, d = Q.shape
+    out = np.zeros((B, Hq, T, d), dtype=np.float64)
+    tiles = []
+    for q0 in range(0, T, Tq):
+        q1 = min(q0 + Tq, T)
+        sc = prefill_tile_score(np.asarray(sel_q)[:, q0:q1], np.asarray(sel_w)[:, q0:q1],
+                                sel_k, q_pos0 + q0, block)
+        sets = [select_topp_row(sc[b], p, K_min, K_max, n_sink, n_rec)[0] for b in range(B)]
+        out[:, :, q0:q1] = prefill_attention(Q[:, :, q0:q1], K, V, sets, block, sm_scale,
+                                             q_pos0 + q0)
+        tiles.append((sc, sets))
+    return out, tiles
+

@@ -559,6 +559,46 @@ def test_prefill_subset_equals_masked_sdpa():
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_prefill_sequence_all_blocks_equals_causal_sdpa():
+    # p = 1 with no cap keeps every visible block in every tile: the whole sequence is
+    # then dense causal attention (library routine: torch SDPA with is_causal)
+    g = torch.Generator().manual_seed(21)
+    B, Hq, Hkv, T, d, H, di, block, Tq = 1, 4, 2, 200, 16, 2, 8, 16, 48
+    Q = torch.randn(B, Hq, T, d, generator=g, dtype=torch.float64)
+    K = torch.randn(B, Hkv, T, d, generator=g, dtype=torch.float64)
+    V = torch.randn(B, Hkv, T, d, generator=g, dtype=torch.float64)
+    sq = torch.randn(B, T, H, di, generator=g, dtype=torch.float64).numpy()
+    sw = torch.rand(B, T, H, generator=g, dtype=torch.float64).numpy()
+    nb = -(-T // block)
+    sk = torch.randn(B, nb, 1, H, di, generator=g, dtype=torch.float64).numpy()
+    out, tiles = O.prefill_sequence(sq, sw, sk, Q.numpy(), K.numpy(), V.numpy(), Tq, 0,
+                                    block, 0.25, 1.0, 0, nb, 1, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q, K.repeat_interleave(2, 1), V.repeat_interleave(2, 1), is_causal=True, scale=0.25)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert len(tiles) == -(-T // Tq)
+    for i, (sc, sets) in enumerate(tiles):
+        assert sc.shape[1] == -(-min((i + 1) * Tq, T) // block)   # visible blocks grow
+        assert sets[0] == list(range(sc.shape[1]))
+
+
+def test_prefill_sequence_tiles_use_their_own_diagonal():
+    # with p = 0 and no floor only the reserved blocks remain: the sink and the n_rec
+    # blocks ending at each tile's last visible block
+    g = torch.Generator().manual_seed(22)
+    B, T, H, di, block, Tq = 1, 160, 2, 8, 16, 32
+    nb = T // block
+    sq = torch.randn(B, T, H, di, generator=g, dtype=torch.float64).numpy()
+    sw = torch.rand(B, T, H, generator=g, dtype=torch.float64).numpy()
+    sk = torch.randn(B, nb, 1, H, di, generator=g, dtype=torch.float64).numpy()
+    Q = np.zeros((B, 2, T, 4))
+    KV = np.zeros((B, 1, T, 4))
+    _, tiles = O.prefill_sequence(sq, sw, sk, Q, KV, KV, Tq, 0, block, 1.0, 0.0, 0, nb, 1, 2)
+    for i, (sc, sets) in enumerate(tiles):
+        nv = sc.shape[1]
+        assert sets[0] == sorted({0} | {max(nv - 2, 0), nv - 1})
+
+
 def test_prefill_tile_score_is_max_over_visible_queries():
     r = rng(17)
     B, Tq, H, di, nb, block = 1, 8, 2, 4, 6, 4
