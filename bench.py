@@ -234,6 +234,63 @@ def prefill_leg(steps, warmup, stream):
             "attn_frac_of_bf16_mfma_peak": round(flops / (t["attn"] * 1e-6) / 2.5e15, 4)}
 
 
+def prefill_sequence_leg(steps, warmup, stream):
+    """A whole 32K prefill of the c5 layer (32 query / 8 KV heads, d 128, selector 4 x
+    64, block 64) in 256 tiles of 128 queries: tile scoring, per-tile top-p (sink 1,
+    recency 4 blocks at each tile's diagonal, p 0.95) and causal sparse attention, one
+    launch each. Reports per-call µs, the attention's algorithmic TFLOP/s and the
+    fraction of dense causal attention's flops that the selection keeps."""
+    wl = W.WORKLOADS["c5_prefill_32k"]
+    B, T, Tq, d, H, di, block = 1, wl.L, wl.prefill_Tq, wl.d, wl.H_idx, wl.d_idx, wl.block
+    L, nb = wl.L, wl.nb
+    n_tiles = -(-T // Tq)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(49)
+    sel_q = torch.randn(B, T, H, di, generator=g, device="cuda").bfloat16()
+    sel_w = torch.randn(B, T, H, generator=g, device="cuda").abs()
+    sel_k = torch.randn(B, nb, 1, H, di, generator=g, device="cuda").bfloat16()
+    Q = torch.randn(B, wl.Hq, T, d, generator=g, device="cuda").bfloat16()
+    K = torch.randn(B, wl.Hkv, L, d, generator=g, device="cuda").bfloat16()
+    V = torch.randn(B, wl.Hkv, L, d, generator=g, device="cuda").bfloat16()
+    scores = torch.empty(B, n_tiles, nb, device="cuda")
+    idx = torch.empty(B, n_tiles, nb, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, n_tiles, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, wl.Hq, T, d, dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    calls = {
+        "score": lambda: spot.spot_prefill_select_score(sel_q, sel_w, sel_k, scores, 0, Tq=Tq,
+                                                        stream=stream),
+        "topp": lambda: spot.spot_prefill_select_topp(scores, idx, cnt, None, wl.p, wl.K_min,
+                                                      nb, wl.n_sink, wl.n_rec, 0, T, Tq=Tq,
+                                                      stream=stream),
+        "attn": lambda: spot.spot_prefill_attn(Q, K, V, idx, cnt, out, 0, scale, Tq=Tq,
+                                               stream=stream),
+    }
+
+    def whole():
+        for f in calls.values():
+            f()
+
+    us_total, _ = time_back_to_back(whole, steps, warmup, stream)
+    per = {k: round(time_back_to_back(f, steps, warmup, stream)[0], 3) for k, f in calls.items()}
+    whole()
+    torch.cuda.synchronize()
+    ic, cc = idx.cpu().numpy()[0], cnt.cpu().numpy()[0]
+    vis = 0
+    for t in range(n_tiles):
+        pos = np.arange(t * Tq, min((t + 1) * Tq, T))
+        for blk in ic[t, : cc[t]]:
+            lo = blk * block
+            vis += int(np.clip(np.minimum(pos + 1, lo + block) - lo, 0, None).sum())
+    flops = 4.0 * d * vis * wl.Hq
+    dense = 4.0 * d * wl.Hq * T * (T + 1) / 2
+    return {"T": T, "tiles": n_tiles, "us_total": round(us_total, 3), "per_call_us": per,
+            "selected_blocks_mean": round(float(cc.mean()), 2),
+            "attn_flops": flops, "dense_causal_flops": dense,
+            "flop_fraction_of_dense": round(flops / dense, 5),
+            "attn_TFLOPs": round(flops / (per["attn"] * 1e-6) / 1e12, 2)}
+
+
 def static_topk_leg(inp, wl, steps, warmup, stream):
     """Static top-K (Eq. 6) with K = half the blocks, no reserved blocks: the paper's
     K = 0.5L decode rows (Table 1), on the same 128K batch-8 inputs. Four times the
@@ -538,6 +595,8 @@ def main():
     if a.prefill:
         log("bench: prefill tile")
         result["prefill"] = prefill_leg(max(10, a.steps // 4), 5, stream)
+        log("bench: whole-sequence sparse prefill")
+        result["prefill_sequence"] = prefill_sequence_leg(max(5, a.steps // 50), 3, stream)
     if a.page_geometry:
         log("bench: selector at the paper's page geometry")
         result["page_geometry"] = page_geometry_step(max(10, a.steps // 4), 20, stream)

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     spot_abi_version,
     spot_prefill_attn,
     spot_prefill_select_score,
+    spot_prefill_select_topp,
     spot_quantize_selector,
     spot_select_score,
     spot_select_topp,

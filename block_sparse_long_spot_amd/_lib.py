@@ -53,10 +53,12 @@ def load() -> ctypes.CDLL:
                                      vp]
     lib.spot_sparse_attn.restype = i
     lib.spot_prefill_select_score.argtypes = [vp, i, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i,
-                                              vp]
+                                              i, vp]
     lib.spot_prefill_select_score.restype = i
-    lib.spot_prefill_attn.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, i, i, f,
-                                      vp]
+    lib.spot_prefill_select_topp.argtypes = [vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.spot_prefill_select_topp.restype = i
+    lib.spot_prefill_attn.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, i, i, i,
+                                      f, vp]
     lib.spot_prefill_attn.restype = i
     lib.spot_status_string.argtypes = [i]
     lib.spot_status_string.restype = ctypes.c_char_p
@@ -196,27 +198,57 @@ def spot_sparse_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, workspace, sm_s
     _check("spot_sparse_attn", st)
 
 
+def _tiles(T: int, Tq) -> tuple:
+    Tq = T if Tq is None else int(Tq)
+    return Tq, -(-T // Tq)
+
+
 def spot_prefill_select_score(sel_q, sel_w, sel_k, scores, q_pos0: int, block: int = 64,
-                              kpb: int = 1, stream=None):
-    """scores[B][nb_vis] <- tile block scores of the Tq queries at q_pos0.."""
-    B, Tq, H, d_idx = sel_q.shape
+                              kpb: int = 1, Tq: Optional[int] = None, stream=None):
+    """scores[B][n_tiles][nb_seq] (or [B][nb_seq] for one tile) <- tile block scores of
+    the T queries of sel_q [B][T][H][d_idx] at positions q_pos0.., in tiles of Tq
+    (default: one tile of T)."""
+    B, T, H, d_idx = sel_q.shape
+    Tq, n_tiles = _tiles(T, Tq)
     nb_cache = sel_k.shape[1]
+    nb_seq = -(-(q_pos0 + T) // block)
+    assert scores.numel() == B * n_tiles * nb_seq and scores.dtype == torch.float32
     st = load().spot_prefill_select_score(_ptr(sel_q), _dtype_code(sel_q), _ptr(sel_w),
                                           _ptr(sel_k), None, _dtype_code(sel_k), _ptr(scores), B,
-                                          Tq, q_pos0, nb_cache, kpb, H, d_idx, block,
+                                          T, Tq, q_pos0, nb_cache, kpb, H, d_idx, block,
                                           _stream(stream))
     _check("spot_prefill_select_score", st)
 
 
+def spot_prefill_select_topp(scores, sel_idx, sel_cnt, sel_mass, p: float, K_min: int,
+                             K_max: int, n_sink: int, n_rec: int, q_pos0: int, T: int,
+                             Tq: Optional[int] = None, block: int = 64, stream=None):
+    """Per-tile dual top-p: sel_idx [B][n_tiles][K_max], sel_cnt [B][n_tiles]; each tile
+    sees its own visible blocks, recency ending at its diagonal."""
+    B = scores.shape[0]
+    Tq, n_tiles = _tiles(T, Tq)
+    nb_seq = -(-(q_pos0 + T) // block)
+    assert scores.numel() == B * n_tiles * nb_seq
+    assert sel_idx.dtype == torch.int32 and sel_idx.numel() == B * n_tiles * K_max
+    assert sel_cnt.dtype == torch.int32 and sel_cnt.numel() == B * n_tiles
+    st = load().spot_prefill_select_topp(_ptr(scores), _ptr(sel_idx), _ptr(sel_cnt),
+                                         _ptr(sel_mass), B, T, Tq, q_pos0, block, float(p),
+                                         K_min, K_max, n_sink, n_rec, _stream(stream))
+    _check("spot_prefill_select_topp", st)
+
+
 def spot_prefill_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, q_pos0: int,
-                      sm_scale: float, block: int = 64, stream=None):
-    """out[B][Hq][Tq][d] <- causal attention of the tile over the selected blocks."""
-    B, Hq, Tq, d = q.shape
+                      sm_scale: float, block: int = 64, Tq: Optional[int] = None, stream=None):
+    """out[B][Hq][T][d] <- causal attention of every tile over its selected blocks
+    (sel_idx [B][n_tiles][K_max] or [B][K_max] for one tile)."""
+    B, Hq, T, d = q.shape
+    Tq, n_tiles = _tiles(T, Tq)
     Hkv, L = k_cache.shape[1], k_cache.shape[2]
-    K_max = sel_idx.shape[1]
+    K_max = sel_idx.shape[-1]
+    assert sel_idx.numel() == B * n_tiles * K_max and sel_cnt.numel() == B * n_tiles
     st = load().spot_prefill_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
                                   _ptr(sel_idx), _ptr(sel_cnt), K_max, _ptr(out), B, Hq, Hkv,
-                                  Tq, q_pos0, d, L, block, float(sm_scale), _stream(stream))
+                                  T, Tq, q_pos0, d, L, block, float(sm_scale), _stream(stream))
     _check("spot_prefill_attn", st)
 
 

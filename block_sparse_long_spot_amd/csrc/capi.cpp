@@ -174,43 +174,71 @@ int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, in
 
 int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,
                               const void* sel_k, const void* sel_k_scale, int k_dtype,
-                              float* scores, int B, int Tq, int q_pos0, int nb_cache, int kpb,
-                              int H_idx, int d_idx, int block, void* stream) {
-  if (B <= 0 || Tq <= 0 || q_pos0 < 0 || nb_cache <= 0 || block <= 0) return SPOT_ERR_INVALID;
+                              float* scores, int B, int T, int Tq, int q_pos0, int nb_cache,
+                              int kpb, int H_idx, int d_idx, int block, void* stream) {
+  if (B <= 0 || T <= 0 || Tq <= 0 || q_pos0 < 0 || nb_cache <= 0 || block <= 0)
+    return SPOT_ERR_INVALID;
   if (!scores || !aligned(scores, 4)) return SPOT_ERR_INVALID;
   const int c = check_selector(sel_q, q_dtype, nullptr, sel_w, sel_k, sel_k_scale, k_dtype,
                                H_idx, d_idx, kpb);
   if (c != SPOT_OK) return c;
-  const long nb_vis = ((long)q_pos0 + Tq + block - 1) / block;
-  if (nb_vis > nb_cache) return SPOT_ERR_INVALID;
+  const long nb_seq = ((long)q_pos0 + T + block - 1) / block;
+  if (nb_seq > nb_cache) return SPOT_ERR_INVALID;
   if (q_dtype != SPOT_BF16 || k_dtype != SPOT_BF16) return SPOT_ERR_UNSUPPORTED;
-  if (Tq > 128 || B > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
-  return from_hip(spot::launch_prefill_select_score(sel_q, sel_w, sel_k, scores, B, Tq, q_pos0,
-                                                    nb_cache, (int)nb_vis, kpb, H_idx, d_idx,
-                                                    block, as_stream(stream)));
+  const long rows = (long)B * ((T + Tq - 1) / Tq);
+  if (Tq > 128 || rows > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_prefill_select_score(sel_q, sel_w, sel_k, scores, B, T, Tq,
+                                                    q_pos0, nb_cache, (int)nb_seq, kpb, H_idx,
+                                                    d_idx, block, as_stream(stream)));
+}
+
+int spot_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                             float* sel_mass, int B, int T, int Tq, int q_pos0, int block,
+                             float p, int K_min, int K_max, int n_sink, int n_rec,
+                             void* stream) {
+  if (!scores || !sel_idx || !sel_cnt) return SPOT_ERR_INVALID;
+  if (!aligned(scores, 4) || !aligned(sel_idx, 4) || !aligned(sel_cnt, 4) ||
+      (sel_mass && !aligned(sel_mass, 4)))
+    return SPOT_ERR_INVALID;
+  if (B <= 0 || T <= 0 || Tq <= 0 || q_pos0 < 0 || block <= 0 || K_max <= 0)
+    return SPOT_ERR_INVALID;
+  if (!isfinite(p) || n_sink < 0 || n_rec < 0 || K_min < 0) return SPOT_ERR_INVALID;
+  const long nb_seq = ((long)q_pos0 + T + block - 1) / block;
+  if (nb_seq > 16384) return SPOT_ERR_UNSUPPORTED;
+  const int nb = (int)nb_seq;
+  const int rs = n_sink < nb ? n_sink : nb;
+  const int rr = n_rec < nb ? n_rec : nb;
+  const int r = rs + rr < nb ? rs + rr : nb;  // the largest reserved set of any tile
+  if (K_max < r) return SPOT_ERR_INVALID;
+  const long rows = (long)B * ((T + Tq - 1) / Tq);
+  if (rows > 2147483647L / 2) return SPOT_ERR_UNSUPPORTED;
+  return from_hip(spot::launch_prefill_select_topp(scores, sel_idx, sel_cnt, sel_mass, B, T, Tq,
+                                                   q_pos0, block, nb, p, K_min, K_max, n_sink,
+                                                   n_rec, as_stream(stream)));
 }
 
 int spot_prefill_attn(const void* q, const void* k_cache, const void* v_cache, int kv_dtype,
                       const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, void* out,
-                      int B, int Hq, int Hkv, int Tq, int q_pos0, int d, int L, int block,
-                      float sm_scale, void* stream) {
+                      int B, int Hq, int Hkv, int T, int Tq, int q_pos0, int d, int L,
+                      int block, float sm_scale, void* stream) {
   if (!q || !k_cache || !v_cache || !sel_idx || !sel_cnt || !out) return SPOT_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(sel_idx, 4) || !aligned(sel_cnt, 4))
     return SPOT_ERR_INVALID;
   if (kv_dtype != SPOT_F32 && kv_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || q_pos0 < 0 || d <= 0 || L <= 0 ||
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || Tq <= 0 || q_pos0 < 0 || d <= 0 || L <= 0 ||
       block <= 0 || K_max <= 0)
     return SPOT_ERR_INVALID;
   if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
-  if ((long)q_pos0 + Tq > L) return SPOT_ERR_INVALID;
+  if ((long)q_pos0 + T > L) return SPOT_ERR_INVALID;
   const int G = Hq / Hkv;
   if (kv_dtype != SPOT_BF16 || d != 128 || block != 64 || Tq > 128 || K_max > 8192)
     return SPOT_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
-  if (B > kMaxGrid || Hq > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
+  const long rows = (long)B * ((T + Tq - 1) / Tq);
+  if (rows > kMaxGrid || Hkv > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
   return from_hip(spot::launch_prefill_attn(q, k_cache, v_cache, sel_idx, sel_cnt, K_max, out, B,
-                                            Hq, Hkv, Tq, q_pos0, d, L, sm_scale,
+                                            Hq, Hkv, T, Tq, q_pos0, d, L, sm_scale,
                                             as_stream(stream)));
 }
 

@@ -1,4 +1,7 @@
-// Prefill-tile variant: tile block scoring and causal block-sparse attention.
+// Prefill variant: tile block scoring and causal block-sparse attention, for one tile
+// or a whole sequence cut into tiles. A launch covers B x n_tiles rows; row (b, t) is
+// the tile of queries [t*Tq, min((t+1)*Tq, T)) of sequence b, at positions starting at
+// q_pos0 + t*Tq, seeing the blocks whose first token is at or before its last query.
 //
 // Tile scoring (SpotAttention §2.1: one score per query-block x key-block tile, so
 // selection runs as a tensor-core matmul; §2.3 per-block maximum). For every selector
@@ -42,23 +45,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // tiles of 16 queries and combine their column maxima through LDS. Per selector key,
 // a wave holds the key operands of every head in registers and issues the query
 // operands of a row tile together, so the MFMAs wait on one round of loads.
+// The tile of launch row r: sequence b, first query row qs, Tq_t queries, first
+// position pos0 and nb_vis visible blocks.
+struct TileRow {
+  int b, qs, Tq_t, pos0, nb_vis;
+};
+__device__ __forceinline__ TileRow tile_row(int r, int n_tiles, int T, int Tq, int q_pos0,
+                                            int block, int nb_stride) {
+  TileRow tr;
+  tr.b = r / n_tiles;
+  tr.qs = (r % n_tiles) * Tq;
+  tr.Tq_t = min(Tq, T - tr.qs);
+  tr.pos0 = q_pos0 + tr.qs;
+  tr.nb_vis = min(nb_stride, (tr.pos0 + tr.Tq_t + block - 1) / block);
+  return tr;
+}
+
 template <int DIDX, int H>
 __global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
-    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int Tq, int q_pos0,
-    int nb_cache, int nb_vis, int kpb, int block) {
+    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int T, int Tq,
+    int n_tiles, int q_pos0, int nb_cache, int nb_stride, int kpb, int block) {
   constexpr int KS = DIDX / 32;
   constexpr int NWV = 4;
   __shared__ float colmax[NWV][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
-  const int b = blockIdx.y;
+  const TileRow tr = tile_row(blockIdx.y, n_tiles, T, Tq, q_pos0, block, nb_stride);
+  const int b = tr.b, Tq_t = tr.Tq_t, pos0 = tr.pos0, nb_vis = tr.nb_vis;
   const int blk0 = blockIdx.x * 16;
+  if (blk0 >= nb_vis) return;                      // no visible block here (uniform)
   const int blk = blk0 + col;                      // B-operand column of this lane
   const int blk_c = min(blk, nb_vis - 1);
-  const int n_rt = (Tq + 15) / 16;
-  const uint16_t* qb = sel_q + (size_t)b * Tq * H * DIDX;
-  const float* wb = sel_w + (size_t)b * Tq * H;
+  const int n_rt = (Tq_t + 15) / 16;
+  const uint16_t* qb = sel_q + ((size_t)b * T + tr.qs) * H * DIDX;
+  const float* wb = sel_w + ((size_t)b * T + tr.qs) * H;
   float best = -INFINITY;  // max over (visible query, key j) for column blk0 + col
   for (int j = 0; j < kpb; ++j) {
     bf16x8_t kop[H][KS];
@@ -70,7 +91,7 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       for (int s = 0; s < KS; ++s) kop[h][s] = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
     }
     for (int rt = wave; rt < n_rt; rt += NWV) {
-      const int qr = min(rt * 16 + col, Tq - 1);   // A-operand row of this lane
+      const int qr = min(rt * 16 + col, Tq_t - 1);   // A-operand row of this lane
       bf16x8_t qop[H][KS];
       float wq[H][4];
 #pragma unroll
@@ -79,7 +100,8 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 #pragma unroll
         for (int s = 0; s < KS; ++s) qop[h][s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wq[h][r] = wb[(size_t)min(rt * 16 + kg * 4 + r, Tq - 1) * H + h];
+        for (int r = 0; r < 4; ++r)
+          wq[h][r] = wb[(size_t)min(rt * 16 + kg * 4 + r, Tq_t - 1) * H + h];
       }
       floatx4_t tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -95,7 +117,7 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = rt * 16 + kg * 4 + r;
-        const bool vis = qi < Tq && (long)blk * block <= (long)q_pos0 + qi;
+        const bool vis = qi < Tq_t && (long)blk * block <= (long)pos0 + qi;
         if (vis) best = fmaxf(best, tot[r]);
       }
     }
@@ -109,7 +131,7 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     float m = colmax[0][col];
 #pragma unroll
     for (int w = 1; w < NWV; ++w) m = fmaxf(m, colmax[w][col]);
-    scores[(size_t)b * nb_vis + blk] = m;
+    scores[(size_t)blockIdx.y * nb_stride + blk] = m;
   }
 }
 
@@ -117,17 +139,19 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 template <int DIDX>
 __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
     const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
-    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int Tq, int q_pos0,
-    int nb_cache, int nb_vis, int kpb, int H, int block) {
+    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int T, int Tq,
+    int n_tiles, int q_pos0, int nb_cache, int nb_stride, int kpb, int H, int block) {
   constexpr int KS = DIDX / 32;
   const int lane = threadIdx.x;
   const int col = lane & 15, kg = lane >> 4;
-  const int b = blockIdx.y;
+  const TileRow tr = tile_row(blockIdx.y, n_tiles, T, Tq, q_pos0, block, nb_stride);
+  const int b = tr.b, Tq_t = tr.Tq_t, pos0 = tr.pos0, nb_vis = tr.nb_vis;
+  if (blockIdx.x * 16 >= nb_vis) return;
   const int blk = blockIdx.x * 16 + col;
   const int blk_c = min(blk, nb_vis - 1);
-  const int n_rt = (Tq + 15) / 16;
-  const uint16_t* qb = sel_q + (size_t)b * Tq * H * DIDX;
-  const float* wb = sel_w + (size_t)b * Tq * H;
+  const int n_rt = (Tq_t + 15) / 16;
+  const uint16_t* qb = sel_q + ((size_t)b * T + tr.qs) * H * DIDX;
+  const float* wb = sel_w + ((size_t)b * T + tr.qs) * H;
   float best = -INFINITY;
   for (int j = 0; j < kpb; ++j) {
     for (int rt = 0; rt < n_rt; ++rt) {
@@ -135,7 +159,7 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
       for (int h = 0; h < H; ++h) {
         const uint16_t* kp =
             sel_k + ((((size_t)b * nb_cache + blk_c) * kpb + j) * H + h) * DIDX + kg * 8;
-        const int qr = min(rt * 16 + col, Tq - 1);
+        const int qr = min(rt * 16 + col, Tq_t - 1);
         const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
         floatx4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -145,21 +169,21 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
               *reinterpret_cast<const bf16x8_t*>(kp + s * 32), c, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int qi = min(rt * 16 + kg * 4 + r, Tq - 1);
+          const int qi = min(rt * 16 + kg * 4 + r, Tq_t - 1);
           tot[r] += wb[(size_t)qi * H + h] * fmaxf(c[r], 0.f);
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = rt * 16 + kg * 4 + r;
-        const bool vis = qi < Tq && (long)blk * block <= (long)q_pos0 + qi;
+        const bool vis = qi < Tq_t && (long)blk * block <= (long)pos0 + qi;
         if (vis) best = fmaxf(best, tot[r]);
       }
     }
   }
   best = fmaxf(best, shfl_xor_f(best, 16));
   best = fmaxf(best, shfl_xor_f(best, 32));
-  if (kg == 0 && blk < nb_vis) scores[(size_t)b * nb_vis + blk] = best;
+  if (kg == 0 && blk < nb_vis) scores[(size_t)blockIdx.y * nb_stride + blk] = best;
 }
 
 // ---------------------------------------------------------------- attention
@@ -171,26 +195,30 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, uint16_t* __restrict__ out, int Hq,
-    int Hkv, int Tq, int q_pos0, int L, float qscale) {
+    int Hkv, int T, int Tq, int n_tiles, int q_pos0, int L, float qscale) {
   constexpr int D = 128;
   constexpr int NT = G * 64;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kKPad];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kBlk * kKPad];
   __shared__ int32_t sel_s[kMaxPrefillList];
 
-  const int rt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int rt = blockIdx.x, g = blockIdx.y, trow = blockIdx.z;
+  const int b = trow / n_tiles, qs = (trow % n_tiles) * Tq;
+  const int Tq_t = min(Tq, T - qs);                 // queries of this tile
+  const int q0 = rt * 16;
+  if (q0 >= Tq_t) return;                           // past a short last tile (uniform)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = g * G + wave;
   const int row = lane & 15, kg = lane >> 4;
-  const int q0 = rt * 16;
   const int my_q = q0 + row;                // query row this lane's softmax state tracks
-  const int my_pos = q_pos0 + my_q;
+  const int pos0 = q_pos0 + qs;
+  const int my_pos = pos0 + my_q;
 
   // B operand of S' = K.Q^T: column = query row, k = head dim
   bf16x8_t qb[4];
   {
     const uint16_t* qp =
-        Q + (((size_t)b * Hq + hq) * Tq + min(my_q, Tq - 1)) * D + kg * 8;
+        Q + (((size_t)b * Hq + hq) * T + qs + min(my_q, Tq_t - 1)) * D + kg * 8;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
   }
@@ -199,14 +227,14 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int cnt = min(max(sel_cnt[b], 0), K_max);
+  const int cnt = min(max(sel_cnt[trow], 0), K_max);
   const int nbl = (L + kBlk - 1) / kBlk;
-  const int last_pos = q_pos0 + min(q0 + 15, Tq - 1);  // furthest query of the tile
+  const int last_pos = pos0 + min(q0 + 15, Tq_t - 1);  // furthest query of the row tile
   const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
   const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
 
   // the selected list, staged once in LDS (it is read block after block below)
-  for (int i = tid; i < cnt; i += NT) sel_s[i] = sel_idx[(size_t)b * K_max + i];
+  for (int i = tid; i < cnt; i += NT) sel_s[i] = sel_idx[(size_t)trow * K_max + i];
   __syncthreads();
   // next list entry at or after j whose block exists and is not after the whole tile
   auto next_block = [&](int j, int& blk) {
@@ -333,8 +361,8 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
   for (int r = 0; r < 4; ++r) {
     const float lr = __shfl(l, kg * 4 + r, 64);
     const int qi = q0 + kg * 4 + r;
-    if (qi < Tq) {
-      uint16_t* op = out + (((size_t)b * Hq + hq) * Tq + qi) * D;
+    if (qi < Tq_t) {
+      uint16_t* op = out + (((size_t)b * Hq + hq) * T + qs + qi) * D;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         op[dt * 16 + row] = f_to_bf16_rne(lr > 0.f ? o[dt][r] / lr : 0.f);
@@ -345,18 +373,19 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
 }  // namespace
 
 hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
-                                       const void* sel_k, float* scores, int B, int Tq,
-                                       int q_pos0, int nb_cache, int nb_vis, int kpb, int H,
+                                       const void* sel_k, float* scores, int B, int T, int Tq,
+                                       int q_pos0, int nb_cache, int nb_stride, int kpb, int H,
                                        int d_idx, int block, hipStream_t stream) {
-  dim3 grid((nb_vis + 15) / 16, B);
+  const int n_tiles = (T + Tq - 1) / Tq;
+  dim3 grid((nb_stride + 15) / 16, B * n_tiles);
   const uint16_t* q = static_cast<const uint16_t*>(sel_q);
   const uint16_t* k = static_cast<const uint16_t*>(sel_k);
 #define SPOT_PS4(DI)                                                                         \
   hipLaunchKernelGGL((prefill_score_kernel<DI, 4>), grid, dim3(256), 0, stream, q, sel_w, k, \
-                     scores, Tq, q_pos0, nb_cache, nb_vis, kpb, block)
+                     scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, block)
 #define SPOT_PSA(DI)                                                                       \
   hipLaunchKernelGGL((prefill_score_kernel_anyh<DI>), grid, dim3(64), 0, stream, q, sel_w, \
-                     k, scores, Tq, q_pos0, nb_cache, nb_vis, kpb, H, block)
+                     k, scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, H, block)
   if (H == 4) {
     switch (d_idx) {
       case 32: SPOT_PS4(32); break;
@@ -377,11 +406,12 @@ hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
 
 hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* sel_idx, const int32_t* sel_cnt, int K_max,
-                               void* out, int B, int Hq, int Hkv, int Tq, int q_pos0, int d,
-                               int L, float sm_scale, hipStream_t stream) {
+                               void* out, int B, int Hq, int Hkv, int T, int Tq, int q_pos0,
+                               int d, int L, float sm_scale, hipStream_t stream) {
   (void)d;
   const int G = Hq / Hkv;
-  dim3 grid((Tq + 15) / 16, Hkv, B);
+  const int n_tiles = (T + Tq - 1) / Tq;
+  dim3 grid((Tq + 15) / 16, Hkv, B * n_tiles);
   const float qscale = sm_scale * kLog2e;
   const uint16_t* Qp = static_cast<const uint16_t*>(q);
   const uint16_t* Kp = static_cast<const uint16_t*>(k_cache);
@@ -389,7 +419,7 @@ hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v
   uint16_t* Op = static_cast<uint16_t*>(out);
 #define SPOT_PF(GG)                                                                         \
   hipLaunchKernelGGL(prefill_attn_kernel<GG>, grid, dim3(GG * 64), 0, stream, Qp, Kp, Vp, \
-                     sel_idx, sel_cnt, K_max, Op, Hq, Hkv, Tq, q_pos0, L, qscale)
+                     sel_idx, sel_cnt, K_max, Op, Hq, Hkv, T, Tq, n_tiles, q_pos0, L, qscale)
   switch (G) {
     case 1: SPOT_PF(1); break;
     case 2: SPOT_PF(2); break;

@@ -19,6 +19,11 @@ hipError_t launch_quantize_selector(const void* src, bool src_bf16, int fmt, voi
                                     void* scales, const float* tensor_scale, long n_groups,
                                     hipStream_t stream);
 
+hipError_t launch_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                                      float* sel_mass, int B, int T, int Tq, int q_pos0,
+                                      int block, int nb_stride, float p, int K_min, int K_max,
+                                      int n_sink, int n_rec, hipStream_t stream);
+
 hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
                               float* sel_mass, int B, int nb, float p, int K_min, int K_max,
                               int n_sink, int n_rec, hipStream_t stream);
@@ -37,14 +42,16 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
                               int K_max, void* out, void* workspace, int B, int Hq, int Hkv,
                               int d, int L, int block, float sm_scale, hipStream_t stream);
 
+// Prefill: a sequence of T query rows per batch element, cut into tiles of Tq rows
+// (T == Tq: one tile); score rows are [B][n_tiles][nb_stride].
 hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
-                                       const void* sel_k, float* scores, int B, int Tq,
-                                       int q_pos0, int nb_cache, int nb_vis, int kpb, int H,
+                                       const void* sel_k, float* scores, int B, int T, int Tq,
+                                       int q_pos0, int nb_cache, int nb_stride, int kpb, int H,
                                        int d_idx, int block, hipStream_t stream);
 
 hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* sel_idx, const int32_t* sel_cnt, int K_max,
-                               void* out, int B, int Hq, int Hkv, int Tq, int q_pos0, int d,
-                               int L, float sm_scale, hipStream_t stream);
+                               void* out, int B, int Hq, int Hkv, int T, int Tq, int q_pos0,
+                               int d, int L, float sm_scale, hipStream_t stream);
 
 }  // namespace spot

@@ -207,19 +207,33 @@ __device__ __forceinline__ u64 fixed_mass(float s, float mx) {
   return static_cast<u64>(__float2ll_rn(v));
 }
 
+// Rows of prefill tiles (n_tiles > 0): row b is tile b % n_tiles of a sequence of T
+// queries cut into tiles of Tq starting at position q_pos0; it sees the first
+// ceil((q_pos0 + last query of the tile + 1) / block) blocks of its score row, so its
+// recency window ends at the tile's diagonal. n_tiles == 0: every row has nb blocks.
+struct RowGeom {
+  int n_tiles, T, Tq, q_pos0, block;
+};
+
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict__ scores,
                                                          int32_t* __restrict__ sel_idx,
                                                          int32_t* __restrict__ sel_cnt,
-                                                         float* __restrict__ sel_mass, int nb,
-                                                         float p, int K_min, int K_max,
-                                                         int n_sink, int n_rec) {
+                                                         float* __restrict__ sel_mass,
+                                                         int nb_stride, float p, int K_min,
+                                                         int K_max, int n_sink, int n_rec,
+                                                         RowGeom geom) {
   constexpr int BPT = kCoarseBins / NT;
   constexpr int NW = NT / 64;
   __shared__ ToppSmem<NT> sh;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* row = scores + (size_t)b * nb;
+  const float* row = scores + (size_t)b * nb_stride;
+  int nb = nb_stride;  // blocks of this row
+  if (geom.n_tiles > 0) {
+    const int q_end = min((b % geom.n_tiles + 1) * geom.Tq, geom.T);  // past the tile
+    nb = min(nb_stride, (geom.q_pos0 + q_end + geom.block - 1) / geom.block);
+  }
   const int rs = min(n_sink, nb), rr = min(n_rec, nb);
   const int r = min(nb, rs + rr);
   const int n_res = nb - r;
@@ -232,7 +246,8 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   float s[EPT];
   uint32_t key[EPT];
   bool valid[EPT], res[EPT];
-  if ((nb & 3) == 0 && (EPT & 3) == 0) {
+  if ((nb_stride & 3) == 0 && (EPT & 3) == 0) {
+    // whole float4s of the row (nb_stride % 4 == 0 keeps them inside it)
 #pragma unroll
     for (int e = 0; e < EPT; e += 4) {
       const int i = tid * EPT + e;
@@ -519,20 +534,18 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
 template <int NT, int EPT>
 hipError_t launch_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
                        float* sel_mass, int B, int nb, float p, int K_min, int K_max,
-                       int n_sink, int n_rec, hipStream_t stream) {
+                       int n_sink, int n_rec, RowGeom geom, hipStream_t stream) {
   hipLaunchKernelGGL((select_topp_kernel<NT, EPT>), dim3(B), dim3(NT), 0, stream, scores,
-                     sel_idx, sel_cnt, sel_mass, nb, p, K_min, K_max, n_sink, n_rec);
+                     sel_idx, sel_cnt, sel_mass, nb, p, K_min, K_max, n_sink, n_rec, geom);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
-                              float* sel_mass, int B, int nb, float p, int K_min, int K_max,
-                              int n_sink, int n_rec, hipStream_t stream) {
+hipError_t launch_rows(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                       float* sel_mass, int B, int nb, float p, int K_min, int K_max,
+                       int n_sink, int n_rec, RowGeom geom, hipStream_t stream) {
 #define SPOT_TOPP(NT, EPT)                                                                  \
   return launch_topp<NT, EPT>(scores, sel_idx, sel_cnt, sel_mass, B, nb, p, K_min, K_max, \
-                              n_sink, n_rec, stream)
+                              n_sink, n_rec, geom, stream)
   // few blocks per thread keeps each thread's serial chain short (measured at nb 2048:
   // 512 x 4 = 6.3 us, 256 x 8 = 8.3 us, 1024 x 2 = 6.6 us)
   if (nb <= 256) SPOT_TOPP(256, 1);
@@ -543,6 +556,24 @@ hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* se
   if (nb <= 8192) SPOT_TOPP(1024, 8);
   SPOT_TOPP(1024, 16);
 #undef SPOT_TOPP
+}
+
+}  // namespace
+
+hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                              float* sel_mass, int B, int nb, float p, int K_min, int K_max,
+                              int n_sink, int n_rec, hipStream_t stream) {
+  return launch_rows(scores, sel_idx, sel_cnt, sel_mass, B, nb, p, K_min, K_max, n_sink,
+                     n_rec, RowGeom{0, 0, 0, 0, 0}, stream);
+}
+
+hipError_t launch_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                                      float* sel_mass, int B, int T, int Tq, int q_pos0,
+                                      int block, int nb_stride, float p, int K_min, int K_max,
+                                      int n_sink, int n_rec, hipStream_t stream) {
+  const int n_tiles = (T + Tq - 1) / Tq;
+  return launch_rows(scores, sel_idx, sel_cnt, sel_mass, B * n_tiles, nb_stride, p, K_min,
+                     K_max, n_sink, n_rec, RowGeom{n_tiles, T, Tq, q_pos0, block}, stream);
 }
 
 }  // namespace spot

@@ -9,9 +9,10 @@
  *   spot_select_score  -> a score for every past KV block      (§2.1, §2.3)
  *   spot_select_topp   -> the per-query block set S_q           (§2.3, Eq. 7-8)
  *   spot_sparse_attn   -> exact softmax attention over S_q      (§2.3)
- * plus a prefill-tile variant (spot_prefill_select_score, spot_prefill_attn) for a
- * tile of consecutive queries with a causal mask (§2.1 tile scoring; §6 notes the
- * selector runs in the prefill regime).
+ * plus a prefill variant (spot_prefill_select_score, spot_prefill_select_topp,
+ * spot_prefill_attn) for one tile or a whole sequence of query tiles with a causal
+ * mask (§2.1 tile scoring; §6 notes the selector runs in the prefill regime), and
+ * spot_quantize_selector, which encodes new selector keys into a quantised cache.
  *
  * Conventions shared by every call:
  *  - Every pointer argument is DEVICE memory owned by the caller (allocated and freed
@@ -196,41 +197,65 @@ SPOT_API int spot_sparse_attn(const void* q, const void* k_cache, const void* v_
                               float sm_scale, void* stream);
 
 /*
- * spot_prefill_select_score — tile block scores for a prefill tile (§2.1: one score
- * per query-block x key-block tile; §2.3 block maximum).
- *
- * The tile holds Tq consecutive queries at positions q_pos0 .. q_pos0+Tq-1. Block blk
- * is visible to query i when blk*block <= q_pos0 + i. With nb_vis =
- * ceil((q_pos0+Tq)/block):
- *   scores[b][blk] = max over the tile's queries i that see blk of
- *                    max_{j<kpb} sum_h sel_w[b][i][h] * ReLU(sel_q[b][i][h] . sel_k[b][blk][j][h])
- * for blk < nb_vis. Computed as one matrix product per selector head on the MFMA units.
- *   sel_q   [B][Tq][H_idx][d_idx] (q_dtype), sel_w fp32 [B][Tq][H_idx];
+ * Prefill (§2.1 tile scoring; §6 names sparse prefill as the open direction). A batch
+ * element holds T consecutive queries at positions q_pos0 .. q_pos0+T-1, cut into
+ * tiles of Tq queries (the last one shorter): n_tiles = ceil(T / Tq). Tile t holds
+ * queries t*Tq .. min((t+1)*Tq, T)-1 and sees the blocks whose first token is at or
+ * before its last query's position: nb_t = ceil((q_pos0 + min((t+1)*Tq, T)) / block).
+ * T == Tq is a single tile. Per-tile arrays are [B][n_tiles][..].
+ */
+
+/*
+ * spot_prefill_select_score — tile block scores (§2.1: one score per query-block x
+ * key-block tile; §2.3 block maximum). For tile t of batch element b and blk < nb_t:
+ *   scores[b][t][blk] = max over the tile's queries i that see blk (blk*block <=
+ *                       position of i) of max_{j<kpb} sum_h sel_w[b][i][h] *
+ *                       ReLU(sel_q[b][i][h] . sel_k[b][blk][j][h])
+ * Entries blk >= nb_t of a row are not written. Computed as one matrix product per
+ * selector head on the MFMA units.
+ *   sel_q   [B][T][H_idx][d_idx] (q_dtype), sel_w fp32 [B][T][H_idx];
  *   sel_k   [B][nb_cache][kpb][H_idx][d_idx] (16-byte aligned), sel_k_scale must be
  *           NULL;
- *   scores  out fp32 [B][nb_vis] (row stride nb_vis).
- * Errors: SPOT_ERR_INVALID when nb_vis > nb_cache or q_pos0 < 0.
- * Supported: d_idx in {32, 64, 128}; bf16 queries and keys; 1 <= Tq <= 128.
+ *   scores  out fp32 [B][n_tiles][nb_seq], nb_seq = ceil((q_pos0 + T) / block).
+ * Errors: SPOT_ERR_INVALID when nb_seq > nb_cache or q_pos0 < 0.
+ * Supported: d_idx in {32, 64, 128}; bf16 queries and keys; 1 <= Tq <= 128;
+ * B * n_tiles <= 65535.
  */
 SPOT_API int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,
                                        const void* sel_k, const void* sel_k_scale,
-                                       int k_dtype, float* scores, int B, int Tq,
+                                       int k_dtype, float* scores, int B, int T, int Tq,
                                        int q_pos0, int nb_cache, int kpb, int H_idx,
                                        int d_idx, int block, void* stream);
 
 /*
- * spot_prefill_attn — causal block-sparse attention for a prefill tile.
+ * spot_prefill_select_topp — dual top-p per tile: row (b, t) of scores [B][n_tiles]
+ * [nb_seq] is treated as spot_select_topp treats a row of nb_t blocks, so its recency
+ * window is the n_rec blocks ending at the tile's diagonal (Table 3: recency "per
+ * tile"), and its sink the first n_sink blocks.
+ *   sel_idx  out int32 [B][n_tiles][K_max]; sel_cnt out [B][n_tiles]; sel_mass optional
+ *            out [B][n_tiles].
+ * Errors and ordering as spot_select_topp (K_max must hold the largest reserved set).
+ * Supported: nb_seq <= 16384.
+ */
+SPOT_API int spot_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
+                                      float* sel_mass, int B, int T, int Tq, int q_pos0,
+                                      int block, float p, int K_min, int K_max, int n_sink,
+                                      int n_rec, void* stream);
+
+/*
+ * spot_prefill_attn — causal block-sparse attention for the tiles of a prefill.
  *
- * Query i of the tile (position q_pos0 + i) attends to the tokens t <= q_pos0 + i,
- * t < L, whose block is in sel_idx[b][0 .. sel_cnt[b]-1] (the same set for the whole
- * tile and every head). Rows with no visible selected token get zeros.
- *   q    [B][Hq][Tq][d]; K, V [B][Hkv][L][d]; out [B][Hq][Tq][d]; kv_dtype SPOT_BF16;
- *        16-byte aligned.
- * Supported: d == 128, block == 64, 1 <= Tq <= 128, K_max <= 8192, Hq/Hkv in {1, 2, 4, 8}.
+ * Query i of tile t (position q_pos0 + i) attends to the tokens s <= q_pos0 + i, s < L,
+ * whose block is in sel_idx[b][t][0 .. sel_cnt[b][t]-1] (one set for the whole tile
+ * and every head). Rows with no visible selected token get zeros.
+ *   q    [B][Hq][T][d]; K, V [B][Hkv][L][d]; out [B][Hq][T][d]; kv_dtype SPOT_BF16;
+ *        16-byte aligned. q_pos0 + T <= L (the queries' own tokens are in the cache).
+ * Supported: d == 128, block == 64, 1 <= Tq <= 128, K_max <= 8192, Hq/Hkv in
+ * {1, 2, 4, 8}, B * n_tiles <= 65535.
  */
 SPOT_API int spot_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                                int kv_dtype, const int32_t* sel_idx, const int32_t* sel_cnt,
-                               int K_max, void* out, int B, int Hq, int Hkv, int Tq,
+                               int K_max, void* out, int B, int Hq, int Hkv, int T, int Tq,
                                int q_pos0, int d, int L, int block, float sm_scale,
                                void* stream);
 

@@ -26,7 +26,7 @@ def fake(addr=0x10000):
 
 def test_exports_match_header(lib):
     declared = _lib.declared_symbols()
-    assert len(declared) == 9
+    assert len(declared) == 10
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -146,15 +146,32 @@ def test_sparse_attn_validation(lib):
 
 def test_prefill_validation(lib):
     a = dict(sel_q=fake(), q_dtype=BF16, sel_w=fake(), sel_k=fake(), sel_k_scale=None,
-             k_dtype=BF16, scores=fake(), B=1, Tq=128, q_pos0=32640, nb_cache=512, kpb=1,
-             H_idx=4, d_idx=64, block=64, stream=None)
+             k_dtype=BF16, scores=fake(), B=1, T=128, Tq=128, q_pos0=32640, nb_cache=512,
+             kpb=1, H_idx=4, d_idx=64, block=64, stream=None)
     assert lib.spot_prefill_select_score(*{**a, "nb_cache": 100}.values()) == INVALID
     assert lib.spot_prefill_select_score(*{**a, "q_pos0": -1}.values()) == INVALID
-    assert lib.spot_prefill_select_score(*{**a, "Tq": 256, "q_pos0": 0}.values()) == UNSUPPORTED
+    assert lib.spot_prefill_select_score(*{**a, "T": 0}.values()) == INVALID
+    assert lib.spot_prefill_select_score(*{**a, "T": 256, "Tq": 256, "q_pos0": 0}.values()) \
+        == UNSUPPORTED
     assert lib.spot_prefill_select_score(*{**a, "q_dtype": F32}.values()) == UNSUPPORTED
+    # a whole 32K sequence needs 512 visible blocks: more than the cache holds here
+    assert lib.spot_prefill_select_score(*{**a, "T": 32768, "q_pos0": 0,
+                                           "nb_cache": 511}.values()) == INVALID
+    # 65536 tiles of one query exceed the grid
+    assert lib.spot_prefill_select_score(*{**a, "T": 65536, "Tq": 1, "q_pos0": 0,
+                                           "nb_cache": 1024}.values()) == UNSUPPORTED
+    t = dict(scores=fake(), sel_idx=fake(), sel_cnt=fake(), sel_mass=None, B=1, T=32768,
+             Tq=128, q_pos0=0, block=64, p=0.95, K_min=0, K_max=512, n_sink=1, n_rec=4,
+             stream=None)
+    assert lib.spot_prefill_select_topp(*{**t, "scores": None}.values()) == INVALID
+    assert lib.spot_prefill_select_topp(*{**t, "Tq": 0}.values()) == INVALID
+    assert lib.spot_prefill_select_topp(*{**t, "p": float("inf")}.values()) == INVALID
+    assert lib.spot_prefill_select_topp(*{**t, "K_max": 4}.values()) == INVALID  # r = 5
+    assert lib.spot_prefill_select_topp(*{**t, "T": 2 ** 21}.values()) == UNSUPPORTED
     b = dict(q=fake(), k=fake(), v=fake(), kv_dtype=BF16, sel_idx=fake(), sel_cnt=fake(),
-             K_max=512, out=fake(), B=1, Hq=32, Hkv=8, Tq=128, q_pos0=32640, d=128, L=32768,
-             block=64, sm_scale=0.08, stream=None)
+             K_max=512, out=fake(), B=1, Hq=32, Hkv=8, T=128, Tq=128, q_pos0=32640, d=128,
+             L=32768, block=64, sm_scale=0.08, stream=None)
     assert lib.spot_prefill_attn(*{**b, "q_pos0": 32700}.values()) == INVALID   # past L
+    assert lib.spot_prefill_attn(*{**b, "T": 32768, "q_pos0": 1}.values()) == INVALID
     assert lib.spot_prefill_attn(*{**b, "d": 64}.values()) == UNSUPPORTED
     assert lib.spot_prefill_attn(*{**b, "kv_dtype": F32}.values()) == UNSUPPORTED

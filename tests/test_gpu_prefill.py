@@ -154,3 +154,73 @@ class _KV:
     def __getitem__(self, key):
         b, g = key
         return self.t[b, g].to("cpu", torch.float64).numpy()
+
+
+def _sequence_case(B, T, Tq, q_pos0, Hq, Hkv, p, n_sink, n_rec, K_min, seed, tiles_checked,
+                   heads_checked):
+    """Whole-sequence prefill through the three tile-indexed calls, checked per tile
+    against the oracle: every score of the checked tiles, their selection (on the GPU's
+    own scores and end to end) and the outputs of the checked heads."""
+    d, H, di, block = 128, 4, 64, 64
+    L = q_pos0 + T
+    nb_seq = -(-L // block)
+    n_tiles = -(-T // Tq)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    sel_q = torch.randn(B, T, H, di, generator=g, device=DEV).bfloat16()
+    sel_w = torch.rand(B, T, H, generator=g, device=DEV)
+    sel_k = torch.randn(B, nb_seq, 1, H, di, generator=g, device=DEV).bfloat16()
+    Q = torch.randn(B, Hq, T, d, generator=g, device=DEV).bfloat16()
+    K = torch.randn(B, Hkv, L, d, generator=g, device=DEV).bfloat16()
+    V = torch.randn(B, Hkv, L, d, generator=g, device=DEV).bfloat16()
+    scores = torch.full((B, n_tiles, nb_seq), float("nan"), device=DEV)
+    _lib.spot_prefill_select_score(sel_q, sel_w, sel_k, scores, q_pos0, Tq=Tq)
+    K_max = nb_seq
+    idx = torch.full((B, n_tiles, K_max), 12345, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, n_tiles), -1, dtype=torch.int32, device=DEV)
+    _lib.spot_prefill_select_topp(scores, idx, cnt, None, p, K_min, K_max, n_sink, n_rec,
+                                  q_pos0, T, Tq=Tq)
+    out = torch.full((B, Hq, T, d), float("nan"), device=DEV).bfloat16()
+    scale = 1 / math.sqrt(d)
+    _lib.spot_prefill_attn(Q, K, V, idx, cnt, out, q_pos0, scale, Tq=Tq)
+    torch.cuda.synchronize()
+    log(f"sequence B{B} T{T} Tq{Tq} q_pos0 {q_pos0}: {n_tiles} tiles on the GPU")
+    sq, sw, sk = np64(sel_q), np64(sel_w), np64(sel_k)
+    gs, got = np64(scores), np64(out)
+    pf = float(np.float32(p))
+    sizes = []
+    for t in tiles_checked:
+        q0, q1 = t * Tq, min((t + 1) * Tq, T)
+        nb_t = -(-(q_pos0 + q1) // block)
+        ref_s = O.prefill_tile_score(sq[:, q0:q1], sw[:, q0:q1], sk, q_pos0 + q0, block)
+        assert ref_s.shape[1] == nb_t
+        assert_scores_close(gs[:, t, :nb_t], ref_s,
+                            tile_score_magnitude(sq[:, q0:q1], sw[:, q0:q1], sk, q_pos0 + q0,
+                                                 block))
+        sets = gpu_sets(idx[:, t], cnt[:, t])
+        for b in range(B):
+            assert_topp_unit(sets[b], gs[b, t, :nb_t], pf, K_min, K_max, n_sink, n_rec,
+                             tag=f"tile {t} row {b}")
+            assert_selection_e2e(sets[b], ref_s[b], pf, K_min, K_max, n_sink, n_rec,
+                                 tag=f"tile {t} e2e {b}")
+            assert max(sets[b]) < nb_t and set(range(max(nb_t - n_rec, 0), nb_t)) <= set(sets[b])
+            sizes.append(len(sets[b]))
+        heads = {(b, h) for b in range(B) for h in heads_checked}
+        ref = O.prefill_attention(np64(Q[:, :, q0:q1]), _KV(K), _KV(V), sets, block, scale,
+                                  q_pos0 + q0, heads=heads)
+        for (b, h) in heads:
+            assert_out_close(got[b, h, q0:q1], ref[b, h], torch.bfloat16, tag=f"tile {t} ({b},{h})")
+    log(f"checked tiles {list(tiles_checked)}: |S| {sizes}")
+
+
+def test_prefill_sequence_ragged():
+    """1000 queries from position 48 in tiles of 128 (the last has 104): every tile."""
+    _sequence_case(B=2, T=1000, Tq=128, q_pos0=48, Hq=8, Hkv=2, p=0.9, n_sink=1, n_rec=4,
+                   K_min=0, seed=31, tiles_checked=range(8), heads_checked=range(8))
+
+
+def test_prefill_sequence_32k():
+    """A whole 32K prefill (256 tiles of 128, the c5 layer shape), sampled tiles."""
+    _sequence_case(B=1, T=32768, Tq=128, q_pos0=0, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
+                   K_min=0, seed=32, tiles_checked=(0, 1, 2, 37, 128, 200, 255),
+                   heads_checked=(0, 13, 31))
