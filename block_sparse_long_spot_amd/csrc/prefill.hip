@@ -9,7 +9,7 @@
 // (v_mfma_f32_16x16x32_bf16); the epilogue applies ReLU and the per-query weight w[q][h],
 // adds the heads, and keeps the maximum over the tile's queries that can see the block.
 //
-// Attention: one work-group per (16-query row tile, KV head); wave w computes query
+// Attention: one work-group per (16-query row tile, tile, KV head); wave w computes query
 // head g*G + w, so the G heads of a KV group share every K/V block the work-group
 // stages in LDS (K and V row-major, 16-byte writes). Per selected block:
 //   S' = K . Q^T   (tokens x queries; A = K from LDS, B = Q from registers)
@@ -188,21 +188,29 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
 
 // ---------------------------------------------------------------- attention
 constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
-constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS)
+constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS at most)
 
 template <int G>
 __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, uint16_t* __restrict__ out, int Hq,
-    int Hkv, int T, int Tq, int n_tiles, int q_pos0, int L, float qscale) {
+    int Hkv, int T, int Tq, int n_tiles, int B_rows, int q_pos0, int L, float qscale) {
   constexpr int D = 128;
   constexpr int NT = G * 64;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kKPad];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kBlk * kKPad];
-  __shared__ int32_t sel_s[kMaxPrefillList];
+  extern __shared__ int32_t sel_s[];  // the selected list: K_max entries (launch size)
 
-  const int rt = blockIdx.x, g = blockIdx.y, trow = blockIdx.z;
+  // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin by linear id, so
+  // the row tiles of one (tile, KV head) unit get ids of the same residue mod 8 and run
+  // back to back on one XCD, where the unit's selected blocks stay in its L2.
+  const int n_rt = (Tq + 15) / 16;
+  const int lin = blockIdx.x, x = lin & 7, j8 = lin >> 3;
+  const int rt = j8 % n_rt;
+  const int unit = (j8 / n_rt) * 8 + x;           // (tile row, KV head)
+  if (unit >= Hkv * B_rows) return;               // padding of the last group of 8 units
+  const int g = unit % Hkv, trow = unit / Hkv;
   const int b = trow / n_tiles, qs = (trow % n_tiles) * Tq;
   const int Tq_t = min(Tq, T - qs);                 // queries of this tile
   const int q0 = rt * 16;
@@ -411,15 +419,21 @@ hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v
   (void)d;
   const int G = Hq / Hkv;
   const int n_tiles = (T + Tq - 1) / Tq;
-  dim3 grid((Tq + 15) / 16, Hkv, B * n_tiles);
+  const long units = (long)Hkv * B * n_tiles;
+  const size_t lds_list = (size_t)K_max * sizeof(int32_t);  // K_max <= kMaxPrefillList
+  dim3 grid(static_cast<unsigned>((units + 7) / 8 * 8 * ((Tq + 15) / 16)));
   const float qscale = sm_scale * kLog2e;
   const uint16_t* Qp = static_cast<const uint16_t*>(q);
   const uint16_t* Kp = static_cast<const uint16_t*>(k_cache);
   const uint16_t* Vp = static_cast<const uint16_t*>(v_cache);
   uint16_t* Op = static_cast<uint16_t*>(out);
 #define SPOT_PF(GG)                                                                         \
-  hipLaunchKernelGGL(prefill_attn_kernel<GG>, grid, dim3(GG * 64), 0, stream, Qp, Kp, Vp, \
-                     sel_idx, sel_cnt, K_max, Op, Hq, Hkv, T, Tq, n_tiles, q_pos0, L, qscale)
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_attn_kernel<GG>),        \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_list);      \
+  hipLaunchKernelGGL(prefill_attn_kernel<GG>, grid, dim3(GG * 64), lds_list, stream, Qp, Kp, \
+                     Vp,                                                                   \
+                     sel_idx, sel_cnt, K_max, Op, Hq, Hkv, T, Tq, n_tiles, B * n_tiles,      \
+                     q_pos0, L, qscale)
   switch (G) {
     case 1: SPOT_PF(1); break;
     case 2: SPOT_PF(2); break;

@@ -66,6 +66,7 @@ ATTN_CASES = [
     (2, 8, 1, 64, 64, 1000, "random"),
     (1, 8, 4, 128, 700, 900, "diag_only"),
     (1, 8, 2, 33, 2000, 2100, "empty"),
+    (1, 8, 1, 16, 524272, 524288, "all"),     # the longest list: 8192 selected blocks
 ]
 
 
