@@ -1,7 +1,7 @@
 // Dual top-p block selection (SpotAttention §2.3, Eq. 7 and Eq. 8).
 //
 // One work-group per query row; latency-bound (a few thousand scores), so the design
-// minimises the chain of dependent steps: 7 work-group barriers, wave-level scans on
+// minimises the chain of dependent steps: 6 work-group barriers, wave-level scans on
 // the DPP network, one 64-bit LDS atomic per block. Every thread keeps EPT consecutive
 // blocks in registers: the score, an order-preserving 32-bit key of it, and the
 // block's softmax mass exp(s - max) in 2^-29 fixed point (integer sums are exact, so
@@ -16,7 +16,7 @@
 //      k = clamp(k_p, K_min - r, K_max - r) can produce; as the clamp is monotone this
 //      decides whether k is already known or falls inside the cut bin;
 //   4. only the bin holding the k-th block needs an exact order: its blocks (usually a
-//      handful) are gathered and one wave ranks them by (score desc, index asc),
+//      handful) are gathered and every wave ranks them by (score desc, index asc),
 //      accumulating mass in that order to finish k_p when needed. A bin with more than
 //      64 blocks (dense ties) falls back to an exact radix select, 11+11+10 bits of
 //      the key, restricted to that bin;
@@ -45,14 +45,11 @@ struct ToppSmem {
   uint32_t gk[kRankMax];             // gathered boundary-bin blocks: key, index, mass
   int32_t gi[kRankMax];
   u64 gm[kRankMax];
-  int32_t gsel[kRankMax];            // 1 if the gathered block is chosen
   int32_t ng;
   // bins found by the prefix pass: [0] mass target, [1] low count target, [2] high
   int32_t f_bin[3];
   u64 f_pre[3];                      // packed prefix (blocks and mass above the bin)
   u64 f_cnt[3];                      // blocks in the bin
-  int32_t k_final;
-  u64 inbin_mass;                    // mass of the chosen blocks of the boundary bin
   u64 wt[NT / 64];                   // per-wave totals
   u64 wt2[NT / 64];
   float wf[NT / 64];
@@ -279,7 +276,6 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   for (int i = 0; i < BPT; ++i) sh.hist[tid * BPT + i] = 0;
   if (tid == 0) {
     sh.ng = 0;
-    sh.inbin_mass = 0;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       sh.f_bin[t] = 0;
@@ -399,6 +395,8 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   u64 take = 0;  // fallback: blocks of key tau to take, lowest index first
   int slot[EPT];
   bool fallback = false;
+  u64 chosen_mask = 0;  // gathered boundary-bin blocks that are chosen (bit = slot)
+  u64 inbin_mass = 0;   // their mass
 #pragma unroll
   for (int e = 0; e < EPT; ++e) slot[e] = 0;
   if (bk >= 0) {
@@ -414,38 +412,32 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
         }
       }
       __syncthreads();  // barrier 5
-      if (wave == 0) {
-        const bool act = lane < C;
-        const uint32_t mk = act ? sh.gk[lane] : 0u;
-        const int mi = act ? sh.gi[lane] : 0x7fffffff;
-        const u64 mm = act ? sh.gm[lane] : 0ull;
-        int rank = 0;
-        u64 cm = mm;  // mass of the blocks ranked at or before this one
-        for (int j = 0; j < C; ++j) {  // j is uniform: broadcast block j from lane j
-          const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
-          const int ij = __builtin_amdgcn_readlane(mi, j);
-          const u64 gj = lane_value(mm, j);
-          const bool before_me = kj > mk || (kj == mk && ij < mi);
-          rank += before_me ? 1 : 0;
-          cm += before_me ? gj : 0ull;
-        }
-        int kk = k;
-        if (need_kp) {
-          int cand = (act && PM + cm >= T) ? A + rank + 1 : 0x7fffffff;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) cand = min(cand, __shfl_xor(cand, o, 64));
-          kk = clampk(cand);
-        }
-        const bool chosen = act && rank < kk - A;
-        if (act) sh.gsel[lane] = chosen ? 1 : 0;
-        const u64 im = lane_value(wave_incl_scan(chosen ? mm : 0ull), 63);
-        if (lane == 0) {
-          sh.k_final = kk;
-          sh.inbin_mass = im;
-        }
+      // Every wave ranks the gathered blocks (at most 64, one per lane) by itself, so
+      // the choice reaches each thread as a wave-uniform bit mask with no further
+      // barrier: lane j holds gathered block j.
+      const bool act = lane < C;
+      const uint32_t mk = act ? sh.gk[lane] : 0u;
+      const int mi = act ? sh.gi[lane] : 0x7fffffff;
+      const u64 mm = act ? sh.gm[lane] : 0ull;
+      int rank = 0;
+      u64 cm = mm;  // mass of the blocks ranked at or before this one
+      for (int j = 0; j < C; ++j) {  // j is uniform: broadcast block j from lane j
+        const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
+        const int ij = __builtin_amdgcn_readlane(mi, j);
+        const u64 gj = lane_value(mm, j);
+        const bool before_me = kj > mk || (kj == mk && ij < mi);
+        rank += before_me ? 1 : 0;
+        cm += before_me ? gj : 0ull;
       }
-      __syncthreads();  // barrier 6
-      k = sh.k_final;
+      if (need_kp) {
+        int cand = (act && PM + cm >= T) ? A + rank + 1 : 0x7fffffff;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+        k = clampk(cand);
+      }
+      const bool chosen = act && rank < k - A;
+      chosen_mask = __ballot(chosen);
+      inbin_mass = lane_value(wave_incl_scan(chosen ? mm : 0ull), 63);
     } else {
       // dense boundary bin: exact radix select over the keys of that bin only
       fallback = true;
@@ -496,7 +488,7 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
         pick = true;
       } else if (cb[e] == bk) {
         if (!fallback) {
-          pick = sh.gsel[slot[e]] != 0;
+          pick = ((chosen_mask >> slot[e]) & 1ull) != 0;
         } else if (key[e] > tau) {
           pick = true;
         } else if (key[e] == tau) {
@@ -510,7 +502,7 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
     if (pick) mass_sel += mass[e];
   }
   uint32_t cnt;
-  uint32_t pos = block_excl_scan<NT>(sel_local, cnt, sh.wt2);  // barrier 7
+  uint32_t pos = block_excl_scan<NT>(sel_local, cnt, sh.wt2);  // barrier 6
   int32_t* out = sel_idx + (size_t)b * K_max;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -522,7 +514,7 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
     if (fallback) {
       ms = block_sum<NT>(mass_sel, sh.wt);
     } else if (k > 0 && bk >= 0) {
-      ms = PM + sh.inbin_mass;
+      ms = PM + inbin_mass;
     }
     if (tid == 0)
       sel_mass[b] = Z > 0 ? static_cast<float>(static_cast<double>(ms) / static_cast<double>(Z))
