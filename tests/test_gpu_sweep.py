@@ -1,0 +1,96 @@
+"""Randomised end-to-end sweep of the decode step: many small configurations drawn
+from a seeded generator (batch, GQA ratio, head dim, block size, ragged context
+length, selector heads / dims / keys per block, key and query formats, p, budgets,
+reserved blocks, fp32 or bf16), each run through the three calls and checked against
+the oracle (every score, the selection of every row, every output head). Also two
+decode steps running concurrently on two streams."""
+import math
+import random
+
+import pytest
+import torch
+
+from block_sparse_long_spot_amd import _lib
+from block_sparse_long_spot_amd import workloads as W
+from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
+from test_gpu_parity import run_e2e
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    _lib.load()
+
+
+def _chunk(fmt):
+    return {"int4": 32, "fp4": 32, "int8": 16, "fp8": 16}.get(fmt, 8)
+
+
+def _configs(n=96, seed=1234):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        dtype = rng.choice(["f32", "bf16", "bf16"])
+        d = rng.choice([64, 128])
+        G = rng.choice([1, 2, 4, 8])
+        Hkv = rng.choice([1, 2, 4])
+        block = rng.choice([16, 32, 64, 128])
+        L = rng.randint(1, 40) * block + rng.choice([0, 0, rng.randint(1, block - 1)])
+        nb = -(-L // block)
+        kf = rng.choice(["f32", "bf16", "int8", "fp8", "int4", "fp4"])
+        qf = rng.choice([None, None, "int8", "fp8", "int4", "fp4"])
+        d_idx = rng.choice([32, 64, 128])
+        H_idx = rng.choice([1, 2, 4, 8, 16])
+        if H_idx * d_idx // _chunk(kf) > 64:
+            continue
+        kpb = rng.choice([1, 1, 2, min(block, 16)])
+        n_sink, n_rec = rng.randint(0, 3), rng.randint(0, 4)
+        r = min(nb, min(n_sink, nb) + min(n_rec, nb))
+        K_max = rng.randint(max(r, 1), nb + 3)
+        K_min = rng.randint(0, min(8, K_max))
+        p = rng.choice([0.0, 0.3, 0.9, 0.99, 1.0])
+        B = rng.randint(1, 3)
+        structure = "zipf" if nb - r > 2 and rng.random() < 0.5 else "none"
+        out.append(W.Workload(
+            f"sweep{len(out)}", B=B, Hq=G * Hkv, Hkv=Hkv, d=d, L=L, block=block, H_idx=H_idx,
+            d_idx=d_idx, kpb=kpb, dtype=dtype, sel_k_dtype=kf, p=p, K_min=K_min, K_max=K_max,
+            n_sink=n_sink, n_rec=n_rec, structure=structure, zipf_s=rng.choice([1.1, 1.6]),
+            seed=1000 + len(out), sel_q_dtype=qf))
+    return out
+
+
+SWEEP = _configs()
+
+
+@pytest.mark.parametrize("wl", SWEEP, ids=lambda w: w.name)
+def test_decode_sweep(wl):
+    print(f"{wl.name}: {wl}", flush=True)
+    inp = W.make_inputs(wl, device=DEV)
+    run_e2e(wl, inp, tag=wl.name)
+
+
+def test_two_streams_concurrently():
+    """Two decode steps with their own buffers on two streams, interleaved: each result
+    equals the same step run alone, bit for bit (the library keeps no shared state)."""
+    wa = W.WORKLOADS["c2_32k_b4"]
+    wb = W.WORKLOADS["c3_128k_b8"].with_(B=2, L=16384)
+    ia, ib = W.make_inputs(wa, device=DEV, seed=5), W.make_inputs(wb, device=DEV, seed=6)
+    ref = []
+    for wl, inp in ((wa, ia), (wb, ib)):
+        bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+        decode_step(inp, wl, bufs)
+        torch.cuda.synchronize()
+        ref.append((bufs.sel_idx.clone(), bufs.out.clone()))
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ba = DecodeBuffers(wa.B, wa.nb, wa.Hq, wa.d, wa.K_max, torch.bfloat16)
+    bb = DecodeBuffers(wb.B, wb.nb, wb.Hq, wb.d, wb.K_max, torch.bfloat16)
+    for _ in range(20):
+        decode_step(ia, wa, ba, stream=sa)
+        decode_step(ib, wb, bb, stream=sb)
+    torch.cuda.synchronize()
+    assert torch.equal(ba.sel_idx, ref[0][0]) and torch.equal(ba.out, ref[0][1])
+    assert torch.equal(bb.sel_idx, ref[1][0]) and torch.equal(bb.out, ref[1][1])
