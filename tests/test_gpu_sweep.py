@@ -94,3 +94,76 @@ def test_two_streams_concurrently():
     torch.cuda.synchronize()
     assert torch.equal(ba.sel_idx, ref[0][0]) and torch.equal(ba.out, ref[0][1])
     assert torch.equal(bb.sel_idx, ref[1][0]) and torch.equal(bb.out, ref[1][1])
+
+
+def _prefill_configs(n=40, seed=4321):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        Tq = rng.choice([1, 7, 16, 33, 64, 100, 128])
+        T = rng.randint(1, 6) * Tq + rng.choice([0, rng.randint(0, max(Tq - 1, 0))])
+        q_pos0 = rng.choice([0, 0, rng.randint(1, 700)])
+        G, Hkv = rng.choice([1, 2, 4, 8]), rng.choice([1, 2])
+        H_idx = rng.choice([1, 2, 4, 8])
+        d_idx = rng.choice([32, 64, 128])
+        if H_idx * d_idx // 8 > 64:
+            H_idx = 4
+        out.append(dict(B=rng.randint(1, 2), T=T, Tq=Tq, q_pos0=q_pos0, Hq=G * Hkv, Hkv=Hkv,
+                        H_idx=H_idx, d_idx=d_idx, kpb=rng.choice([1, 1, 2, 3]),
+                        p=rng.choice([0.0, 0.5, 0.9, 1.0]), K_min=rng.randint(0, 6),
+                        n_sink=rng.randint(0, 2), n_rec=rng.randint(0, 4), seed=2000 + i))
+    return out
+
+
+@pytest.mark.parametrize("c", _prefill_configs(), ids=lambda c: f"T{c['T']}-Tq{c['Tq']}-p0{c['q_pos0']}-s{c['seed']}")
+def test_prefill_sweep(c):
+    """Random whole-sequence prefills (any tile size, start position and GQA ratio)
+    against the oracle, every tile."""
+    import numpy as np
+    from oracle import spot_oracle as O
+    from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
+                        assert_topp_unit, gpu_sets, np64, tile_score_magnitude)
+    print(c, flush=True)
+    B, T, Tq, q_pos0, Hq, Hkv = c["B"], c["T"], c["Tq"], c["q_pos0"], c["Hq"], c["Hkv"]
+    H, di, kpb, d, block = c["H_idx"], c["d_idx"], c["kpb"], 128, 64
+    L = q_pos0 + T
+    nb = -(-L // block)
+    n_tiles = -(-T // Tq)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(c["seed"])
+    sel_q = torch.randn(B, T, H, di, generator=g, device=DEV).bfloat16()
+    sel_w = torch.randn(B, T, H, generator=g, device=DEV)
+    sel_k = torch.randn(B, nb, kpb, H, di, generator=g, device=DEV).bfloat16()
+    Q = torch.randn(B, Hq, T, d, generator=g, device=DEV).bfloat16()
+    K = torch.randn(B, Hkv, L, d, generator=g, device=DEV).bfloat16()
+    V = torch.randn(B, Hkv, L, d, generator=g, device=DEV).bfloat16()
+    K_max = max(nb, 1)
+    K_min, p, n_sink, n_rec = c["K_min"], c["p"], c["n_sink"], c["n_rec"]
+    scores = torch.full((B, n_tiles, nb), float("nan"), device=DEV)
+    _lib.spot_prefill_select_score(sel_q, sel_w, sel_k, scores, q_pos0, kpb=kpb, Tq=Tq)
+    idx = torch.empty(B, n_tiles, K_max, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(B, n_tiles, dtype=torch.int32, device=DEV)
+    _lib.spot_prefill_select_topp(scores, idx, cnt, None, p, K_min, K_max, n_sink, n_rec, q_pos0,
+                                  T, Tq=Tq)
+    out = torch.full((B, Hq, T, d), float("nan"), device=DEV).bfloat16()
+    scale = 1 / math.sqrt(d)
+    _lib.spot_prefill_attn(Q, K, V, idx, cnt, out, q_pos0, scale, Tq=Tq)
+    torch.cuda.synchronize()
+    sq, sw, sk, gs = np64(sel_q), np64(sel_w), np64(sel_k), np64(scores)
+    Qd, Kd, Vd, got = np64(Q), np64(K), np64(V), np64(out)
+    pf = float(np.float32(p))
+    for t in range(n_tiles):
+        q0, q1 = t * Tq, min((t + 1) * Tq, T)
+        nb_t = -(-(q_pos0 + q1) // block)
+        ref_s = O.prefill_tile_score(sq[:, q0:q1], sw[:, q0:q1], sk, q_pos0 + q0, block)
+        assert_scores_close(gs[:, t, :nb_t], ref_s,
+                            tile_score_magnitude(sq[:, q0:q1], sw[:, q0:q1], sk, q_pos0 + q0,
+                                                 block))
+        sets = gpu_sets(idx[:, t], cnt[:, t])
+        for b in range(B):
+            assert_topp_unit(sets[b], gs[b, t, :nb_t], pf, K_min, K_max, n_sink, n_rec,
+                             tag=f"tile {t} row {b}")
+            assert_selection_e2e(sets[b], ref_s[b], pf, K_min, K_max, n_sink, n_rec,
+                                 tag=f"tile {t} e2e {b}")
+        ref = O.prefill_attention(Qd[:, :, q0:q1], Kd, Vd, sets, block, scale, q_pos0 + q0)
+        assert_out_close(got[:, :, q0:q1], ref, torch.bfloat16, tag=f"tile {t}")
