@@ -152,20 +152,46 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// Reductions across the rows of 16 lanes with gfx950's lane-swap instructions (VALU,
+// no LDS round trip). With both operands equal, v_permlane16_swap returns in every
+// lane the values of lanes l & ~16 and l | 16, and v_permlane32_swap those of lanes
+// l & 31 and (l & 31) + 32: their sum or maximum is the reduction over the lane pair
+// l, l ^ 16 (resp. l, l ^ 32), computed in the same order in both lanes.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sum over aligned groups of W lanes (W a power of two <= 64), result in every lane of
 // the group, for values already summed over aligned groups of FROM lanes (every lane of
 // such a group holds the same value; FROM = 1 for arbitrary values). Inside a row of 16
 // the steps run on the DPP network (quad_perm swaps, then row half-mirror and mirror,
 // which pair each lane with one in the other half of its group of 8 or 16); across rows
-// they are shuffles.
+// they are lane swaps.
 template <int W, int FROM = 1>
 __device__ __forceinline__ float group_sum_dpp(float x) {
   if constexpr (FROM <= 1 && W >= 2) x += dpp_rot<0xB1>(x);    // quad_perm [1,0,3,2]
   if constexpr (FROM <= 2 && W >= 4) x += dpp_rot<0x4E>(x);    // quad_perm [2,3,0,1]
   if constexpr (FROM <= 4 && W >= 8) x += dpp_rot<0x141>(x);   // row_half_mirror
   if constexpr (FROM <= 8 && W >= 16) x += dpp_rot<0x140>(x);  // row_mirror
-  if constexpr (FROM <= 16 && W >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (FROM <= 32 && W >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (FROM <= 16 && W >= 32) x = xor16_sum(x);
+  if constexpr (FROM <= 32 && W >= 64) x = xor32_sum(x);
   return x;
 }
 // The same with the group size 2^log2w chosen at run time (uniform across the wave).

@@ -123,8 +123,7 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     }
   }
   // lanes col, col+16, col+32, col+48 hold the same column; then across the waves
-  best = fmaxf(best, shfl_xor_f(best, 16));
-  best = fmaxf(best, shfl_xor_f(best, 32));
+  best = xor32_max(xor16_max(best));
   if (kg == 0) colmax[wave][col] = best;
   __syncthreads();
   if (wave == 0 && kg == 0 && blk < nb_vis) {
@@ -181,8 +180,7 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
       }
     }
   }
-  best = fmaxf(best, shfl_xor_f(best, 16));
-  best = fmaxf(best, shfl_xor_f(best, 32));
+  best = xor32_max(xor16_max(best));
   if (kg == 0 && blk < nb_vis) scores[(size_t)blockIdx.y * nb_stride + blk] = best;
 }
 
@@ -308,8 +306,7 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
         sc[T][r] = z;
         bm = fmaxf(bm, z);
       }
-    bm = fmaxf(bm, shfl_xor_f(bm, 16));
-    bm = fmaxf(bm, shfl_xor_f(bm, 32));
+    bm = xor32_max(xor16_max(bm));
     const float mn = fmaxf(m, bm);
     const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
     float rs = 0.f;
@@ -321,8 +318,7 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
         sc[T][r] = pz;
         rs += pz;
       }
-    rs += shfl_xor_f(rs, 16);
-    rs += shfl_xor_f(rs, 32);
+    rs = xor32_sum(xor16_sum(rs));
     l = l * alpha + rs;
     m = mn;
     // rescale O rows kg*4 + r by the alpha of those rows (held by lanes with that row)
