@@ -17,17 +17,20 @@
 // size moves the same bytes per work-group.
 //
 // HBM-bound (about 4 flop per byte in bf16 with G = 4). Two run kernels:
-//  * attn_mfma (bf16, d in {64,128}): each wave owns whole 64-token chunks.
-//    q.K^T runs on the MFMA units (v_mfma_f32_16x16x32_bf16, the G heads padded to
-//    16 rows): every lane loads 16 contiguous bytes of a K row straight into the
-//    B-operand layout, no LDS staging and no bf16->fp32 conversion. K and V are read
-//    once, so their loads are non-temporal (measured: ~7% more HBM throughput on this
-//    random-block gather than cached loads), and each wave loads the next block's K
-//    while it consumes the current block (~5% more). P.V runs on the
-//    VALU: each lane owns 8 head dims of a set of tokens, reading V rows with
-//    coalesced 16-byte loads, and probabilities come through a per-wave LDS tile.
+//  * attn_mfma (bf16, d in {64,128}): each wave owns whole 64-token chunks, and both
+//    products run on the MFMA units (v_mfma_f32_16x16x32_bf16, the G heads padded to
+//    16). S' = K.Q^T (tokens x heads): every lane loads 16 contiguous bytes of a K row
+//    straight into the A-operand layout, no LDS staging. The accumulator layout leaves
+//    each lane 16 scores of one head, so the online softmax reduces across four lanes
+//    and the probabilities, rounded to bf16, are already the A operand of O += P.V;
+//    V goes to a per-wave LDS tile (coalesced 16-byte row loads) and comes back as the
+//    B operand through gfx950's transposing LDS read. K and V are read once, so their
+//    loads are non-temporal (measured: ~7% more HBM throughput on this random-block
+//    gather than cached loads), and each wave loads the next chunk's K while it
+//    consumes the current one (~5% more).
 //  * attn_generic (fp32 or bf16, any supported shape): one wave per run;
-//    lane = token for q.K^T (64 tokens of a block at a time), lane = head dim for P.V.
+//    lane = token for q.K^T (64 tokens of a block at a time), lane = head dim for P.V,
+//    all in fp32.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
 #include "device_common.h"
 #include "spot_internal.h"
@@ -174,17 +177,18 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml, int Hq, int Hkv, int L, float qscale, int bps, int nsplit) {
-  constexpr int KS = D / 32;   // MFMA k-steps over the head dim
-  constexpr int DC = D / 8;    // lanes covering one V row (8 dims each)
-  constexpr int TG = 64 / DC;  // token groups in P.V
-  constexpr int TPL = DC;      // tokens per lane per chunk in P.V (= 64 / TG)
-  constexpr int NG = (G + 3) / 4;  // 16-lane groups that hold real heads in S
+  constexpr int KS = D / 32;   // MFMA k-steps over the head dim in q.K^T
+  constexpr int NT = D / 16;   // 16-dim output tiles of P.V
+  constexpr int DC = D / 8;    // lanes covering one V row (8 dims each) in the V loads
+  constexpr int TG = 64 / DC;  // V rows per load instruction
+  constexpr int TPL = DC;      // V loads per lane per chunk (= 64 / TG)
+  constexpr int VP = D + 8;    // V tile row stride in LDS, in bf16 (16 B of padding)
   constexpr int TPB = BS / 16;                    // 16-token tiles per block
   constexpr int EPC = BS >= kChunk ? 1 : kChunk / BS;  // list entries per chunk
   constexpr int CPE = BS >= kChunk ? BS / kChunk : 1;  // chunks per list entry
   static_assert(G <= 8, "at most 8 query heads per KV head");
   static_assert(BS == 16 || BS == 32 || BS == 64 || BS == 128, "block of 16 to 128 tokens");
-  static_assert(16 % TG == 0, "a lane's P.V tokens of one step lie in one tile");
+  static_assert(16 % TG == 0, "the rows of one V load lie in one tile");
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int cnt = min(max(sel_cnt[b], 0), K_max);
@@ -201,14 +205,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   const int j1 = min(j0 + run, cnt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;  // MFMA operand coordinates
-  const int dc = lane % DC, tg = lane / DC;   // P.V coordinates
+  const int dc = lane % DC, tg = lane / DC;   // V load coordinates
 
-  __shared__ __attribute__((aligned(16))) float Ps[NW][kChunk][G < 4 ? 4 : G];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NW][kChunk * VP];
   __shared__ float mm[NW][G], ll[NW][G];
   __shared__ float accs[NW][G][D];
 
-  // A operand: row = query head of the group (zero rows beyond G), k = head dim
-  bf16x8_t qa[KS];
+  // B operand of S' = K.Q^T: column = query head of the group (zero beyond G), k = head dim
+  bf16x8_t qb[KS];
   {
     const bool hv = row < G;
     const uint16_t* qp = q + ((size_t)b * Hq + g * G + (hv ? row : 0)) * D;
@@ -216,33 +220,25 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     for (int s = 0; s < KS; ++s) {
       bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + s * 32 + kg * 8);
       if (!hv) v = bf16x8_t{};
-      qa[s] = v;
+      qb[s] = v;
     }
   }
-
-  float mrow[4], lrow[4];  // state of heads kg*4 + r (meaningful for kg < NG)
+  float m = -INFINITY, l = 0.f;  // online-softmax state of head `row`
+  floatx4_t o[NT];               // o[dt][r] = O[head 4kg + r][dim 16dt + row]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mrow[r] = -INFINITY;
-    lrow[r] = 0.f;
-  }
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+  for (int dt = 0; dt < NT; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nbl = (L + BS - 1) / BS;
   const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
   const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+  const int n_ent = j1 - j0;
+  const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
+  const int n_mine = (n_chunks - wave + NW - 1) / NW;
   // This wave's chunks are wave + i*NW. The list entries they use are read once, one
   // per lane (at most 64 per wave; the split plan keeps runs within that), so a
   // chunk's tile starts are register reads, not loads on the critical path.
   //   BS >= 64: lane i holds the entry of chunk i;
   //   BS <  64: lane i*EPC + u holds entry u of chunk i.
-  const int n_ent = j1 - j0;
-  const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
-  const int n_mine = (n_chunks - wave + NW - 1) / NW;
   int my_blk = -1;
   {
     const int i = lane / EPC, u = lane % EPC;
@@ -273,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     for (int T = 0; T < 4; ++T) a = a || (st[T] >= 0 && st[T] < L);
     return a;
   };
-  // K rows of a chunk in the B-operand layout: lane (token row, k-group kg)
+  // K rows of a chunk in the A-operand layout: lane (token row, k-group kg)
   auto load_k = [&](const int (&st)[4], bf16x8_t (&kb)[4][KS]) {
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
@@ -284,8 +280,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
         kb[T][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kp + s * 32));
     }
   };
-  // V rows of a chunk: lane (dim chunk dc, token group tg), whole rows per instruction;
-  // chunk token i*TG + tg lies in tile (i*TG)/16
+  // V rows of a chunk: lane (dim chunk dc, row group tg), whole rows per instruction
   auto load_v = [&](const int (&st)[4], u32x4_t (&vv)[TPL]) {
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
@@ -295,93 +290,77 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
           reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + dc * 8));
     }
   };
-  // online-softmax update of this wave's state with one chunk
+  uint16_t* const vs = Vs[wave];
   auto consume = [&](const int (&st)[4], const bf16x8_t (&kb)[4][KS],
                      const u32x4_t (&vv)[TPL]) {
-    // S[head][token] for the 4 tiles of 16 tokens
-    floatx4_t sa[4];
+    // the chunk's V rows to this wave's LDS tile, row t = chunk token t
+#pragma unroll
+    for (int i = 0; i < TPL; ++i)
+      *reinterpret_cast<u32x4_t*>(&vs[(i * TG + tg) * VP + dc * 8]) = vv[i];
+    // S'[token][head] for the 4 tiles: sc[T][r] = S'[chunk token 16T + 4kg + r][head row]
+    floatx4_t sc[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       floatx4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb[T][s], a, 0, 0, 0);
-      sa[T] = a;
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[T][s], qb[s], a, 0, 0, 0);
+      sc[T] = a;
     }
-    float z[4][4];
+    float bm = -INFINITY;
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const bool tv = st[T] >= 0 && st[T] + row < L;
+    for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[T][r] = tv ? sa[T][r] * qscale : -INFINITY;
-    }
-    float alpha[4];
+      for (int r = 0; r < 4; ++r) {
+        const bool tv = st[T] >= 0 && st[T] + 4 * kg + r < L;
+        const float z = tv ? sc[T][r] * qscale : -INFINITY;
+        sc[T][r] = z;
+        bm = fmaxf(bm, z);
+      }
+    bm = xor32_max(xor16_max(bm));
+    // the chunk has a token below L, so bm and mn are finite; alpha = 0 on the first chunk
+    const float mn = fmaxf(m, bm);
+    const float alpha = exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sc[T][r] - mn);
+        sc[T][r] = p;
+        rs += p;
+      }
+    rs = xor32_sum(xor16_sum(rs));
+    l = l * alpha + rs;
+    m = mn;
+    // rescale O rows 4kg + r by their head's alpha, held by lane 4kg + r (rows >= G
+    // are padding and take any finite factor)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float bm = fmaxf(fmaxf(z[0][r], z[1][r]), fmaxf(z[2][r], z[3][r]));
-      bm = row16_max(bm);
-      const float mn = fmaxf(mrow[r], bm);
-      alpha[r] = exp2f(mrow[r] - mn);
-      float rs = 0.f;
+      float ar = readlane_f(alpha, r);
+      if constexpr (G > 4) ar = kg == 1 ? readlane_f(alpha, 4 + r) : ar;
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        z[T][r] = exp2f(z[T][r] - mn);
-        rs += z[T][r];
-      }
-      rs = row16_sum(rs);
-      lrow[r] = lrow[r] * alpha[r] + rs;
-      mrow[r] = mn;
-    }
-    // probabilities to the wave's LDS tile, [token][head]
-    if (kg < NG) {
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        float* dst = &Ps[wave][T * 16 + row][kg * 4];
-        if constexpr (G >= 4) {
-          *reinterpret_cast<float4*>(dst) = make_float4(z[T][0], z[T][1], z[T][2], z[T][3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < G; ++r) dst[r] = z[T][r];
-        }
-      }
-    }
-    // rescale the accumulators by each head's alpha (heads live in lane groups)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = readlane_f(alpha[h & 3], (h >> 2) * 16);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] *= a;
+      for (int dt = 0; dt < NT; ++dt) o[dt][r] *= ar;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O += P.V: A = P (k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}, in bf16),
+    // B = V from the transposing LDS read in the same token order
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const int tok = i * TG + tg;
-      float ph[G];
-      if constexpr (G >= 4) {
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8_t pa = {(__bf16)sc[2 * s][0],     (__bf16)sc[2 * s][1],
+                           (__bf16)sc[2 * s][2],     (__bf16)sc[2 * s][3],
+                           (__bf16)sc[2 * s + 1][0], (__bf16)sc[2 * s + 1][1],
+                           (__bf16)sc[2 * s + 1][2], (__bf16)sc[2 * s + 1][3]};
 #pragma unroll
-        for (int h4 = 0; h4 < G; h4 += 4) {
-          const float4 pv = *reinterpret_cast<const float4*>(&Ps[wave][tok][h4]);
-          ph[h4] = pv.x;
-          ph[h4 + 1] = pv.y;
-          ph[h4 + 2] = pv.z;
-          ph[h4 + 3] = pv.w;
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) ph[h] = Ps[wave][tok][h];
+      for (int dt = 0; dt < NT; ++dt) {
+        // lane `row` receives V[32s + 4kg + k][16dt + row], k = 0..3, then the same 16
+        // tokens later: the token order of pa
+        const uint16_t* vp = &vs[(32 * s + 4 * kg + row / 4) * VP + dt * 16 + 4 * (row % 4)];
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, lds_tr_b_operand(vp, VP), o[dt],
+                                                        0, 0, 0);
       }
-      float v[8];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        v[2 * c] = bf16_lo(vv[i][c]);
-        v[2 * c + 1] = bf16_hi(vv[i][c]);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(ph[h], v[c], acc[h][c]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -414,37 +393,25 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     }
   }
 
-  // sum the token groups: lanes dc, dc + DC, ... hold the same head dims
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float x = acc[h][c];
-#pragma unroll
-      for (int o = DC; o < 64; o <<= 1) x += shfl_xor_f(x, o);
-      acc[h][c] = x;
-    }
-  if (lane < DC) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) accs[wave][h][dc * 8 + c] = acc[h][c];
+  // this wave's state to LDS: heads h < G (O row h lives in lanes kg = h / 4, r = h % 4)
+  if (lane < G) {
+    mm[wave][lane] = m;
+    ll[wave][lane] = l;
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mh = readlane_f(mrow[h & 3], (h >> 2) * 16);
-    const float lh = readlane_f(lrow[h & 3], (h >> 2) * 16);
-    if (lane == 0) {
-      mm[wave][h] = mh;
-      ll[wave][h] = lh;
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * kg + r;
+    if (h < G) {
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) accs[wave][h][dt * 16 + row] = o[dt][r];
     }
   }
   __syncthreads();
   // merge the waves of this work-group into the run result
   __shared__ float racc[G][D];
   __shared__ float rm[G], rl[G];
-  for (int o = threadIdx.x; o < G * D; o += NW * 64) {
-    const int h = o / D, dd = o % D;
+  for (int oi = threadIdx.x; oi < G * D; oi += NW * 64) {
+    const int h = oi / D, dd = oi % D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w][h]);

@@ -12,6 +12,30 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// An LDS address of a kernel's shared arrays as the LDS-space pointer that the
+// transposing LDS read takes.
+__device__ __forceinline__ lds_s16x4_t* lds_s16x4(const uint16_t* p) {
+  return (lds_s16x4_t*)((__attribute__((address_space(3))) uint16_t*)p);
+}
+
+// B operand (k = 8 tokens, n = 16 dims) of v_mfma_f32_16x16x32_bf16 from a row-major
+// [token][dim] bf16 tile in LDS, through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16). In each 16-lane group, source lane `row` passes the address of
+// tile row r0 + row/4, column c0 + 4(row%4); lane `row` then receives column c0 + row
+// of rows r0 .. r0+3 (k = 0..3) and of rows r0+16 .. r0+19 (k = 4..7). `stride` is the
+// tile's row stride in elements.
+__device__ __forceinline__ bf16x8_t lds_tr_b_operand(const uint16_t* p, int stride) {
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(p));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(p + 16 * stride));
+  const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  const u32x4_t v = {l2[0], l2[1], h2[0], h2[1]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // bfloat16 is the upper half of a binary32: widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

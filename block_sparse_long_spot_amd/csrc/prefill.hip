@@ -27,15 +27,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBlk = 64;
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-// An LDS address of this kernel's shared arrays as the LDS-space pointer the
-// transposing read takes.
-__device__ __forceinline__ lds_s16x4_t* lds_s16x4(const uint16_t* p) {
-  return (lds_s16x4_t*)((__attribute__((address_space(3))) uint16_t*)p);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f_to_bf16_rne(lo)) | (static_cast<uint32_t>(f_to_bf16_rne(hi)) << 16);
 }
@@ -331,8 +322,7 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
     // P as the A operand: k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-      u32x4 pk;
+      u32x4_t pk;
       pk[0] = pack_bf16x2(sc[2 * s][0], sc[2 * s][1]);
       pk[1] = pack_bf16x2(sc[2 * s][2], sc[2 * s][3]);
       pk[2] = pack_bf16x2(sc[2 * s + 1][0], sc[2 * s + 1][1]);
@@ -340,20 +330,11 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
       const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        // transposing LDS reads: source lane `row` of each 16-lane group points at V row
-        // 32s + 4kg + row/4, dims dt*16 + 4*(row%4); lane `row` then receives
-        // V[32s + 4kg + k][dt*16 + row] for k = 0..3 (and the same 16 tokens later)
+        // lane `row` receives V[32s + 4kg + k][dt*16 + row], k = 0..3, then the same 16
+        // tokens later: the token order of pa
         const uint16_t* vp = &Vs[(32 * s + 4 * kg + row / 4) * kKPad + dt * 16 + 4 * (row % 4)];
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(vp));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_s16x4(vp + 16 * kKPad));
-        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        u32x4 vb;
-        vb[0] = l2[0];
-        vb[1] = l2[1];
-        vb[2] = h2[0];
-        vb[3] = h2[1];
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, vb),
-                                                        o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, lds_tr_b_operand(vp, kKPad), o[dt],
+                                                        0, 0, 0);
       }
     }
     __syncthreads();
