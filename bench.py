@@ -456,6 +456,9 @@ def main():
     ap.add_argument("--no-static", dest="static", action="store_false", default=True)
     ap.add_argument("--no-page-geometry", dest="page_geometry", action="store_false",
                     default=True)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the two prefill legs (for profiling) and print them as "
+                         "one JSON line instead of the decode headline")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -465,6 +468,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     spot.load()
+    if a.prefill_only:
+        stream = torch.cuda.Stream()
+        calibration_copy()
+        out = {"prefill": prefill_leg(max(10, a.steps // 4), 5, stream),
+               "prefill_sequence": prefill_sequence_leg(max(5, a.steps // 50), 3, stream)}
+        print(json.dumps(out), flush=True)
+        return
     wl = W.WORKLOADS[a.workload]
     if wl.prefill_Tq:
         print("choose a decode workload", file=sys.stderr)

@@ -179,8 +179,11 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
 constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
 constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS at most)
 
+// Three work-groups per CU at G = 4 (at most 168 registers, no spills): each work-group
+// waits on one block's loads at a time, so resident work-groups are what hides them
+// (measured: 15 % faster than two per CU; four per CU spill).
 template <int G>
-__global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
+__global__ __launch_bounds__(G * 64, G == 4 ? 3 : 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, uint16_t* __restrict__ out, int Hq,
@@ -242,7 +245,10 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
     return cnt;
   };
   // K and V of one block pass through registers (kbuf, vbuf) on their way to LDS, so
-  // the next block's loads are in flight while the current one is consumed
+  // the next block's loads are in flight while the current one is consumed. The loads
+  // are cached ones: the row work-groups of a tile read the same blocks, and adjacent
+  // tiles share their recency blocks, so most of them hit in L2 (measured: half the
+  // HBM fetch of non-temporal loads, 4 % faster).
   constexpr int CPT = kBlk * (D / 8) / NT;  // 16-byte chunks per thread per tensor
   u32x4_t kbuf[CPT], vbuf[CPT];
   auto fetch = [&](int blk) {
@@ -252,8 +258,8 @@ __global__ __launch_bounds__(G * 64) void prefill_attn_kernel(
       const int c = tid + i * NT;
       const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
       const int tok = min(t0 + t, L - 1);
-      kbuf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kg + (size_t)tok * D + d0));
-      vbuf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + d0));
+      kbuf[i] = *reinterpret_cast<const u32x4_t*>(Kg + (size_t)tok * D + d0);
+      vbuf[i] = *reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + d0);
     }
   };
   auto stage = [&]() {  // K and V row-major
