@@ -1,7 +1,8 @@
 // Dual top-p block selection (SpotAttention §2.3, Eq. 7 and Eq. 8).
 //
 // One work-group per query row; latency-bound (a few thousand scores), so the design
-// minimises the chain of dependent steps: 6 work-group barriers, wave-level scans on
+// minimises the chain of dependent steps: 6 work-group barriers (7 when the boundary
+// bin below holds more than 8 blocks), wave-level scans on
 // the DPP network, one 64-bit LDS atomic per block. Every thread keeps EPT consecutive
 // blocks in registers: the score, an order-preserving 32-bit key of it, and the
 // block's softmax mass exp(s - max) in 2^-29 fixed point (integer sums are exact, so
@@ -16,8 +17,9 @@
 //      k = clamp(k_p, K_min - r, K_max - r) can produce; as the clamp is monotone this
 //      decides whether k is already known or falls inside the cut bin;
 //   4. only the bin holding the k-th block needs an exact order: its blocks (usually a
-//      handful) are gathered and every wave ranks them by (score desc, index asc),
-//      accumulating mass in that order to finish k_p when needed. A bin with more than
+//      handful) are gathered and ranked by (score desc, index asc), by every wave for
+//      a handful, split over the waves for more, accumulating mass in that order to
+//      finish k_p when needed. A bin with more than
 //      64 blocks (dense ties) falls back to an exact radix select, 11+11+10 bits of
 //      the key, restricted to that bin;
 //   5. blocks in earlier bins, the chosen ones of the boundary bin, and R form S; a
@@ -33,6 +35,7 @@ typedef unsigned long long u64;
 constexpr int kCoarseBins = 2048;
 constexpr float kBinsPerNat = 64.f;  // coarse bin width: 1/64 of a unit of log-mass
 constexpr int kRankMax = 64;         // boundary bins up to this size are ranked by one wave
+constexpr int kRankRedundant = 8;    // up to this size every wave ranks the whole bin
 constexpr int kMassBits = 29;        // fixed point of a block's mass (<= 1.0)
 constexpr int kCntShift = 44;        // count field of a packed bin: 16384 blocks * 2^29 < 2^44
 constexpr u64 kMassMask = (1ull << kCntShift) - 1;
@@ -45,6 +48,8 @@ struct ToppSmem {
   uint32_t gk[kRankMax];             // gathered boundary-bin blocks: key, index, mass
   int32_t gi[kRankMax];
   u64 gm[kRankMax];
+  uint32_t grank[kRankMax];          // their rank and the mass ranked before them, summed
+  u64 gcm[kRankMax];                 // over the waves (bins of more than kRankRedundant)
   int32_t ng;
   // bins found by the prefix pass: [0] mass target, [1] low count target, [2] high
   int32_t f_bin[3];
@@ -274,6 +279,10 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   }
 #pragma unroll
   for (int i = 0; i < BPT; ++i) sh.hist[tid * BPT + i] = 0;
+  if (tid < kRankMax) {
+    sh.grank[tid] = 0;
+    sh.gcm[tid] = 0;
+  }
   if (tid == 0) {
     sh.ng = 0;
 #pragma unroll
@@ -412,23 +421,44 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
         }
       }
       __syncthreads();  // barrier 5
-      // Every wave ranks the gathered blocks (at most 64, one per lane) by itself, so
-      // the choice reaches each thread as a wave-uniform bit mask with no further
-      // barrier: lane j holds gathered block j.
+      // Lane j of every wave holds gathered block j and learns its rank by (score desc,
+      // index asc) and the mass ranked before it, so the choice reaches each thread as
+      // a wave-uniform bit mask. A small bin is ranked by every wave on its own (no
+      // barrier); a larger one is split over the waves, wave w comparing against
+      // blocks w, w + NW, ..., and the partial counts meet in LDS (one barrier).
       const bool act = lane < C;
       const uint32_t mk = act ? sh.gk[lane] : 0u;
       const int mi = act ? sh.gi[lane] : 0x7fffffff;
       const u64 mm = act ? sh.gm[lane] : 0ull;
       int rank = 0;
-      u64 cm = mm;  // mass of the blocks ranked at or before this one
-      for (int j = 0; j < C; ++j) {  // j is uniform: broadcast block j from lane j
-        const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
-        const int ij = __builtin_amdgcn_readlane(mi, j);
-        const u64 gj = lane_value(mm, j);
-        const bool before_me = kj > mk || (kj == mk && ij < mi);
-        rank += before_me ? 1 : 0;
-        cm += before_me ? gj : 0ull;
+      u64 cm = 0;  // mass of the blocks ranked before this one
+      if (C <= kRankRedundant) {
+        for (int j = 0; j < C; ++j) {  // j is uniform: broadcast block j from lane j
+          const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
+          const int ij = __builtin_amdgcn_readlane(mi, j);
+          const u64 gj = lane_value(mm, j);
+          const bool before_me = kj > mk || (kj == mk && ij < mi);
+          rank += before_me ? 1 : 0;
+          cm += before_me ? gj : 0ull;
+        }
+      } else {
+        for (int j = wave; j < C; j += NW) {  // uniform LDS reads are broadcasts
+          const uint32_t kj = sh.gk[j];
+          const int ij = sh.gi[j];
+          const u64 gj = sh.gm[j];
+          const bool before_me = kj > mk || (kj == mk && ij < mi);
+          rank += before_me ? 1 : 0;
+          cm += before_me ? gj : 0ull;
+        }
+        if (act) {
+          atomicAdd(&sh.grank[lane], static_cast<uint32_t>(rank));
+          atomicAdd(&sh.gcm[lane], cm);
+        }
+        __syncthreads();
+        rank = static_cast<int>(sh.grank[lane]);
+        cm = sh.gcm[lane];
       }
+      cm += mm;  // mass of the blocks ranked at or before this one
       if (need_kp) {
         int cand = (act && PM + cm >= T) ? A + rank + 1 : 0x7fffffff;
 #pragma unroll

@@ -113,6 +113,16 @@ def _topp_rows(kind, B, nb, g):
         x[:, 5:15] = 4.0
         x[:, 20:20 + n] = 2.5
         return x
+    if kind.startswith("nearbin"):
+        # 10 high blocks, then n blocks within 1/64 of a unit of each other where the cut
+        # falls (distinct scores in random order, pairs of them tied), then noise
+        n = int(kind[7:])
+        x = torch.rand(B, nb, generator=g) - 2.0
+        x[:, 5:15] = 4.0
+        for r in range(B):
+            x[r, 20:20 + n] = 2.49 + torch.div(torch.randperm(n, generator=g), 2,
+                                              rounding_mode="floor").float() * 1e-4
+        return x
     if kind == "zipf":
         ranks = torch.stack([torch.randperm(nb, generator=g) for _ in range(B)]).float() + 1
         return 1.1 * torch.log(nb / ranks)
@@ -146,6 +156,11 @@ TOPP_CASES = [
     (200, "tiebin65", 0.9, 0, 200, 1, 2),       # 65 tied blocks: exact radix fallback
     (300, "tiebin65", 0.9, 0, 40, 1, 2),        # fallback, then the cap inside the bin
     (300, "tiebin64", 0.5, 30, 300, 1, 2),      # floor lands inside the tied bin
+    (200, "nearbin8", 0.9, 0, 200, 1, 2),       # 8 near blocks at the cut: every wave ranks
+    (200, "nearbin9", 0.9, 0, 200, 1, 2),       # 9: ranking split over the waves
+    (300, "nearbin40", 0.8, 0, 300, 1, 2),      # the nucleus cut inside the bin
+    (300, "nearbin40", 0.0, 30, 30, 0, 0),      # a count cut inside the bin
+    (300, "nearbin63", 0.9, 16, 40, 1, 2),      # the cap inside the bin
     (40, "normal", 0.9, 100, 40, 1, 2),         # floor above nb
     (10, "normal", 0.9, 0, 10, 6, 6),           # empty residual
     (20, "normal", -0.5, 3, 20, 1, 1),          # p <= 0: floor only
