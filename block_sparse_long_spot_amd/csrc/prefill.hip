@@ -32,10 +32,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- tile scoring
-// Work-group = 16 blocks (columns) x all Tq queries; its 4 waves take interleaved row
-// tiles of 16 queries and combine their column maxima through LDS. Per selector key,
-// a wave holds the key operands of every head in registers and issues the query
-// operands of a row tile together, so the MFMAs wait on one round of loads.
 // The tile of launch row r: sequence b, first query row qs, Tq_t queries, first
 // position pos0 and nb_vis visible blocks.
 struct TileRow {
@@ -52,28 +48,67 @@ __device__ __forceinline__ TileRow tile_row(int r, int n_tiles, int T, int Tq, i
   return tr;
 }
 
-template <int DIDX, int H>
+// Four selector heads (a tile has at most 128 queries): a work-group covers CG groups of
+// 16 block columns, its 4 waves taking row tiles wave and wave + 4 of 16 queries. Each
+// wave loads the query operands and weights of its row tiles once, then streams only
+// keys, 16 blocks at a time, the next group's keys in flight while the current group is
+// scored, and the waves combine their column maxima through LDS. With one group per
+// work-group every work-group re-reads the tile's 64 KiB of selector queries (d_idx 64);
+// four groups cut that traffic and the work-group count by four.
+constexpr int kScoreMaxCG = 4;
+
+template <int DIDX>
 __global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
     const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int T, int Tq,
-    int n_tiles, int q_pos0, int nb_cache, int nb_stride, int kpb, int block) {
-  constexpr int KS = DIDX / 32;
-  constexpr int NWV = 4;
-  __shared__ float colmax[NWV][16];
+    int n_tiles, int q_pos0, int nb_cache, int nb_stride, int kpb, int block, int CG) {
+  constexpr int H = 4, KS = DIDX / 32, NWV = 4, RPW = 2;
+  __shared__ float colmax[NWV][kScoreMaxCG * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const TileRow tr = tile_row(blockIdx.y, n_tiles, T, Tq, q_pos0, block, nb_stride);
   const int b = tr.b, Tq_t = tr.Tq_t, pos0 = tr.pos0, nb_vis = tr.nb_vis;
-  const int blk0 = blockIdx.x * 16;
-  if (blk0 >= nb_vis) return;                      // no visible block here (uniform)
-  const int blk = blk0 + col;                      // B-operand column of this lane
-  const int blk_c = min(blk, nb_vis - 1);
-  const int n_rt = (Tq_t + 15) / 16;
+  const int base = blockIdx.x * CG * 16;
+  if (base >= nb_vis) return;                       // no visible block here (uniform)
+  const int n_cg = min(CG, (nb_vis - base + 15) / 16);
+  const int n_rt = (Tq_t + 15) / 16;                // <= NWV * RPW
   const uint16_t* qb = sel_q + ((size_t)b * T + tr.qs) * H * DIDX;
   const float* wb = sel_w + ((size_t)b * T + tr.qs) * H;
-  float best = -INFINITY;  // max over (visible query, key j) for column blk0 + col
-  for (int j = 0; j < kpb; ++j) {
-    bf16x8_t kop[H][KS];
+  const bool w16 = (reinterpret_cast<uintptr_t>(sel_w) & 15) == 0;
+
+  // A operands (query row = lane % 16) and weights (queries kg*4 + r) of row tiles
+  // wave and wave + NWV
+  bf16x8_t qop[RPW][H][KS];
+  float wq[RPW][4][H];
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) {
+    const int rt = min(wave + u * NWV, n_rt - 1);
+    const int qr = min(rt * 16 + col, Tq_t - 1);
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qop[u][h][s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float* wp = wb + (size_t)min(rt * 16 + kg * 4 + r, Tq_t - 1) * H;
+      if (w16) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wp);
+        wq[u][r][0] = w4.x;
+        wq[u][r][1] = w4.y;
+        wq[u][r][2] = w4.z;
+        wq[u][r][3] = w4.w;
+      } else {
+#pragma unroll
+        for (int h = 0; h < H; ++h) wq[u][r][h] = wp[h];
+      }
+    }
+  }
+  // B operands of item i = (column group i / kpb, key i % kpb): column = block
+  auto load_keys = [&](int i, bf16x8_t (&kop)[H][KS]) {
+    const int cg = i / kpb, j = i - cg * kpb;
+    const int blk_c = min(base + cg * 16 + col, nb_vis - 1);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const uint16_t* kp =
@@ -81,47 +116,59 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 #pragma unroll
       for (int s = 0; s < KS; ++s) kop[h][s] = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
     }
-    for (int rt = wave; rt < n_rt; rt += NWV) {
-      const int qr = min(rt * 16 + col, Tq_t - 1);   // A-operand row of this lane
-      bf16x8_t qop[H][KS];
-      float wq[H][4];
+  };
+  const int n_items = n_cg * kpb;
+  bf16x8_t kop[H][KS];
+  load_keys(0, kop);
+  float cur = -INFINITY;  // max over (visible query, key) of the current column group
+  for (int i = 0; i < n_items; ++i) {  // uniform
+    bf16x8_t kn[H][KS];
+    if (i + 1 < n_items) load_keys(i + 1, kn);
+    const int cg = i / kpb;
+    const int blk = base + cg * 16 + col;
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
-        const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qop[h][s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          wq[h][r] = wb[(size_t)min(rt * 16 + kg * 4 + r, Tq_t - 1) * H + h];
-      }
+    for (int u = 0; u < RPW; ++u) {
+      const int rt = wave + u * NWV;
+      if (rt >= n_rt) break;  // uniform
       floatx4_t tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         floatx4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[h][s], kop[h][s], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[u][h][s], kop[h][s], c, 0, 0, 0);
         // c[r] = S_h[query rt*16 + kg*4 + r][column col]
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tot[r] += wq[h][r] * fmaxf(c[r], 0.f);
+        for (int r = 0; r < 4; ++r) tot[r] += wq[u][r][h] * fmaxf(c[r], 0.f);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = rt * 16 + kg * 4 + r;
         const bool vis = qi < Tq_t && (long)blk * block <= (long)pos0 + qi;
-        if (vis) best = fmaxf(best, tot[r]);
+        if (vis) cur = fmaxf(cur, tot[r]);
       }
     }
-  }
-  // lanes col, col+16, col+32, col+48 hold the same column; then across the waves
-  best = xor32_max(xor16_max(best));
-  if (kg == 0) colmax[wave][col] = best;
-  __syncthreads();
-  if (wave == 0 && kg == 0 && blk < nb_vis) {
-    float m = colmax[0][col];
+    if (i - cg * kpb == kpb - 1) {  // the group's last key: lanes col, col+16, ... agree
+      const float m = xor32_max(xor16_max(cur));
+      if (kg == 0) colmax[wave][cg * 16 + col] = m;
+      cur = -INFINITY;
+    }
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) m = fmaxf(m, colmax[w][col]);
-    scores[(size_t)blockIdx.y * nb_stride + blk] = m;
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kop[h][s] = kn[h][s];
+  }
+  __syncthreads();
+  if (wave == 0 && kg == 0) {
+    for (int cg = 0; cg < n_cg; ++cg) {
+      const int blk = base + cg * 16 + col;
+      if (blk < nb_vis) {
+        float m = colmax[0][cg * 16 + col];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) m = fmaxf(m, colmax[w][cg * 16 + col]);
+        scores[(size_t)blockIdx.y * nb_stride + blk] = m;
+      }
+    }
   }
 }
 
@@ -368,29 +415,33 @@ hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
                                        int q_pos0, int nb_cache, int nb_stride, int kpb, int H,
                                        int d_idx, int block, hipStream_t stream) {
   const int n_tiles = (T + Tq - 1) / Tq;
-  dim3 grid((nb_stride + 15) / 16, B * n_tiles);
   const uint16_t* q = static_cast<const uint16_t*>(sel_q);
   const uint16_t* k = static_cast<const uint16_t*>(sel_k);
-#define SPOT_PS4(DI)                                                                         \
-  hipLaunchKernelGGL((prefill_score_kernel<DI, 4>), grid, dim3(256), 0, stream, q, sel_w, k, \
-                     scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, block)
-#define SPOT_PSA(DI)                                                                       \
-  hipLaunchKernelGGL((prefill_score_kernel_anyh<DI>), grid, dim3(64), 0, stream, q, sel_w, \
-                     k, scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, H, block)
+  const long groups = (nb_stride + 15) / 16;  // 16-block column groups
   if (H == 4) {
+    // several column groups per work-group once there are work-groups to spare
+    const int CG = (long)B * n_tiles * groups >= 2048 ? kScoreMaxCG : 1;
+    dim3 grid(static_cast<unsigned>((groups + CG - 1) / CG), B * n_tiles);
+#define SPOT_PS4(DI)                                                                          \
+  hipLaunchKernelGGL((prefill_score_kernel<DI>), grid, dim3(256), 0, stream, q, sel_w, k,     \
+                     scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, block, CG)
     switch (d_idx) {
       case 32: SPOT_PS4(32); break;
       case 64: SPOT_PS4(64); break;
       default: SPOT_PS4(128); break;
     }
+#undef SPOT_PS4
   } else {
+    dim3 grid(static_cast<unsigned>(groups), B * n_tiles);
+#define SPOT_PSA(DI)                                                                       \
+  hipLaunchKernelGGL((prefill_score_kernel_anyh<DI>), grid, dim3(64), 0, stream, q, sel_w, \
+                     k, scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, H, block)
     switch (d_idx) {
       case 32: SPOT_PSA(32); break;
       case 64: SPOT_PSA(64); break;
       default: SPOT_PSA(128); break;
     }
   }
-#undef SPOT_PS4
 #undef SPOT_PSA
   return hipGetLastError();
 }

@@ -56,6 +56,46 @@ def test_prefill_score_parity(case):
     assert_scores_close(np64(scores), ref, mag)
 
 
+SEQ_SCORE_CASES = [
+    # B, T, Tq, q_pos0, block, kpb, d_idx, weights at a 4-byte (not 16-byte) address,
+    # tiles checked. Each launch has >= 2048 (tile, 16-block column group) pairs, so a
+    # work-group scores several column groups with one load of its tile's queries.
+    (1, 1024, 16, 7168, 16, 2, 32, True, (0, 1, 31, 63)),
+    (2, 2000, 100, 30000, 32, 1, 64, False, (0, 7, 19)),
+    (1, 4000, 128, 62000, 64, 1, 128, True, (0, 13, 31)),
+]
+
+
+@pytest.mark.parametrize("case", SEQ_SCORE_CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_prefill_sequence_score_parity(case):
+    B, T, Tq, q_pos0, block, kpb, di, unaligned, tiles = case
+    log(f"prefill sequence score {case}")
+    H = 4
+    nb_seq = -(-(q_pos0 + T) // block)
+    n_tiles = -(-T // Tq)
+    assert B * n_tiles * -(-nb_seq // 16) >= 2048
+    g = torch.Generator().manual_seed(T + q_pos0)
+    sel_q = torch.randn(B, T, H, di, generator=g).bfloat16()
+    w = torch.rand(B * T * H + 1, generator=g)
+    sel_k = torch.randn(B, nb_seq, kpb, H, di, generator=g).bfloat16()
+    wd = w.to(DEV)
+    sel_w = (wd[1:] if unaligned else wd[:-1]).view(B, T, H)
+    assert (sel_w.data_ptr() % 16 != 0) == unaligned
+    scores = torch.full((B, n_tiles, nb_seq), float("nan"), device=DEV)
+    _lib.spot_prefill_select_score(sel_q.to(DEV), sel_w, sel_k.to(DEV), scores, q_pos0,
+                                   block=block, kpb=kpb, Tq=Tq)
+    torch.cuda.synchronize()
+    sq, sw, sk, gs = np64(sel_q), np64(sel_w.cpu()), np64(sel_k), np64(scores)
+    for t in tiles:
+        q0, q1 = t * Tq, min((t + 1) * Tq, T)
+        nb_t = -(-(q_pos0 + q1) // block)
+        ref = O.prefill_tile_score(sq[:, q0:q1], sw[:, q0:q1], sk, q_pos0 + q0, block)
+        assert_scores_close(gs[:, t, :nb_t], ref,
+                            tile_score_magnitude(sq[:, q0:q1], sw[:, q0:q1], sk, q_pos0 + q0,
+                                                 block))
+        assert np.isnan(gs[:, t, nb_t:]).all()  # blocks after the tile are not written
+
+
 ATTN_CASES = [
     # B, Hq, Hkv, Tq, q_pos0, L, pattern
     (1, 32, 8, 128, 32640, 32768, "random"),
