@@ -88,6 +88,7 @@ def time_back_to_back(fn, steps, warmup, stream):
     """K calls of `fn` enqueued back to back on `stream`, after `warmup` untimed ones,
     bracketed by device synchronisations. Returns (wall us per call, HIP-event us per
     call) with the two events recorded on `stream` around the K calls."""
+    torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn()
@@ -108,6 +109,7 @@ def time_back_to_back(fn, steps, warmup, stream):
 def time_steps(inp, wl, bufs, steps, warmup, stream):
     """Per-call breakdown: events between the three calls of every step. Each event adds
     a gap on the stream, so these per-call times are diagnostics, not the step time."""
+    torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     for _ in range(warmup):
         decode_step(inp, wl, bufs, stream=stream)
     torch.cuda.synchronize()
@@ -143,6 +145,7 @@ def time_graph(inp, wl, bufs, steps, warmup, stream):
     """The same step captured once as a HIP graph and replayed: identical kernels and
     arguments, without per-launch host work between them."""
     g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     decode_step(inp, wl, bufs, stream=stream)   # warm the code objects before capture
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=stream):
@@ -167,6 +170,7 @@ def time_flushed(inp, wl, bufs, reps, stream):
     step reads data left in the last-level caches by the previous one."""
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     times = []
+    torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     with torch.cuda.stream(stream):
         for _ in range(reps):
             scratch.fill_(1.0)
@@ -210,6 +214,7 @@ def prefill_leg(steps, warmup, stream):
         if ev:
             ev[3].record(stream)
 
+    torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             run()
