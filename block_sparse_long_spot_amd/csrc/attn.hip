@@ -318,15 +318,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
         bm = fmaxf(bm, z);
       }
     bm = xor32_max(xor16_max(bm));
-    // the chunk has a token below L, so bm and mn are finite; alpha = 0 on the first chunk
+    // the chunk has a token below L, so bm and mn are finite; alpha = 0 on the first chunk.
+    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 weigh nothing.
     const float mn = fmaxf(m, bm);
-    const float alpha = exp2f(m - mn);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     float rs = 0.f;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(sc[T][r] - mn);
+        const float p = __builtin_amdgcn_exp2f(sc[T][r] - mn);
         sc[T][r] = p;
         rs += p;
       }

@@ -27,10 +27,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBlk = 64;
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f_to_bf16_rne(lo)) | (static_cast<uint32_t>(f_to_bf16_rne(hi)) << 16);
-}
-
 // ---------------------------------------------------------------- tile scoring
 // The tile of launch row r: sequence b, first query row qs, Tq_t queries, first
 // position pos0 and nb_vis visible blocks.
@@ -341,24 +337,39 @@ __global__ __launch_bounds__(G * 64, G == 4 ? 3 : 1) void prefill_attn_kernel(
       sc[T] = a;  // sc[T][r] = S[query row][token T*16 + kg*4 + r]
     }
     float bm = -INFINITY;
+    if (t0 + kBlk - 1 <= pos0 + q0 && t0 + kBlk <= L) {
+      // every token of the block is visible to every query of the row tile (uniform)
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+      for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + T * 16 + kg * 4 + r;
-        const float z = (t <= my_pos && t < L) ? sc[T][r] * qscale : -INFINITY;
-        sc[T][r] = z;
-        bm = fmaxf(bm, z);
-      }
+        for (int r = 0; r < 4; ++r) {
+          sc[T][r] *= qscale;
+          bm = fmaxf(bm, sc[T][r]);
+        }
+    } else {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + T * 16 + kg * 4 + r;
+          const float z = (t <= my_pos && t < L) ? sc[T][r] * qscale : -INFINITY;
+          sc[T][r] = z;
+          bm = fmaxf(bm, z);
+        }
+    }
     bm = xor32_max(xor16_max(bm));
     const float mn = fmaxf(m, bm);
-    const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
+    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 weigh nothing.
+    // A row with no visible token yet (mn = -inf, so every z = -inf) subtracts 0
+    // instead: its p are 0 and its alpha 0 on an empty state.
+    const float mn_s = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mn_s);
     float rs = 0.f;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pz = mn == -INFINITY ? 0.f : exp2f(sc[T][r] - mn);
+        const float pz = __builtin_amdgcn_exp2f(sc[T][r] - mn_s);
         sc[T][r] = pz;
         rs += pz;
       }
@@ -375,12 +386,10 @@ __global__ __launch_bounds__(G * 64, G == 4 ? 3 : 1) void prefill_attn_kernel(
     // P as the A operand: k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4_t pk;
-      pk[0] = pack_bf16x2(sc[2 * s][0], sc[2 * s][1]);
-      pk[1] = pack_bf16x2(sc[2 * s][2], sc[2 * s][3]);
-      pk[2] = pack_bf16x2(sc[2 * s + 1][0], sc[2 * s + 1][1]);
-      pk[3] = pack_bf16x2(sc[2 * s + 1][2], sc[2 * s + 1][3]);
-      const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pk);
+      const bf16x8_t pa = {(__bf16)sc[2 * s][0],     (__bf16)sc[2 * s][1],
+                           (__bf16)sc[2 * s][2],     (__bf16)sc[2 * s][3],
+                           (__bf16)sc[2 * s + 1][0], (__bf16)sc[2 * s + 1][1],
+                           (__bf16)sc[2 * s + 1][2], (__bf16)sc[2 * s + 1][3]};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         // lane `row` receives V[32s + 4kg + k][dt*16 + row], k = 0..3, then the same 16
