@@ -69,25 +69,6 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
   o[6] = bf16_lo(a.w); o[7] = bf16_hi(a.w);
 }
 
-// The same for data read exactly once (non-temporal loads).
-__device__ __forceinline__ void load8_stream(const float* p, float* o) {
-  const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  const u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 4));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[i] = __uint_as_float(a[i]);
-    o[4 + i] = __uint_as_float(b[i]);
-  }
-}
-__device__ __forceinline__ void load8_stream(const uint16_t* p, float* o) {
-  const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = bf16_lo(a[i]);
-    o[2 * i + 1] = bf16_hi(a[i]);
-  }
-}
-
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 
 template <int WIDTH>
@@ -154,26 +135,12 @@ __device__ __forceinline__ T lane_value(T x, int lane) {
   }
 }
 
-// Sum / maximum over each row of 16 lanes (lanes 16r .. 16r+15), result in every lane
-// of the row, by rotations inside the row on the DPP network (row_ror:8,4,2,1).
+// Value of another lane of the same row of 16 lanes, on the DPP network (CTRL is a DPP
+// row control: quad_perm, row_ror, row mirror, ...).
 template <int CTRL>
 __device__ __forceinline__ float dpp_rot(float x) {
   const int xi = __float_as_int(x);
   return __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_rot<0x128>(x);
-  x += dpp_rot<0x124>(x);
-  x += dpp_rot<0x122>(x);
-  x += dpp_rot<0x121>(x);
-  return x;
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_rot<0x128>(x));
-  x = fmaxf(x, dpp_rot<0x124>(x));
-  x = fmaxf(x, dpp_rot<0x122>(x));
-  x = fmaxf(x, dpp_rot<0x121>(x));
-  return x;
 }
 
 // Reductions across the rows of 16 lanes with gfx950's lane-swap instructions (VALU,
@@ -237,9 +204,6 @@ __device__ __forceinline__ float group_sum_dpp_rt(float x, int log2w) {
 __device__ __forceinline__ uint32_t float_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 }  // namespace spot
