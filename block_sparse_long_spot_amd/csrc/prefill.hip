@@ -221,6 +221,7 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
 // ---------------------------------------------------------------- attention
 constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
 constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS at most)
+constexpr float kRescaleSlack = 8.f;   // log2 units a row maximum may grow unrescaled
 
 // Three work-groups per CU at G = 4 (at most 168 registers, no spills): each work-group
 // waits on one block's loads at a time, so resident work-groups are what hides them
@@ -358,31 +359,38 @@ __global__ __launch_bounds__(G * 64, G == 4 ? 3 : 1) void prefill_attn_kernel(
         }
     }
     bm = xor32_max(xor16_max(bm));
-    const float mn = fmaxf(m, bm);
-    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 weigh nothing.
-    // A row with no visible token yet (mn = -inf, so every z = -inf) subtracts 0
-    // instead: its p are 0 and its alpha 0 on an empty state.
-    const float mn_s = mn == -INFINITY ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - mn_s);
+    // Lazy rescaling: a row's reference maximum m moves only when a block's maximum
+    // exceeds it by more than kRescaleSlack (log2 units), so most blocks leave O and l
+    // as they are; probabilities stay below 2^kRescaleSlack, well inside bf16 and fp32,
+    // and O and l share the reference, so the final O / l is unchanged.
+    if (__ballot(bm > m + kRescaleSlack) != 0ull) {  // uniform
+      const float mn = bm > m + kRescaleSlack ? bm : m;
+      const float alpha = mn == m ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+      m = mn;
+      // rescale O rows kg*4 + r by the alpha of those rows (held by lanes with that row)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, kg * 4 + r, 64);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt][r] *= ar;
+      }
+    }
+    // v_exp_f32 directly: arguments are at most kRescaleSlack and results below 2^-126
+    // weigh nothing. A row with no visible token yet (m = -inf, so every z = -inf)
+    // subtracts 0 instead: its p are 0.
+    const float m_s = m == -INFINITY ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pz = __builtin_amdgcn_exp2f(sc[T][r] - mn_s);
+        const float pz = __builtin_amdgcn_exp2f(sc[T][r] - m_s);
         sc[T][r] = pz;
         rs += pz;
       }
     rs = xor32_sum(xor16_sum(rs));
-    l = l * alpha + rs;
-    m = mn;
-    // rescale O rows kg*4 + r by the alpha of those rows (held by lanes with that row)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, kg * 4 + r, 64);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][r] *= ar;
-    }
+    l += rs;
     // P as the A operand: k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
