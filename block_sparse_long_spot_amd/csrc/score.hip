@@ -200,10 +200,11 @@ __global__ __launch_bounds__(256) void select_score_kernel(
     }
   };
 
-  // Keys of a block are read KU at a time so their loads overlap (per-token keys): a
-  // denser format has shorter key rows, so more keys per batch keep about the same
-  // bytes in flight per wave.
-  constexpr int KU = CH == 32 ? 16 : (CH == 16 ? 8 : 4);
+  // Keys of a block are read KU at a time so their loads overlap (per-token keys): 8
+  // (16 for the 4-bit formats, whose key rows are shortest) keep enough bytes in flight
+  // per wave (measured at 16 bf16 keys of 4 x 128 per block: 8 at a time 5 % faster
+  // than 4, 16 no faster).
+  constexpr int KU = CH == 32 ? 16 : 8;
   float best = -INFINITY;
   int j = 0;
   for (; j + KU <= kpb; j += KU) {
