@@ -260,6 +260,16 @@ def test_prefill_sequence_ragged():
                    K_min=0, seed=31, tiles_checked=range(8), heads_checked=range(8))
 
 
+def test_prefill_sequence_two_heads_per_wave_ragged():
+    """Grids large enough for two heads per wave: 100-query tiles (7 row tiles, so the
+    last pair has one idle wave) with a 50-query last tile, and 128-query tiles with a
+    32-query last tile; both heads of each wave's pair are checked."""
+    _sequence_case(B=2, T=1450, Tq=100, q_pos0=37, Hq=32, Hkv=8, p=0.9, n_sink=1, n_rec=4,
+                   K_min=0, seed=33, tiles_checked=(0, 7, 14), heads_checked=(0, 1, 2, 3, 31))
+    _sequence_case(B=1, T=4000, Tq=128, q_pos0=100, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
+                   K_min=8, seed=34, tiles_checked=(0, 16, 31), heads_checked=(0, 1, 6, 7, 30))
+
+
 def test_prefill_sequence_32k():
     """A whole 32K prefill (256 tiles of 128, the c5 layer shape), sampled tiles."""
     _sequence_case(B=1, T=32768, Tq=128, q_pos0=0, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
