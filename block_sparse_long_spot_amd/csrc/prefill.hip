@@ -242,8 +242,11 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
   constexpr int RT = HPW;      // row tiles per work-group
   constexpr int HG = G / HPW;  // waves per row tile
   static_assert(G % HPW == 0, "heads per wave must divide the group");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBlk * kKPad];
+  // K and V tiles of the current block; after the last block, the output staging area
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * kBlk * kKPad];
+  uint16_t* const Ks = KVs;
+  uint16_t* const Vs = KVs + kBlk * kKPad;
+  static_assert(G * HPW * 16 * 128 <= 2 * kBlk * kKPad, "output staging must fit");
   extern __shared__ int32_t sel_s[];  // the selected list: K_max entries (launch size)
 
   // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin by linear id, so
@@ -446,20 +449,35 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
     blk = blk_next;
   }
   if (!active) return;
-  // normalise: rows kg*4 + r need the l of those rows
+  // Normalise, round to bf16 and pass through LDS so that each lane stores whole 16-byte
+  // pieces: a head's 16 x 128 output tile is one contiguous 4 KiB run of `out`. The
+  // wave's staging region is its own, and every wave is past the loop's last barrier,
+  // so no other wave still reads the K/V tiles.
+  uint16_t* const st = KVs + wave * (HPW * 16 * D);
 #pragma unroll
   for (int h = 0; h < HPW; ++h)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      // rows kg*4 + r need the l of those rows
       const float lr = __shfl(l[h], kg * 4 + r, 64);
-      const int qi = q0 + kg * 4 + r;
-      if (qi < Tq_t) {
-        uint16_t* op = out + (((size_t)b * Hq + h0 + h) * T + qs + qi) * D;
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          op[dt * 16 + row] = f_to_bf16_rne(lr > 0.f ? o[h][dt][r] / lr : 0.f);
-      }
+      for (int dt = 0; dt < 8; ++dt)
+        st[(h * 16 + kg * 4 + r) * D + dt * 16 + row] =
+            __builtin_bit_cast(uint16_t, (__bf16)(o[h][dt][r] * inv));
     }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    uint16_t* op = out + (((size_t)b * Hq + h0 + h) * T + qs + q0) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane + 64 * i;  // 16-byte piece: query c / 16, dims (c % 16) * 8 ..
+      if (q0 + c / 16 < Tq_t)
+        *reinterpret_cast<u32x4_t*>(op + c * 8) =
+            *reinterpret_cast<const u32x4_t*>(&st[(h * 16) * D + c * 8]);
+    }
+  }
 }
 
 }  // namespace
