@@ -263,7 +263,11 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
   const int Tq_t = min(Tq, T - qs);                 // queries of this tile
   const int qg0 = rg * RT * 16;                     // first query row of the work-group
   if (qg0 >= Tq_t) return;                          // past a short last tile (uniform)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index through readfirstlane, so that the compiler knows everything derived
+  // from it (heads, row tile, the per-block full/masked choice) is wave-uniform and
+  // branches on it instead of evaluating both sides under a lane mask
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h0 = g * G + (wave % HG) * HPW;         // first head of this wave
   const int q0 = qg0 + (wave / HG) * 16;            // its row tile
   const bool active = q0 < Tq_t;                    // uniform per wave
@@ -279,16 +283,26 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
     const uint16_t* qp =
         Q + (((size_t)b * Hq + h0 + h) * T + qs + min(my_q, Tq_t - 1)) * D + kg * 8;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qb[h][s] = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t w = *reinterpret_cast<const u32x4_t*>(qp + s * 32);
+      if (qscale < 0.f) w ^= 0x80008000u;  // negated q: the scores change sign instead
+      qb[h][s] = __builtin_bit_cast(bf16x8_t, w);
+    }
   }
-  float m[HPW], l[HPW];     // state of query row `row` (same in its 4 lane groups)
-  floatx4_t o[HPW][8];      // O[query (kg*4 + r)][d = dt*16 + row] per head
+  // scores are scaled into log2 units inside the exponential, by zs > 0 (a zero scale
+  // becomes a negligible positive one, so masked scores stay -inf)
+  const float zs = fmaxf(fabsf(qscale), 1e-30f);
+  // Per head: the running maximum m of query row `row` (same in its 4 lane groups) and
+  // O[query (kg*4 + r)][d = dt*16 + row] for dt < 8. Tile dt = 8 multiplies P by a
+  // column of ones, so every one of its columns holds the row sums l: the denominator
+  // comes from the same bf16 probabilities as the numerator, on the matrix units.
+  float m[HPW];
+  floatx4_t o[HPW][9];
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     m[h] = -INFINITY;
-    l[h] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[h][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 9; ++dt) o[h][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   const int cnt = min(max(sel_cnt[trow], 0), K_max);
@@ -362,32 +376,35 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
             sc[h][T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[h][s], sc[h][T], 0, 0, 0);
         }
       }
-      // sc[h][T][r] = S_h[query row][token T*16 + kg*4 + r]
-      const bool full = t0 + kBlk - 1 <= pos0 + q0 && t0 + kBlk <= L;  // uniform
+      // sc[h][T][r] = S_h[query row][token T*16 + kg*4 + r], unscaled. One uniform
+      // branch for every head: the causal and L masks are computed only for a block that
+      // crosses the row tile's diagonal or the end of the cache.
+      float bmax[HPW];
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) bmax[h] = -INFINITY;
+      if (!(t0 + kBlk - 1 <= pos0 + q0 && t0 + kBlk <= L)) {
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + T * 16 + kg * 4 + r;
+            const bool vis = t <= my_pos && t < L;
+#pragma unroll
+            for (int h = 0; h < HPW; ++h) sc[h][T][r] = vis ? sc[h][T][r] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
-        float bm = -INFINITY;
-        if (full) {
-          // every token of the block is visible to every query of the row tile
 #pragma unroll
-          for (int T = 0; T < 4; ++T)
+        for (int T = 0; T < 4; ++T)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              sc[h][T][r] *= qscale;
-              bm = fmaxf(bm, sc[h][T][r]);
-            }
-        } else {
+          for (int r = 0; r < 4; ++r) bmax[h] = fmaxf(bmax[h], sc[h][T][r]);
+      }
 #pragma unroll
-          for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = t0 + T * 16 + kg * 4 + r;
-              const float z = (t <= my_pos && t < L) ? sc[h][T][r] * qscale : -INFINITY;
-              sc[h][T][r] = z;
-              bm = fmaxf(bm, z);
-            }
-        }
-        bm = xor32_max(xor16_max(bm));
+      for (int h = 0; h < HPW; ++h) {
+        // the block maximum in log2 units (zs > 0, so scaling keeps the order)
+        float bm = xor32_max(xor16_max(bmax[h]));
+        bm = bm == -INFINITY ? bm : bm * zs;
         // Lazy rescaling: a row's reference maximum m moves only when a block's maximum
         // exceeds it by more than kRescaleSlack (log2 units), so most blocks leave O and
         // l as they are; probabilities stay below 2^kRescaleSlack, well inside bf16 and
@@ -395,30 +412,24 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
         if (__ballot(bm > m[h] + kRescaleSlack) != 0ull) {  // uniform
           const float mn = bm > m[h] + kRescaleSlack ? bm : m[h];
           const float alpha = mn == m[h] ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
-          l[h] *= alpha;
           m[h] = mn;
           // rescale O rows kg*4 + r by the alpha of those rows (held by lanes with that row)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float ar = __shfl(alpha, kg * 4 + r, 64);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[h][dt][r] *= ar;
+            for (int dt = 0; dt < 9; ++dt) o[h][dt][r] *= ar;
           }
         }
         // v_exp_f32 directly: arguments are at most kRescaleSlack and results below
         // 2^-126 weigh nothing. A row with no visible token yet (m = -inf, so every
         // z = -inf) subtracts 0 instead: its p are 0.
         const float m_s = m[h] == -INFINITY ? 0.f : m[h];
-        float rs = 0.f;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pz = __builtin_amdgcn_exp2f(sc[h][T][r] - m_s);
-            sc[h][T][r] = pz;
-            rs += pz;
-          }
-        l[h] += xor32_sum(xor16_sum(rs));
+          for (int r = 0; r < 4; ++r)
+            sc[h][T][r] = __builtin_amdgcn_exp2f(fmaf(sc[h][T][r], zs, -m_s));
       }
       // P as the A operand: k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}; each V
       // fragment serves every head
@@ -442,6 +453,11 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
           for (int h = 0; h < HPW; ++h)
             o[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h], vb, o[h][dt], 0, 0, 0);
         }
+        const bf16x8_t ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                               (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+        for (int h = 0; h < HPW; ++h)
+          o[h][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h], ones, o[h][8], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -458,8 +474,7 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
   for (int h = 0; h < HPW; ++h)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      // rows kg*4 + r need the l of those rows
-      const float lr = __shfl(l[h], kg * 4 + r, 64);
+      const float lr = o[h][8][r];  // l of query kg*4 + r
       const float inv = lr > 0.f ? 1.f / lr : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
