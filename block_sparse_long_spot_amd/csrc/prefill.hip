@@ -220,19 +220,17 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
 }
 
 // ---------------------------------------------------------------- attention
-constexpr int kKPad = 136;  // K tile row stride in bf16 (256 B + 16 B against conflicts)
 constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS at most)
 constexpr float kRescaleSlack = 8.f;   // log2 units a row maximum may grow unrescaled
 
-// A work-group stages one K/V block at a time for RT = HPW row tiles of 16 queries and
-// the G heads of a KV group: wave w takes heads g*G + (w % (G/HPW))*HPW .. +HPW-1 of row
-// tile w / (G/HPW). Every K or V fragment a wave reads from LDS feeds HPW MFMAs, so
-// with HPW = 2 the LDS reads per query and head halve (the LDS, not the matrix units,
-// bounds the one-head-per-wave form: each wave reads the whole 32 KiB block per block).
-// One head per wave holds 164 registers, three work-groups per CU at G = 4; two heads
-// per wave hold about 200, two work-groups per CU.
+// A work-group stages the selected K/V blocks one at a time for RT = HPW row tiles of 16
+// queries and the G heads of a KV group: wave w takes heads g*G + (w % (G/HPW))*HPW ..
+// +HPW-1 of row tile w / (G/HPW). Every K or V fragment a wave reads from LDS feeds HPW
+// MFMAs, so with HPW = 2 the LDS reads per query and head halve (each wave reads the
+// whole 32 KiB block per block). Two work-groups per CU (64 KiB of LDS each; about 140
+// registers with one head per wave, 216 with two).
 template <int G, int HPW>
-__global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefill_attn_kernel(
+__global__ __launch_bounds__(G * 64, G >= 4 ? 2 : 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, uint16_t* __restrict__ out, int Hq,
@@ -242,11 +240,12 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
   constexpr int RT = HPW;      // row tiles per work-group
   constexpr int HG = G / HPW;  // waves per row tile
   static_assert(G % HPW == 0, "heads per wave must divide the group");
-  // K and V tiles of the current block; after the last block, the output staging area
-  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * kBlk * kKPad];
-  uint16_t* const Ks = KVs;
-  uint16_t* const Vs = KVs + kBlk * kKPad;
-  static_assert(G * HPW * 16 * 128 <= 2 * kBlk * kKPad, "output staging must fit");
+  // Two block buffers, each a K tile and a V tile of 64 x 128 bf16 (unpadded, chunks
+  // swizzled); after the last block buffer A is the output staging area.
+  constexpr int TILE = kBlk * D;
+  __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * TILE];
+  static_assert(G * HPW * 16 * D <= 2 * TILE, "output staging must fit");
   extern __shared__ int32_t sel_s[];  // the selected list: K_max entries (launch size)
 
   // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin by linear id, so
@@ -323,42 +322,36 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
     }
     return cnt;
   };
-  // K and V of one block pass through registers (kbuf, vbuf) on their way to LDS, so
-  // the next block's loads are in flight while the current one is consumed. The loads
-  // are cached ones: the row work-groups of a tile read the same blocks, and adjacent
-  // tiles share their recency blocks, so most of them hit in L2 (measured: half the
-  // HBM fetch of non-temporal loads, 4 % faster).
-  constexpr int CPT = kBlk * (D / 8) / NT;  // 16-byte chunks per thread per tensor
-  u32x4_t kbuf[CPT], vbuf[CPT];
-  auto fetch = [&](int blk) {
+  // K and V reach LDS by direct global-to-LDS loads (global_load_lds_dwordx4: each lane
+  // fetches 16 bytes into its slot of a 1 KiB run), so no registers hold a block in
+  // flight. The next block is loaded into one buffer while the other is consumed; one
+  // barrier per block both publishes the loaded block and frees the consumed one. The
+  // loads are cached ones: the row work-groups of a tile read the same blocks, and
+  // adjacent tiles share their recency blocks, so most of them hit in L2.
+  //
+  // Swizzle: 16-byte chunk c of tile row r sits at chunk c ^ swz(r) of that row, so the
+  // 16 rows of a K fragment read and the 8 rows of each half of a transposing V read
+  // fall in distinct banks.
+  auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
+  const int ksw = swz(row);                // K fragment rows T*16 + row
+  const int vsw = swz(4 * kg + row / 4);   // V rows 32s + 4kg + row/4 (and 16 later)
+  auto load_block = [&](uint16_t* slot, int blk) {
     const int t0 = blk * kBlk;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      const int tok = min(t0 + t, L - 1);
-      kbuf[i] = *reinterpret_cast<const u32x4_t*>(Kg + (size_t)tok * D + d0);
-      vbuf[i] = *reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + d0);
+    for (int n = 0; n < 16 / G; ++n) {
+      const int piece = wave * (16 / G) + n;  // 1 KiB run: tile rows 4*piece .. +3
+      const int ch = piece * 64 + lane;       // the LDS chunk this lane fills
+      const int r = ch >> 4, c = (ch & 15) ^ swz(ch >> 4);
+      const size_t src = (size_t)min(t0 + r, L - 1) * D + c * 8;
+      __builtin_amdgcn_global_load_lds(
+          Kg + src, (__attribute__((address_space(3))) void*)(slot + piece * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          Vg + src, (__attribute__((address_space(3))) void*)(slot + TILE + piece * 512), 16,
+          0, 0);
     }
   };
-  auto stage = [&]() {  // K and V row-major
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int t = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4_t*>(&Ks[t * kKPad + d0]) = kbuf[i];
-      *reinterpret_cast<u32x4_t*>(&Vs[t * kKPad + d0]) = vbuf[i];
-    }
-  };
-  int blk = 0;
-  int j = next_block(0, blk);
-  if (j < cnt) fetch(blk);
-  while (j < cnt) {  // j and blk are uniform across the work-group
-    stage();
-    __syncthreads();
-    int blk_next = 0;
-    const int jn = next_block(j + 1, blk_next);
-    if (jn < cnt) fetch(blk_next);
+  auto consume = [&](const uint16_t* Ks, int blk) {
+    const uint16_t* Vs = Ks + TILE;
     const int t0 = blk * kBlk;
     if (active && t0 <= pos0 + q0 + 15) {  // some token visible to the wave's row tile
       // S'[token][query] for 4 tiles of 16 tokens; each K fragment serves every head
@@ -367,10 +360,10 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
       for (int T = 0; T < 4; ++T) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) sc[h][T] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* kp = &Ks[(T * 16 + row) * kKPad + kg * 8];
+        const uint16_t* kp = Ks + (T * 16 + row) * D;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + ((kg + 4 * s) ^ ksw) * 8);
 #pragma unroll
           for (int h = 0; h < HPW; ++h)
             sc[h][T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[h][s], sc[h][T], 0, 0, 0);
@@ -446,9 +439,9 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
         for (int dt = 0; dt < 8; ++dt) {
           // lane `row` receives V[32s + 4kg + k][dt*16 + row], k = 0..3, then the same 16
           // tokens later: the token order of pa
-          const uint16_t* vp =
-              &Vs[(32 * s + 4 * kg + row / 4) * kKPad + dt * 16 + 4 * (row % 4)];
-          const bf16x8_t vb = lds_tr_b_operand(vp, kKPad);
+          const uint16_t* vp = Vs + (32 * s + 4 * kg + row / 4) * D +
+                               ((2 * dt + (row % 4) / 2) ^ vsw) * 8 + 4 * (row & 1);
+          const bf16x8_t vb = lds_tr_b_operand(vp, D);
 #pragma unroll
           for (int h = 0; h < HPW; ++h)
             o[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h], vb, o[h][dt], 0, 0, 0);
@@ -460,16 +453,31 @@ __global__ __launch_bounds__(G * 64, HPW == 2 ? 2 : (G == 4 ? 3 : 1)) void prefi
           o[h][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h], ones, o[h][8], 0, 0, 0);
       }
     }
+  };
+  // j: the list entry of the block in buffer A (or cnt when there is none)
+  int ba = 0, bb = 0;
+  int j = next_block(0, ba);
+  if (j < cnt) load_block(bufA, ba);
+  __syncthreads();
+  // Unrolled by two so that every LDS read names the buffer it reads (bufA or bufB) and
+  // the compiler need not wait for the other buffer's loads before it.
+  while (j < cnt) {
+    j = next_block(j + 1, bb);
+    if (j < cnt) load_block(bufB, bb);
+    consume(bufA, ba);
     __syncthreads();
-    j = jn;
-    blk = blk_next;
+    if (j >= cnt) break;
+    j = next_block(j + 1, ba);
+    if (j < cnt) load_block(bufA, ba);
+    consume(bufB, bb);
+    __syncthreads();
   }
   if (!active) return;
   // Normalise, round to bf16 and pass through LDS so that each lane stores whole 16-byte
   // pieces: a head's 16 x 128 output tile is one contiguous 4 KiB run of `out`. The
   // wave's staging region is its own, and every wave is past the loop's last barrier,
   // so no other wave still reads the K/V tiles.
-  uint16_t* const st = KVs + wave * (HPW * 16 * D);
+  uint16_t* const st = bufA + wave * (HPW * 16 * D);
 #pragma unroll
   for (int h = 0; h < HPW; ++h)
 #pragma unroll
@@ -552,8 +560,9 @@ hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v
 #define SPOT_PF(GG, HPW)                                                                    \
   do {                                                                                      \
     const dim3 grid(static_cast<unsigned>((units + 7) / 8 * 8 * ((n_rt + HPW - 1) / HPW))); \
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_attn_kernel<GG, HPW>), \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_list);    \
+    (void)hipFuncSetAttribute(                                                              \
+        reinterpret_cast<const void*>(&prefill_attn_kernel<GG, HPW>),                      \
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_list);                         \
     hipLaunchKernelGGL((prefill_attn_kernel<GG, HPW>), grid, dim3(GG * 64), lds_list,       \
                        stream, Qp, Kp, Vp, sel_idx, sel_cnt, K_max, Op, Hq, Hkv, T, Tq,      \
                        n_tiles, B * n_tiles, q_pos0, L, qscale);                            \
