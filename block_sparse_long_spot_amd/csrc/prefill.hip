@@ -11,14 +11,16 @@
 //
 // Attention: one work-group per (HPW row tiles of 16 queries, tile, KV head), G waves;
 // each wave computes HPW query heads of one row tile, so the G heads of a KV group share
-// every K/V block the work-group stages in LDS (K and V row-major, 16-byte writes), and
-// each fragment a wave reads back from LDS feeds its HPW heads. Per selected block:
+// every K/V block the work-group stages in LDS (row-major, by direct global-to-LDS
+// loads, double-buffered), and each fragment a wave reads back from LDS feeds its HPW
+// heads. Per selected block:
 //   S' = K . Q^T   (tokens x queries; A = K from LDS, B = Q from registers)
-// whose accumulator layout gives each lane 8 scores of one query row. Those become,
+// whose accumulator layout gives each lane 16 scores of one query row. Those become,
 // after the online softmax and a bf16 conversion, the A operand of
 //   O += P . V     (B = V read with gfx950's transposing LDS load, ds_read_b64_tr_b16,
 //                   in the same token order),
-// so P never leaves registers. Causal and L masks are applied per element.
+// so P never leaves registers; P times a column of ones gives the row sums. Causal and
+// L masks are applied per element, only on blocks that cross a row tile's diagonal.
 #include "device_common.h"
 #include "spot_internal.h"
 
