@@ -224,29 +224,32 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
 // ---------------------------------------------------------------- attention
 constexpr int kMaxPrefillList = 8192;  // longest selected list (32 KiB of LDS at most)
 constexpr float kRescaleSlack = 8.f;   // log2 units a row maximum may grow unrescaled
+constexpr long kSplitMaxWg = 256;      // one-head grids up to this size split each list in two
 
 // A work-group stages the selected K/V blocks one at a time for RT = HPW row tiles of 16
-// queries and the G heads of a KV group: wave w takes heads g*G + (w % (G/HPW))*HPW ..
-// +HPW-1 of row tile w / (G/HPW). Every K or V fragment a wave reads from LDS feeds HPW
-// MFMAs, so with HPW = 2 the LDS reads per query and head halve (each wave reads the
-// whole 32 KiB block per block). Two work-groups per CU (64 KiB of LDS each; about 140
-// registers with one head per wave, 216 with two).
-template <int G, int HPW>
-__global__ __launch_bounds__(G * 64, G >= 4 ? 2 : 1) void prefill_attn_kernel(
+// queries and the G heads of a KV group: wave w of a group of G waves takes heads
+// g*G + (w % (G/HPW))*HPW .. +HPW-1 of row tile w / (G/HPW). Every K or V fragment a wave
+// reads from LDS feeds HPW MFMAs, so with HPW = 2 the LDS reads per query and head halve
+// (each wave reads the whole 32 KiB block per block). Two work-groups per CU (64 KiB of
+// LDS each; about 140 registers with one head per wave, 216 with two). With S = 2 wave
+// groups, the groups take alternate blocks of the list and merge their partial softmaxes
+// at the end (for grids too small to fill the CUs).
+template <int G, int HPW, int S>
+__global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, uint16_t* __restrict__ out, int Hq,
     int Hkv, int T, int Tq, int n_tiles, int B_rows, int q_pos0, int L, float qscale) {
   constexpr int D = 128;
-  constexpr int NT = G * 64;
+  constexpr int NT = G * S * 64;
   constexpr int RT = HPW;      // row tiles per work-group
   constexpr int HG = G / HPW;  // waves per row tile
   static_assert(G % HPW == 0, "heads per wave must divide the group");
   // Two block buffers, each a K tile and a V tile of 64 x 128 bf16 (unpadded, chunks
   // swizzled); after the last block buffer A is the output staging area.
   constexpr int TILE = kBlk * D;
-  __shared__ __attribute__((aligned(16))) uint16_t bufA[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t bufB[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t bufA[S * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t bufB[S * 2 * TILE];
   static_assert(G * HPW * 16 * D <= 2 * TILE, "output staging must fit");
   extern __shared__ int32_t sel_s[];  // the selected list: K_max entries (launch size)
 
@@ -269,8 +272,9 @@ __global__ __launch_bounds__(G * 64, G >= 4 ? 2 : 1) void prefill_attn_kernel(
   // from it (heads, row tile, the per-block full/masked choice) is wave-uniform and
   // branches on it instead of evaluating both sides under a lane mask
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h0 = g * G + (wave % HG) * HPW;         // first head of this wave
-  const int q0 = qg0 + (wave / HG) * 16;            // its row tile
+  const int gw = wave % G, split = wave / G;       // wave in its group; the group
+  const int h0 = g * G + (gw % HG) * HPW;           // first head of this wave
+  const int q0 = qg0 + (gw / HG) * 16;              // its row tile
   const bool active = q0 < Tq_t;                    // uniform per wave
   const int row = lane & 15, kg = lane >> 4;
   const int my_q = q0 + row;                // query row this lane's softmax state tracks
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(G * 64, G >= 4 ? 2 : 1) void prefill_attn_kernel(
     const int t0 = blk * kBlk;
 #pragma unroll
     for (int n = 0; n < 16 / G; ++n) {
-      const int piece = wave * (16 / G) + n;  // 1 KiB run: tile rows 4*piece .. +3
+      const int piece = gw * (16 / G) + n;    // 1 KiB run: tile rows 4*piece .. +3
       const int ch = piece * 64 + lane;       // the LDS chunk this lane fills
       const int r = ch >> 4, c = (ch & 15) ^ swz(ch >> 4);
       const size_t src = (size_t)min(t0 + r, L - 1) * D + c * 8;
@@ -456,23 +460,70 @@ __global__ __launch_bounds__(G * 64, G >= 4 ? 2 : 1) void prefill_attn_kernel(
       }
     }
   };
-  // j: the list entry of the block in buffer A (or cnt when there is none)
-  int ba = 0, bb = 0;
-  int j = next_block(0, ba);
-  if (j < cnt) load_block(bufA, ba);
+  // Each set of S blocks (the next S of the list) goes to the S wave groups, one block
+  // each: group k loads and consumes entry k of the set in its own slot of the buffer.
+  int j = 0;
+  auto gather = [&](int (&bl)[S]) {
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      int blk = 0;
+      const int jj = next_block(j, blk);
+      bl[k] = jj < cnt ? blk : -1;
+      any = any || jj < cnt;
+      j = jj < cnt ? jj + 1 : cnt;
+    }
+    return any;
+  };
+  int ba[S], bb[S];
+  bool has_a = gather(ba);
+  if (ba[split] >= 0) load_block(bufA + split * 2 * TILE, ba[split]);
   __syncthreads();
   // Unrolled by two so that every LDS read names the buffer it reads (bufA or bufB) and
   // the compiler need not wait for the other buffer's loads before it.
-  while (j < cnt) {
-    j = next_block(j + 1, bb);
-    if (j < cnt) load_block(bufB, bb);
-    consume(bufA, ba);
+  while (has_a) {
+    const bool has_b = gather(bb);
+    if (bb[split] >= 0) load_block(bufB + split * 2 * TILE, bb[split]);
+    if (ba[split] >= 0) consume(bufA + split * 2 * TILE, ba[split]);
     __syncthreads();
-    if (j >= cnt) break;
-    j = next_block(j + 1, ba);
-    if (j < cnt) load_block(bufA, ba);
-    consume(bufB, bb);
+    if (!has_b) break;
+    has_a = gather(ba);
+    if (ba[split] >= 0) load_block(bufA + split * 2 * TILE, ba[split]);
+    if (bb[split] >= 0) consume(bufB + split * 2 * TILE, bb[split]);
     __syncthreads();
+  }
+  if constexpr (S == 2) {
+    // group 1 hands (m, O, l) to group 0 through buffer B, lane for lane; group 0 merges
+    // the two partial softmaxes on the larger reference maximum
+    constexpr int NV = HPW * 37;  // floats per lane: m, then 9 tiles x 4
+    float* xch = reinterpret_cast<float*>(bufB) + gw * NV * 64 + lane;
+    static_assert(G * NV * 64 * 4 <= S * 2 * TILE * 2, "exchange must fit");
+    if (split == 1) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        xch[(h * 37) * 64] = m[h];
+#pragma unroll
+        for (int dt = 0; dt < 9; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xch[(h * 37 + 1 + dt * 4 + r) * 64] = o[h][dt][r];
+      }
+    }
+    __syncthreads();
+    if (split == 1) return;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      const float m1 = xch[(h * 37) * 64];
+      const float mn = fmaxf(m[h], m1);
+      const float a0 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+      const float a1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar0 = __shfl(a0, kg * 4 + r, 64), ar1 = __shfl(a1, kg * 4 + r, 64);
+#pragma unroll
+        for (int dt = 0; dt < 9; ++dt)
+          o[h][dt][r] = o[h][dt][r] * ar0 + xch[(h * 37 + 1 + dt * 4 + r) * 64] * ar1;
+      }
+    }
   }
   if (!active) return;
   // Normalise, round to bf16 and pass through LDS so that each lane stores whole 16-byte
@@ -559,30 +610,34 @@ hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v
   const uint16_t* Vp = static_cast<const uint16_t*>(v_cache);
   uint16_t* Op = static_cast<uint16_t*>(out);
   // grid: units in groups of 8 (one per XCD) x groups of HPW row tiles
-#define SPOT_PF(GG, HPW)                                                                    \
+#define SPOT_PF(GG, HPW, SS)                                                                \
   do {                                                                                      \
     const dim3 grid(static_cast<unsigned>((units + 7) / 8 * 8 * ((n_rt + HPW - 1) / HPW))); \
     (void)hipFuncSetAttribute(                                                              \
-        reinterpret_cast<const void*>(&prefill_attn_kernel<GG, HPW>),                      \
+        reinterpret_cast<const void*>(&prefill_attn_kernel<GG, HPW, SS>),                  \
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_list);                         \
-    hipLaunchKernelGGL((prefill_attn_kernel<GG, HPW>), grid, dim3(GG * 64), lds_list,       \
-                       stream, Qp, Kp, Vp, sel_idx, sel_cnt, K_max, Op, Hq, Hkv, T, Tq,      \
-                       n_tiles, B * n_tiles, q_pos0, L, qscale);                            \
+    hipLaunchKernelGGL((prefill_attn_kernel<GG, HPW, SS>), grid, dim3(GG * SS * 64),        \
+                       lds_list, stream, Qp, Kp, Vp, sel_idx, sel_cnt, K_max, Op, Hq, Hkv, T, \
+                       Tq, n_tiles, B * n_tiles, q_pos0, L, qscale);                        \
   } while (0)
   // Two heads per wave (half the LDS reads per head) pay once the one-head grid has
   // work-groups to spare -- at least 1024, four per CU -- and the row tiles pair up
   // (an odd count leaves one wave of the last pair idle). Measured on the 32/8-head,
   // 128-query-tile layer: 10-20 % faster from 1024 work-groups up, 8 % slower at 512
-  // and 40 % slower for a lone tile.
+  // and 40 % slower for a lone tile. A grid that fits the CUs once over (one work-group
+  // each) instead splits every list between two wave groups per work-group, which halves
+  // the chain of blocks each wave runs (a lone 128-query tile: 3 % faster, 256
+  // work-groups: 7 %; at 512 work-groups, 128 KiB of LDS per work-group costs more).
   const bool two_heads = G == 4 && (n_rt % 2 == 0 || n_rt >= 7) && units * n_rt >= 1024;
   switch (G) {
-    case 1: SPOT_PF(1, 1); break;
-    case 2: SPOT_PF(2, 1); break;
+    case 1: SPOT_PF(1, 1, 1); break;
+    case 2: SPOT_PF(2, 1, 1); break;
     case 4:
-      if (two_heads) SPOT_PF(4, 2);
-      else SPOT_PF(4, 1);
+      if (two_heads) SPOT_PF(4, 2, 1);
+      else if (units * n_rt <= kSplitMaxWg) SPOT_PF(4, 1, 2);
+      else SPOT_PF(4, 1, 1);
       break;
-    default: SPOT_PF(8, 1); break;
+    default: SPOT_PF(8, 1, 1); break;
   }
 #undef SPOT_PF
   return hipGetLastError();
