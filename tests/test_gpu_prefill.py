@@ -270,6 +270,12 @@ def test_prefill_sequence_two_heads_per_wave_ragged():
                    K_min=8, seed=34, tiles_checked=(0, 16, 31), heads_checked=(0, 1, 6, 7, 30))
 
 
+def test_prefill_sequence_mid_grid():
+    """512 one-head work-groups (between the split-list and two-heads-per-wave forms)."""
+    _sequence_case(B=1, T=1000, Tq=128, q_pos0=0, Hq=32, Hkv=8, p=0.9, n_sink=1, n_rec=4,
+                   K_min=4, seed=35, tiles_checked=(0, 3, 7), heads_checked=(0, 5, 31))
+
+
 def test_prefill_sequence_32k():
     """A whole 32K prefill (256 tiles of 128, the c5 layer shape), sampled tiles."""
     _sequence_case(B=1, T=32768, Tq=128, q_pos0=0, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
