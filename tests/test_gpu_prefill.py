@@ -156,6 +156,28 @@ def test_prefill_attn_parity(case):
     assert_out_close(np64(out), ref, torch.bfloat16, tag=str(case))
 
 
+@pytest.mark.parametrize("scale", [-1 / math.sqrt(128), 0.0, 0.5])
+def test_prefill_attn_scale_sign_and_zero(scale):
+    """The softmax scale is folded into the exponential: a negative scale (the kernel
+    negates q instead), a zero scale (uniform weights over the visible tokens) and a
+    large one, on a diagonal tile with a ragged end."""
+    B, Hq, Hkv, Tq, q_pos0, L = 1, 8, 2, 40, 300, 340
+    log(f"prefill attn scale {scale}")
+    g = torch.Generator().manual_seed(77)
+    Q = torch.randn(B, Hq, Tq, 128, generator=g).bfloat16()
+    K = torch.randn(B, Hkv, L, 128, generator=g).bfloat16()
+    V = torch.randn(B, Hkv, L, 128, generator=g).bfloat16()
+    sets = [[0, 2, 4, 5]]
+    idx = torch.tensor([sets[0]], dtype=torch.int32)
+    cnt = torch.tensor([4], dtype=torch.int32)
+    out = torch.full((B, Hq, Tq, 128), float("nan"), device=DEV).bfloat16()
+    _lib.spot_prefill_attn(Q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), cnt.to(DEV), out, q_pos0,
+                           scale)
+    torch.cuda.synchronize()
+    ref = O.prefill_attention(np64(Q), np64(K), np64(V), sets, 64, scale, q_pos0)
+    assert_out_close(np64(out), ref, torch.bfloat16, tag=f"scale {scale}")
+
+
 def test_prefill_tile_end_to_end():
     """The 128-query tile at positions 32640..32767 of a 32K context."""
     wl = W.WORKLOADS["c5_prefill_32k"]
