@@ -314,6 +314,33 @@ def static_topk_leg(inp, wl, steps, warmup, stream):
             "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in per.items()}}
 
 
+def budgets_vary_leg(wl, steps, warmup, stream):
+    """The 128K batch-8 layer with the Zipf exponent of each batch row spread over
+    [1.3, 2.0], so the p = 0.95 nucleus (and the selected set) differs from row to row
+    instead of every row hitting the K_max cap: the case top-p exists for. Reports the
+    step, the attention call and the per-row block counts."""
+    ws = wl.with_(zipf_spread=(1.3, 2.0))
+    inp = W.make_inputs(ws, device="cuda")
+    bufs = DecodeBuffers(ws.B, ws.nb, ws.Hq, ws.d, ws.K_max, inp["q"].dtype)
+    us, _ = time_back_to_back(lambda: decode_step(inp, ws, bufs, stream=stream), steps,
+                              warmup, stream)
+    scale = 1.0 / math.sqrt(ws.d)
+    attn_us, _ = time_back_to_back(
+        lambda: spot.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx,
+                                      bufs.sel_cnt, bufs.out, bufs.workspace, scale,
+                                      block=ws.block, stream=stream), steps, warmup, stream)
+    tok = selected_tokens(bufs.sel_idx, bufs.sel_cnt, ws.L, ws.block)
+    bb = byte_budget(ws, ws.B, tok)
+    res = {"zipf_exponents": [1.3, 2.0], "selected_blocks": bufs.sel_cnt.tolist(),
+           "us_per_step": round(us, 3), "algorithmic_bytes": bb["step"],
+           "GBps": round(bb["step"] / (us * 1e-6) / 1e9, 1),
+           "attn_call_us": round(attn_us, 3),
+           "attn_GBps": round(bb["attn"] / (attn_us * 1e-6) / 1e9, 1)}
+    del inp, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def page_geometry_step(steps, warmup, stream):
     """A whole decode step at the paper's own geometry and inference settings (Appendix
     A, Table 3): 16-token blocks, one selector key per token (4 heads x 128), sink 128
@@ -610,6 +637,8 @@ def main():
             "score_GBps": round(b4["score"] / (statistics.fmean(p4["score"]) * 1e-6) / 1e9, 1)}
         del inp4, bufs4
         torch.cuda.empty_cache()
+        log("bench: budgets that vary across the batch")
+        result["budgets_vary"] = budgets_vary_leg(wl, a.steps, a.warmup, stream)
         inp = W.make_inputs(wl, device="cuda") if not a.no_cpu_baseline else None
     if a.prefill:
         log("bench: prefill tile")

@@ -1,14 +1,17 @@
 // Decode attention over the selected KV blocks (SpotAttention §2.3: the layer attends
 // only to keys in blocks of S_q, one S_q per query shared by every head).
 //
-// Split-K: the selected-block list of one (query, KV head) "unit" is cut into runs; a
-// work-group reduces one run with an online softmax for the G query heads that share
-// the KV head (GQA) and stores (m, l, acc) per head; runs past the end of the list
-// store an empty marker. The MFMA path cuts runs from each row's actual count, so a
-// list far shorter than K_max still spreads over every work-group. attn_combine then merges the runs of every
-// (query, head) in run order (deterministic). Merging across work-groups inside one
-// kernel would need an agent-scope release/acquire per work-group, which on this
-// multi-XCD part is an L2 writeback plus invalidate; a second small kernel is cheaper.
+// Split-K: the selected-block lists are cut into runs; a work-group reduces one run with
+// an online softmax for the G query heads that share a KV head (GQA) and stores
+// (m, l, acc) per head in a slot of that query. The MFMA path at batch 2..64 cuts the
+// lists of all queries, concatenated, into equal runs (a run may end one query's list
+// and start the next one's, one partial each), so queries that select very different
+// numbers of blocks still keep every work-group equally busy; otherwise each
+// (query, KV head) gets the same number of runs, cut from that query's own count (runs
+// past its end store an empty partial). attn_combine then merges the slots of every
+// (query, head) in order (deterministic). Merging across work-groups inside one kernel
+// would need an agent-scope release/acquire per work-group, which on this multi-XCD
+// part is an L2 writeback plus invalidate; a second small kernel is cheaper.
 //
 // Block sizes 16, 32, 64 and 128 tokens. The unit of work of a wave is a 64-token
 // chunk made of four 16-token tiles, each with its own start token: the four tiles of
@@ -40,6 +43,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 64;  // tokens a wave consumes at a time (four 16-token tiles)
+constexpr int kFlatMaxB = 64;  // batches up to this size cut runs across queries
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f(x); }
@@ -52,25 +56,39 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 
 // The run result of this work-group (per head: max m, sum l, unnormalised acc[D]) is
 // in LDS: stored as the run's partial result for attn_combine.
+// A partial result (m, l, acc) per head. `last` marks a head's last partial: its l is
+// stored as -l - 1 (a real l is >= 0), and the merge stops after it.
 template <int D, int G, int NT>
 __device__ void store_run(const float (&racc)[G][D], const float (&rm)[G], const float (&rl)[G],
-                          int b, int g, int split, int Hq, int nsplit,
-                          float* __restrict__ ws_acc, float2* __restrict__ ws_ml) {
+                          size_t base, int nslot, float* __restrict__ ws_acc,
+                          float2* __restrict__ ws_ml, bool last = false) {
   for (int o = threadIdx.x; o < G * D; o += NT) {
     const int h = o / D, dd = o % D;
-    const size_t idx = ((size_t)b * Hq + g * G + h) * nsplit + split;
+    const size_t idx = base + (size_t)h * nslot;
     ws_acc[idx * D + dd] = racc[h][dd];
-    if (dd == 0) ws_ml[idx] = make_float2(rm[h], rl[h]);
+    if (dd == 0) ws_ml[idx] = make_float2(rm[h], last ? -rl[h] - 1.f : rl[h]);
   }
 }
 
-// A run past the end of its unit's list: an empty partial (m = -inf, l = 0), so the
-// merge reads every run slot without looking at the selection count.
-template <int G, int NT>
-__device__ void store_empty_run(int b, int g, int split, int Hq, int nsplit,
-                                float2* __restrict__ ws_ml) {
+// Partial-result slots: head hq of query b owns nslot consecutive slots from
+// (b * Hq + hq) * nslot; a work-group writes slot `slot` of its G heads, so `base` is
+// (b * Hq + g * G) * nslot + slot and head h of the group is base + h * nslot.
+__host__ __device__ inline size_t slot_base(int b, int g, int G, int Hq, int nslot, int slot) {
+  return ((size_t)b * Hq + (size_t)g * G) * nslot + slot;
+}
+
+// A run with nothing to merge: an empty partial (m = -inf, l = 0).
+template <int G>
+__device__ void store_empty_run(size_t base, int nslot, float2* __restrict__ ws_ml) {
   if (threadIdx.x < G)
-    ws_ml[((size_t)b * Hq + g * G + threadIdx.x) * nsplit + split] = make_float2(-INFINITY, 0.f);
+    ws_ml[base + (size_t)threadIdx.x * nslot] = make_float2(-INFINITY, 0.f);
+}
+
+// An empty last partial (m = -inf, l = 0 stored as -1) for a query with no entry.
+template <int G>
+__device__ void store_end_marker(size_t base, int nslot, float2* __restrict__ ws_ml) {
+  if (threadIdx.x < G)
+    ws_ml[base + (size_t)threadIdx.x * nslot] = make_float2(-INFINITY, -1.f);
 }
 
 // ---------------------------------------------------------------- generic pass 1
@@ -85,7 +103,7 @@ __global__ __launch_bounds__(64) void attn_generic(
   const int cnt = min(max(sel_cnt[b], 0), K_max);
   const int j0 = split * bps;
   if (j0 >= cnt) {
-    store_empty_run<G, 64>(b, g, split, Hq, nsplit, ws_ml);
+    store_empty_run<G>(slot_base(b, g, G, Hq, nsplit, split), nsplit, ws_ml);
     return;
   }
   const int j1 = min(j0 + bps, cnt);
@@ -167,16 +185,18 @@ __global__ __launch_bounds__(64) void attn_generic(
     }
   }
   __syncthreads();
-  store_run<D, G, 64>(racc, rm, rl, b, g, split, Hq, nsplit, ws_acc, ws_ml);
+  store_run<D, G, 64>(racc, rm, rl, slot_base(b, g, G, Hq, nsplit, split), nsplit, ws_acc,
+                      ws_ml);
 }
 
 // ---------------------------------------------------------------- MFMA pass 1 (bf16)
-template <int D, int G, int NW, int BS>
+template <int D, int G, int NW, int BS, bool FLAT>
 __global__ __launch_bounds__(NW * 64) void attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ sel_idx,
     const int32_t* __restrict__ sel_cnt, int K_max, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml, int Hq, int Hkv, int L, float qscale, int bps, int nsplit) {
+    float2* __restrict__ ws_ml, int Hq, int Hkv, int L, float qscale, int bps, int nsplit,
+    int B, int nslot) {
   constexpr int KS = D / 32;   // MFMA k-steps over the head dim in q.K^T
   constexpr int NT = D / 16;   // 16-dim output tiles of P.V
   constexpr int DC = D / 8;    // lanes covering one V row (8 dims each) in the V loads
@@ -190,19 +210,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   static_assert(BS == 16 || BS == 32 || BS == 64 || BS == 128, "block of 16 to 128 tokens");
   static_assert(16 % TG == 0, "the rows of one V load lie in one tile");
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int cnt = min(max(sel_cnt[b], 0), K_max);
-  // Runs are cut from this row's actual count, spread over all nsplit work-groups
-  // (whole chunks for small blocks); `bps` is the split plan's maximum, sized for
-  // K_max, and cnt <= K_max keeps every run within it.
-  int run = (cnt + nsplit - 1) / nsplit;
-  run = min((run + EPC - 1) / EPC * EPC, bps);
-  const int j0 = split * run;
-  if (j0 >= cnt) {
-    store_empty_run<G, NW * 64>(b, g, split, Hq, nsplit, ws_ml);
-    return;
-  }
-  const int j1 = min(j0 + run, cnt);
+  const int g = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;  // MFMA operand coordinates
   const int dc = lane % DC, tg = lane / DC;   // V load coordinates
@@ -210,269 +218,371 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NW][kChunk * VP];
   __shared__ float mm[NW][G], ll[NW][G];
   __shared__ float accs[NW][G][D];
-
-  // B operand of S' = K.Q^T: column = query head of the group (zero beyond G), k = head dim
-  bf16x8_t qb[KS];
-  {
-    const bool hv = row < G;
-    const uint16_t* qp = q + ((size_t)b * Hq + g * G + (hv ? row : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + s * 32 + kg * 8);
-      if (!hv) v = bf16x8_t{};
-      qb[s] = v;
-    }
-  }
-  float m = -INFINITY, l = 0.f;  // online-softmax state of head `row`
-  floatx4_t o[NT];               // o[dt][r] = O[head 4kg + r][dim 16dt + row]
-#pragma unroll
-  for (int dt = 0; dt < NT; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nbl = (L + BS - 1) / BS;
-  const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
-  const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
-  const int n_ent = j1 - j0;
-  const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
-  const int n_mine = (n_chunks - wave + NW - 1) / NW;
-  // This wave's chunks are wave + i*NW. The list entries they use are read once, one
-  // per lane (at most 64 per wave; the split plan keeps runs within that), so a
-  // chunk's tile starts are register reads, not loads on the critical path.
-  //   BS >= 64: lane i holds the entry of chunk i;
-  //   BS <  64: lane i*EPC + u holds entry u of chunk i.
-  int my_blk = -1;
-  {
-    const int i = lane / EPC, u = lane % EPC;
-    const int e_rel = BS >= kChunk ? (wave + i * NW) / CPE : (wave + i * NW) * EPC + u;
-    if (i < n_mine && e_rel < n_ent) {
-      const int e = sel_idx[(size_t)b * K_max + j0 + e_rel];
-      my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
-    }
-  }
-  // first token of each 16-token tile of chunk i, or -1 for a tile with no block
-  auto tile_starts = [&](int i, int (&st)[4]) {
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      if constexpr (BS >= kChunk) {
-        const int blk = __builtin_amdgcn_readlane(my_blk, i);
-        const int off = ((wave + i * NW) % CPE) * kChunk + T * 16;
-        st[T] = blk < 0 ? -1 : blk * BS + off;
-      } else {
-        const int blk = __builtin_amdgcn_readlane(my_blk, i * EPC + T / TPB);
-        st[T] = blk < 0 ? -1 : blk * BS + (T % TPB) * 16;
-      }
-    }
-  };
-  // a chunk with no token below L is skipped (its scores would all be -inf)
-  auto any_token = [&](const int (&st)[4]) {
-    bool a = false;
-#pragma unroll
-    for (int T = 0; T < 4; ++T) a = a || (st[T] >= 0 && st[T] < L);
-    return a;
-  };
-  // K rows of a chunk in the A-operand layout: lane (token row, k-group kg)
-  auto load_k = [&](const int (&st)[4], bf16x8_t (&kb)[4][KS]) {
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const int tok = st[T] < 0 ? 0 : min(st[T] + row, L - 1);
-      const uint16_t* kp = Kg + (size_t)tok * D + kg * 8;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kb[T][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kp + s * 32));
-    }
-  };
-  // V rows of a chunk: lane (dim chunk dc, row group tg), whole rows per instruction
-  auto load_v = [&](const int (&st)[4], u32x4_t (&vv)[TPL]) {
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const int T = (i * TG) / 16;
-      const int tok = st[T] < 0 ? 0 : min(st[T] + (i * TG) % 16 + tg, L - 1);
-      vv[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + dc * 8));
-    }
-  };
-  uint16_t* const vs = Vs[wave];
-  auto consume = [&](const int (&st)[4], const bf16x8_t (&kb)[4][KS],
-                     const u32x4_t (&vv)[TPL]) {
-    // the chunk's V rows to this wave's LDS tile, row t = chunk token t
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-      *reinterpret_cast<u32x4_t*>(&vs[(i * TG + tg) * VP + dc * 8]) = vv[i];
-    // S'[token][head] for the 4 tiles: sc[T][r] = S'[chunk token 16T + 4kg + r][head row]
-    floatx4_t sc[4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      floatx4_t a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[T][s], qb[s], a, 0, 0, 0);
-      sc[T] = a;
-    }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool tv = st[T] >= 0 && st[T] + 4 * kg + r < L;
-        const float z = tv ? sc[T][r] * qscale : -INFINITY;
-        sc[T][r] = z;
-        bm = fmaxf(bm, z);
-      }
-    bm = xor32_max(xor16_max(bm));
-    // the chunk has a token below L, so bm and mn are finite; alpha = 0 on the first chunk.
-    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 weigh nothing.
-    const float mn = fmaxf(m, bm);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float rs = 0.f;
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sc[T][r] - mn);
-        sc[T][r] = p;
-        rs += p;
-      }
-    rs = xor32_sum(xor16_sum(rs));
-    l = l * alpha + rs;
-    m = mn;
-    // rescale O rows 4kg + r by their head's alpha, held by lane 4kg + r (rows >= G
-    // are padding and take any finite factor)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float ar = readlane_f(alpha, r);
-      if constexpr (G > 4) ar = kg == 1 ? readlane_f(alpha, 4 + r) : ar;
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) o[dt][r] *= ar;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O += P.V: A = P (k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}, in bf16),
-    // B = V from the transposing LDS read in the same token order
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8_t pa = {(__bf16)sc[2 * s][0],     (__bf16)sc[2 * s][1],
-                           (__bf16)sc[2 * s][2],     (__bf16)sc[2 * s][3],
-                           (__bf16)sc[2 * s + 1][0], (__bf16)sc[2 * s + 1][1],
-                           (__bf16)sc[2 * s + 1][2], (__bf16)sc[2 * s + 1][3]};
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) {
-        // lane `row` receives V[32s + 4kg + k][16dt + row], k = 0..3, then the same 16
-        // tokens later: the token order of pa
-        const uint16_t* vp = &vs[(32 * s + 4 * kg + row / 4) * VP + dt * 16 + 4 * (row % 4)];
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, lds_tr_b_operand(vp, VP), o[dt],
-                                                        0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-
-  // Software pipeline over this wave's chunks: the next chunk's K loads are in flight
-  // while the current chunk is consumed.
-  int st[4] = {-1, -1, -1, -1};
-  bf16x8_t kb[4][KS];
-  if (n_mine > 0) {
-    tile_starts(0, st);
-    load_k(st, kb);
-  }
-  for (int i = 0; i < n_mine; ++i) {
-    u32x4_t vv[TPL];
-    load_v(st, vv);
-    int stn[4] = {-1, -1, -1, -1};
-    bf16x8_t kn[4][KS];
-    if (i + 1 < n_mine) {
-      tile_starts(i + 1, stn);
-      load_k(stn, kn);
-    }
-    if (any_token(st)) consume(st, kb, vv);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      st[T] = stn[T];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
-    }
-  }
-
-  // this wave's state to LDS: heads h < G (O row h lives in lanes kg = h / 4, r = h % 4)
-  if (lane < G) {
-    mm[wave][lane] = m;
-    ll[wave][lane] = l;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * kg + r;
-    if (h < G) {
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) accs[wave][h][dt * 16 + row] = o[dt][r];
-    }
-  }
-  __syncthreads();
-  // merge the waves of this work-group into the run result
   __shared__ float racc[G][D];
   __shared__ float rm[G], rl[G];
-  for (int oi = threadIdx.x; oi < G * D; oi += NW * 64) {
-    const int h = oi / D, dd = oi % D;
-    float M = -INFINITY;
+
+  // Entries [j0, j1) of query b's list (j0 < j1), reduced into slot `slot` of its heads;
+  // `last`: no later slot of this query holds a partial.
+  auto run_entries = [&](int b, int j0, int j1, int slot, bool last) {
+    // B operand of S' = K.Q^T: column = query head of the group (zero beyond G), k = head dim
+    bf16x8_t qb[KS];
+    {
+      const bool hv = row < G;
+      const uint16_t* qp = q + ((size_t)b * Hq + g * G + (hv ? row : 0)) * D;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w][h]);
-    float ls = 0.f, a = 0.f;
+      for (int s = 0; s < KS; ++s) {
+        bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + s * 32 + kg * 8);
+        if (!hv) v = bf16x8_t{};
+        qb[s] = v;
+      }
+    }
+    float m = -INFINITY, l = 0.f;  // online-softmax state of head `row`
+    floatx4_t o[NT];               // o[dt][r] = O[head 4kg + r][dim 16dt + row]
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sc = mm[w][h] == -INFINITY ? 0.f : exp2f(mm[w][h] - M);
-      ls += sc * ll[w][h];
-      a += sc * accs[w][h][dd];
+    for (int dt = 0; dt < NT; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nbl = (L + BS - 1) / BS;
+    const uint16_t* Kg = Kc + ((size_t)b * Hkv + g) * (size_t)L * D;
+    const uint16_t* Vg = Vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+    const int n_ent = j1 - j0;
+    const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
+    const int n_mine = (n_chunks - wave + NW - 1) / NW;
+    // This wave's chunks are wave + i*NW. The list entries they use are read once, one
+    // per lane (at most 64 per wave; the split plan keeps runs within that), so a
+    // chunk's tile starts are register reads, not loads on the critical path.
+    //   BS >= 64: lane i holds the entry of chunk i;
+    //   BS <  64: lane i*EPC + u holds entry u of chunk i.
+    int my_blk = -1;
+    {
+      const int i = lane / EPC, u = lane % EPC;
+      const int e_rel = BS >= kChunk ? (wave + i * NW) / CPE : (wave + i * NW) * EPC + u;
+      if (i < n_mine && e_rel < n_ent) {
+        const int e = sel_idx[(size_t)b * K_max + j0 + e_rel];
+        my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
+      }
     }
-    racc[h][dd] = a;
-    if (dd == 0) {
-      rm[h] = M;
-      rl[h] = ls;
+    // first token of each 16-token tile of chunk i, or -1 for a tile with no block
+    auto tile_starts = [&](int i, int (&st)[4]) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        if constexpr (BS >= kChunk) {
+          const int blk = __builtin_amdgcn_readlane(my_blk, i);
+          const int off = ((wave + i * NW) % CPE) * kChunk + T * 16;
+          st[T] = blk < 0 ? -1 : blk * BS + off;
+        } else {
+          const int blk = __builtin_amdgcn_readlane(my_blk, i * EPC + T / TPB);
+          st[T] = blk < 0 ? -1 : blk * BS + (T % TPB) * 16;
+        }
+      }
+    };
+    // a chunk with no token below L is skipped (its scores would all be -inf)
+    auto any_token = [&](const int (&st)[4]) {
+      bool a = false;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) a = a || (st[T] >= 0 && st[T] < L);
+      return a;
+    };
+    // K rows of a chunk in the A-operand layout: lane (token row, k-group kg)
+    auto load_k = [&](const int (&st)[4], bf16x8_t (&kb)[4][KS]) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const int tok = st[T] < 0 ? 0 : min(st[T] + row, L - 1);
+        const uint16_t* kp = Kg + (size_t)tok * D + kg * 8;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          kb[T][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kp + s * 32));
+      }
+    };
+    // V rows of a chunk: lane (dim chunk dc, row group tg), whole rows per instruction
+    auto load_v = [&](const int (&st)[4], u32x4_t (&vv)[TPL]) {
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const int T = (i * TG) / 16;
+        const int tok = st[T] < 0 ? 0 : min(st[T] + (i * TG) % 16 + tg, L - 1);
+        vv[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(Vg + (size_t)tok * D + dc * 8));
+      }
+    };
+    uint16_t* const vs = Vs[wave];
+    auto consume = [&](const int (&st)[4], const bf16x8_t (&kb)[4][KS],
+                       const u32x4_t (&vv)[TPL]) {
+      // the chunk's V rows to this wave's LDS tile, row t = chunk token t
+#pragma unroll
+      for (int i = 0; i < TPL; ++i)
+        *reinterpret_cast<u32x4_t*>(&vs[(i * TG + tg) * VP + dc * 8]) = vv[i];
+      // S'[token][head] for the 4 tiles: sc[T][r] = S'[chunk token 16T + 4kg + r][head row]
+      floatx4_t sc[4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        floatx4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[T][s], qb[s], a, 0, 0, 0);
+        sc[T] = a;
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool tv = st[T] >= 0 && st[T] + 4 * kg + r < L;
+          const float z = tv ? sc[T][r] * qscale : -INFINITY;
+          sc[T][r] = z;
+          bm = fmaxf(bm, z);
+        }
+      bm = xor32_max(xor16_max(bm));
+      // the chunk has a token below L, so bm and mn are finite; alpha = 0 on the first chunk.
+      // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 weigh nothing.
+      const float mn = fmaxf(m, bm);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sc[T][r] - mn);
+          sc[T][r] = p;
+          rs += p;
+        }
+      rs = xor32_sum(xor16_sum(rs));
+      l = l * alpha + rs;
+      m = mn;
+      // rescale O rows 4kg + r by their head's alpha, held by lane 4kg + r (rows >= G
+      // are padding and take any finite factor)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float ar = readlane_f(alpha, r);
+        if constexpr (G > 4) ar = kg == 1 ? readlane_f(alpha, 4 + r) : ar;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) o[dt][r] *= ar;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // O += P.V: A = P (k = tokens {32s+4kg..+3} then {32s+16+4kg..+3}, in bf16),
+      // B = V from the transposing LDS read in the same token order
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t pa = {(__bf16)sc[2 * s][0],     (__bf16)sc[2 * s][1],
+                             (__bf16)sc[2 * s][2],     (__bf16)sc[2 * s][3],
+                             (__bf16)sc[2 * s + 1][0], (__bf16)sc[2 * s + 1][1],
+                             (__bf16)sc[2 * s + 1][2], (__bf16)sc[2 * s + 1][3]};
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+          // lane `row` receives V[32s + 4kg + k][16dt + row], k = 0..3, then the same 16
+          // tokens later: the token order of pa
+          const uint16_t* vp = &vs[(32 * s + 4 * kg + row / 4) * VP + dt * 16 + 4 * (row % 4)];
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, lds_tr_b_operand(vp, VP), o[dt],
+                                                          0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // Software pipeline over this wave's chunks: the next chunk's K loads are in flight
+    // while the current chunk is consumed.
+    int st[4] = {-1, -1, -1, -1};
+    bf16x8_t kb[4][KS];
+    if (n_mine > 0) {
+      tile_starts(0, st);
+      load_k(st, kb);
     }
+    for (int i = 0; i < n_mine; ++i) {
+      u32x4_t vv[TPL];
+      load_v(st, vv);
+      int stn[4] = {-1, -1, -1, -1};
+      bf16x8_t kn[4][KS];
+      if (i + 1 < n_mine) {
+        tile_starts(i + 1, stn);
+        load_k(stn, kn);
+      }
+      if (any_token(st)) consume(st, kb, vv);
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        st[T] = stn[T];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
+      }
+    }
+
+    // this wave's state to LDS: heads h < G (O row h lives in lanes kg = h / 4, r = h % 4)
+    if (lane < G) {
+      mm[wave][lane] = m;
+      ll[wave][lane] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * kg + r;
+      if (h < G) {
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) accs[wave][h][dt * 16 + row] = o[dt][r];
+      }
+    }
+    __syncthreads();
+    // merge the waves of this work-group into the run result
+    for (int oi = threadIdx.x; oi < G * D; oi += NW * 64) {
+      const int h = oi / D, dd = oi % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w][h]);
+      float ls = 0.f, a = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = mm[w][h] == -INFINITY ? 0.f : exp2f(mm[w][h] - M);
+        ls += sc * ll[w][h];
+        a += sc * accs[w][h][dd];
+      }
+      racc[h][dd] = a;
+      if (dd == 0) {
+        rm[h] = M;
+        rl[h] = ls;
+      }
+    }
+    __syncthreads();
+    store_run<D, G, NW * 64>(racc, rm, rl, slot_base(b, g, G, Hq, nslot, slot), nslot, ws_acc,
+                             ws_ml, last);
+  };
+
+  if constexpr (FLAT) {
+    // Runs of one common length `chunk` for every query, as many per query as its count
+    // needs (ceil(count / chunk)), with chunk the shortest of three candidates that
+    // keeps the total within the nsplit * B work-groups: so queries that select very
+    // different numbers of blocks keep the work-groups equally busy. Work-group
+    // x + nsplit*z takes run number x + nsplit*z in query order; run k of a query fills
+    // its slot k, and the query's last run is marked as such. With nearly equal counts
+    // (nsplit runs per query no longer than that) the per-query runs are kept: they use
+    // every work-group, which the HBM-bound kernel prefers, and that decision costs one
+    // scan, one maximum and two divisions. Every wave reduces the B counts itself (no
+    // barrier): lane b holds query b's count.
+    const int c = lane < B ? min(max(sel_cnt[lane], 0), K_max) : 0;
+    const int wg = nsplit * B;
+    const int total = __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)c), 63);
+    const float maxf = wave_max_to_last((float)c);  // counts are exact in fp32
+    const int maxc = (int)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(maxf), 63));
+    int chunk = max(1, (total + wg - 1) / wg);
+    const int per_query = (maxc + nsplit - 1) / nsplit;
+    if (per_query > chunk) {
+      // the ideal run length if it is feasible, else one between it and the always
+      // feasible total / (wg - nz) (at most nz runs are partly empty); bps is feasible too
+      // (count <= K_max), and bounds a run by the kernel's per-wave list capacity
+      auto runs_at = [&](int ch) {
+        const int r = c > 0 ? (c + ch - 1) / ch : 0;
+        return __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)r), 63);
+      };
+      const int nz = __popcll(__ballot(c > 0));
+      if (runs_at(chunk) > wg) {
+        const int safe = wg > nz ? min(bps, max(1, (total + wg - nz - 1) / (wg - nz))) : bps;
+        const int mid = max(1, (2 * total + 2 * wg - nz - 1) / (2 * wg - nz));
+        chunk = mid < safe && runs_at(mid) <= wg ? mid : safe;
+      }
+    }
+    if (per_query <= chunk) {
+      const int split = blockIdx.x, b = blockIdx.z;
+      const int cnt = __builtin_amdgcn_readlane(c, b);
+      int run = (cnt + nsplit - 1) / nsplit;
+      run = min((run + EPC - 1) / EPC * EPC, bps);
+      const int j0 = split * run;
+      const bool last = split == nsplit - 1;  // every slot is written; the last is marked
+      const size_t base = slot_base(b, g, G, Hq, nslot, split);
+      if (j0 < cnt)
+        run_entries(b, j0, min(j0 + run, cnt), split, last);
+      else if (last)
+        store_end_marker<G>(base, nslot, ws_ml);
+      else
+        store_empty_run<G>(base, nslot, ws_ml);
+    } else {
+      const int nrun = c > 0 ? (c + chunk - 1) / chunk : 0;  // lane b: runs of query b
+      const int run_incl = (int)wave_incl_scan((uint32_t)nrun);
+      const int sidx = blockIdx.x + nsplit * blockIdx.z;
+      if (sidx == 0) {  // queries with no entry: an empty last partial in their first slot
+        for (int b = 0; b < B; ++b)
+          if (__builtin_amdgcn_readlane(c, b) == 0)
+            store_end_marker<G>(slot_base(b, g, G, Hq, nslot, 0), nslot, ws_ml);
+      }
+      if (sidx < __builtin_amdgcn_readlane(run_incl, 63)) {
+        // the query of run sidx: queries whose runs all come before it
+        const int b = __popcll(__ballot(lane < B && run_incl <= sidx));
+        const int nb_runs = __builtin_amdgcn_readlane(nrun, b);
+        const int k = sidx - (__builtin_amdgcn_readlane(run_incl, b) - nb_runs);
+        const int cb = __builtin_amdgcn_readlane(c, b);
+        run_entries(b, k * chunk, min(cb, (k + 1) * chunk), k, k == nb_runs - 1);
+      }
+    }
+  } else {
+    const int split = blockIdx.x, b = blockIdx.z;
+    const int cnt = min(max(sel_cnt[b], 0), K_max);
+    // Runs are cut from this row's actual count, spread over all nsplit work-groups
+    // (whole chunks for small blocks); `bps` is the split plan's maximum, sized for
+    // K_max, and cnt <= K_max keeps every run within it.
+    int run = (cnt + nsplit - 1) / nsplit;
+    run = min((run + EPC - 1) / EPC * EPC, bps);
+    const int j0 = split * run;
+    if (j0 >= cnt)
+      store_empty_run<G>(slot_base(b, g, G, Hq, nslot, split), nslot, ws_ml);
+    else
+      run_entries(b, j0, min(j0 + run, cnt), split, false);
   }
-  __syncthreads();
-  store_run<D, G, NW * 64>(racc, rm, rl, b, g, split, Hq, nsplit, ws_acc, ws_ml);
 }
 
 // ---------------------------------------------------------------- merge of the runs
-// One work-group per (query, head); thread = head dim. Every run slot holds a partial
-// (empty runs carry m = -inf), read 16 at a time -- one memory round trip per 16 runs
-// -- and merged with an online rescale in run order. A row with no selected token
-// (every m = -inf) gets zeros.
-template <typename T, int D>
+// One work-group per (query, head); thread = head dim. The head's slots are read CH at
+// a time -- one memory round trip per CH runs -- and merged with an online rescale in
+// slot order, up to nslot slots or (MARKED) the partial marked last, whichever comes
+// first; empty runs carry m = -inf. A row with no selected token (every m = -inf) gets
+// zeros. Marked slots are read 8 at a time: a query usually has few runs, and every
+// slot read past its last one is wasted bandwidth (measured: 16 at a time cost the
+// 128K batch-8 call 0.5 us).
+template <typename T, int D, bool MARKED>
 __global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ ws_acc,
                                                   const float2* __restrict__ ws_ml,
-                                                  T* __restrict__ out, int nsplit) {
-  constexpr int CH = 16;
+                                                  T* __restrict__ out, int nslot) {
+  constexpr int CH = MARKED ? 8 : 16;
   const int rowi = blockIdx.x;  // b * Hq + hq
-  const float2* ml = ws_ml + (size_t)rowi * nsplit;
-  const float* ap = ws_acc + (size_t)rowi * nsplit * D + threadIdx.x;
+  const float2* ml = ws_ml + (size_t)rowi * nslot;
+  const float* ap = ws_acc + (size_t)rowi * nslot * D + threadIdx.x;
   float M = -INFINITY, ls = 0.f, a = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += CH) {
+  for (int s0 = 0; s0 < nslot; s0 += CH) {
     float2 v[CH];
     float x[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const bool ok = s0 + i < nsplit;
+      const bool ok = s0 + i < nslot;
       // both loads issue together; an empty run's acc slot may hold anything
       v[i] = ok ? ml[s0 + i] : make_float2(-INFINITY, 0.f);
       x[i] = ok ? ap[(size_t)(s0 + i) * D] : 0.f;
     }
+    // the last partial (l < 0, stored as -l - 1) ends the slots; any after it are stale
+    bool end = false;
+    if constexpr (MARKED) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (end) v[i].x = -INFINITY;
+        if (!end && v[i].y < 0.f) {
+          v[i].y = -v[i].y - 1.f;
+          end = true;
+        }
+      }
+    }
     float Mc = M;
 #pragma unroll
     for (int i = 0; i < CH; ++i) Mc = fmaxf(Mc, v[i].x);
-    if (Mc == -INFINITY) continue;
-    const float sc = M == -INFINITY ? 0.f : exp2f(M - Mc);
-    ls *= sc;
-    a *= sc;
+    if (Mc != -INFINITY) {
+      const float sc = M == -INFINITY ? 0.f : exp2f(M - Mc);
+      ls *= sc;
+      a *= sc;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (v[i].x != -INFINITY) {
-        const float w = exp2f(v[i].x - Mc);
-        ls += w * v[i].y;
-        a += w * x[i];
+      for (int i = 0; i < CH; ++i) {
+        if (v[i].x != -INFINITY) {
+          const float w = exp2f(v[i].x - Mc);
+          ls += w * v[i].y;
+          a += w * x[i];
+        }
       }
+      M = Mc;
     }
-    M = Mc;
+    if (MARKED && end) break;
   }
   store_out(out + (size_t)rowi * D + threadIdx.x, ls > 0.f ? a / ls : 0.f);
 }
@@ -482,10 +592,10 @@ struct Ws {
   float2* ml;
 };
 
-Ws carve(void* workspace, int B, int Hq, int d, int nsplit) {
+Ws carve(void* workspace, int B, int Hq, int d, int nslot) {
   Ws w;
   w.acc = static_cast<float*>(workspace);
-  w.ml = reinterpret_cast<float2*>(w.acc + (size_t)B * Hq * nsplit * d);
+  w.ml = reinterpret_cast<float2*>(w.acc + (size_t)B * Hq * nslot * d);
   return w;
 }
 
@@ -515,11 +625,16 @@ hipError_t launch_mfma_bs(const void* q, const void* k, const void* v, const int
                                          entries_per_chunk;
   if ((chunks + kMfmaWaves - 1) / kMfmaWaves * entries_per_chunk > 64)
     return hipErrorInvalidValue;
-  dim3 grid(sp.nsplit, Hkv, B);
-  hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves, BS>), grid, dim3(kMfmaWaves * 64), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml, Hq,
-                     Hkv, L, qscale, sp.blocks_per_split, sp.nsplit);
+#define SPOT_MFMA(FLAT, GRID)                                                                 \
+  hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves, BS, FLAT>), GRID, dim3(kMfmaWaves * 64), 0, \
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), \
+                     static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml, \
+                     Hq, Hkv, L, qscale, sp.blocks_per_split, sp.nsplit, B, sp.nslot)
+  if (sp.flat)
+    SPOT_MFMA(true, dim3(sp.nsplit, Hkv, B));
+  else
+    SPOT_MFMA(false, dim3(sp.nsplit, Hkv, B));
+#undef SPOT_MFMA
   return hipGetLastError();
 }
 
@@ -570,8 +685,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
   }
 #undef SPOT_ARGS
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine<T, D>), dim3(B * Hq), dim3(D), 0, stream, ws.acc, ws.ml,
-                     static_cast<T*>(out), sp.nsplit);
+  // runs across queries mark each query's last partial; per-query runs fill all nsplit
+  // slots (a fixed trip count, so the loads of every batch issue together)
+  if (sp.flat)
+    hipLaunchKernelGGL((attn_combine<T, D, true>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
+                       ws.ml, static_cast<T*>(out), sp.nslot);
+  else
+    hipLaunchKernelGGL((attn_combine<T, D, false>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
+                       ws.ml, static_cast<T*>(out), sp.nslot);
   return hipGetLastError();
 }
 
@@ -593,12 +714,19 @@ AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_p
     sp.blocks_per_split = bps > 0 ? bps : 256 / block;
   }
   sp.nsplit = (K_max + sp.blocks_per_split - 1) / sp.blocks_per_split;
+  // Runs across queries (MFMA path, B <= kFlatMaxB): nsplit * B work-groups per KV head,
+  // so a query's partials take at most nsplit * B slots; used when that fits the
+  // workspace.
+  sp.flat = bf16_fast_path && B >= 2 && B <= kFlatMaxB &&
+            (long)sp.nsplit * B <= (long)K_max + 32;
+  sp.nslot = sp.flat ? sp.nsplit * B : sp.nsplit;
   return sp;
 }
 
 size_t attn_workspace_bytes(int B, int Hq, int d, int K_max) {
-  // runs per unit are at most K_max (one block per run)
-  return (size_t)B * Hq * K_max * ((size_t)d + 2) * sizeof(float);
+  // slots per (query, head): at most K_max runs of one block (the fp32 path), or up
+  // to K_max + 32 (runs across queries, used only when they fit)
+  return (size_t)B * Hq * ((size_t)K_max + 32) * ((size_t)d + 2) * sizeof(float);
 }
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -607,7 +735,7 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
                               int d, int L, int block, float sm_scale, hipStream_t stream) {
   const bool fast = bf16;
   const AttnSplit sp = attn_split_plan(B, Hkv, K_max, block, fast);
-  const Ws ws = carve(workspace, B, Hq, d, sp.nsplit);
+  const Ws ws = carve(workspace, B, Hq, d, sp.nslot);
   const float qscale = sm_scale * kLog2e;
   if (bf16)
     return d == 64 ? launch_d<uint16_t, 64>(q, k_cache, v_cache, fast, sel_idx, sel_cnt, K_max,

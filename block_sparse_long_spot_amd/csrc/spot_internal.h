@@ -33,6 +33,8 @@ hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* se
 struct AttnSplit {
   int blocks_per_split;
   int nsplit;
+  bool flat;  // runs cut across queries (the MFMA path at small batch)
+  int nslot;  // partial-result slots per (query, head)
 };
 AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path);
 size_t attn_workspace_bytes(int B, int Hq, int d, int K_max);

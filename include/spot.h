@@ -184,9 +184,10 @@ SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max
  *   workspace    device scratch of at least spot_sparse_attn_workspace_bytes(B, Hq, d,
  *                K_max) bytes, 256-byte aligned; contents on entry do not matter. Calls
  *                that run at the same time must not share a workspace.
- * Split-K: each work-group reduces a run of selected blocks of one (b, KV head) with an
- * online softmax; a second kernel merges the runs of every (b, head) in run order, so
- * the result is deterministic.
+ * Split-K: each work-group reduces a run of selected blocks with an online softmax (for
+ * bf16 at batch 2..64 the runs are cut from all queries' lists together, so rows with
+ * very different counts stay balanced); a second kernel merges the runs of every
+ * (b, head) in run order, so the result is deterministic.
  * Supported: d in {64, 128}; block in {16, 32, 64, 128} tokens (16 is the paper's page
  * size, Appendix A Table 3); Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
  */

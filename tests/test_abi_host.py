@@ -140,7 +140,7 @@ def test_sparse_attn_validation(lib):
     assert attn(lib, block=256) == UNSUPPORTED
     assert attn(lib, Hq=48, Hkv=3) == UNSUPPORTED           # 16 heads per KV head
     ws = _lib.spot_sparse_attn_workspace_bytes(8, 32, 128, 256)
-    assert ws == 8 * 32 * 256 * 130 * 4      # fp32 partial results and (m, l) per run
+    assert ws == 8 * 32 * (256 + 32) * 130 * 4  # fp32 partial results and (m, l) per slot
     assert _lib.spot_sparse_attn_workspace_bytes(0, 32, 128, 256) == 0
 
 

@@ -261,6 +261,9 @@ def _sets_for(pattern, B, nb, K_max, g):
             s = sorted(set(torch.randperm(nb - 1, generator=g)[: c - 1].tolist()) | {nb - 1})
         elif pattern == "empty_rows":
             s = [] if b % 2 == 0 else sorted(torch.randperm(nb, generator=g)[:K_max].tolist())
+        elif pattern == "skewed":   # a few full rows, the rest short or empty
+            c = K_max if b % 5 == 0 else (0 if b % 7 == 3 else 1 + b % 4)
+            s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
         else:
             c = int(torch.randint(1, K_max + 1, (1,), generator=g))
             s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
@@ -287,6 +290,13 @@ ATTN_BLOCK_CASES = [
     (2, 8, 2, 64, 1500, 16, 50, "f32", "random"),
     (2, 8, 2, 128, 1000, 128, 6, "f32", "ragged_last"),
     (2, 4, 4, 64, 900, 32, 20, "f32", "random"),
+    # runs cut across queries: the largest batch that uses them, and the next one up
+    # (per-query runs); many short rows beside long ones
+    (64, 8, 2, 128, 4096, 64, 40, "bf16", "random"),
+    (65, 8, 2, 128, 4096, 64, 40, "bf16", "random"),
+    (16, 8, 1, 64, 8192, 16, 300, "bf16", "skewed"),
+    (8, 16, 4, 128, 8192, 32, 200, "bf16", "skewed"),
+    (4, 8, 2, 128, 8192, 64, 128, "bf16", "invalid_prefix"),
     # longest runs of the split plan: 16 chunks per wave (64 list entries at block 16)
     (4, 8, 8, 64, 32768, 16, 2048, "bf16", "random"),
     (8, 8, 8, 64, 16384, 32, 512, "bf16", "random"),
@@ -314,6 +324,10 @@ def _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag, dirty_ws=False)
     for b, s in enumerate(sets):
         idx[b, : len(s)] = torch.tensor(s, dtype=torch.int32)
         cnt[b] = len(s)
+    if pattern == "invalid_prefix":    # whole runs of ignored entries before valid ones
+        for b in range(B):
+            c = int(cnt[b])
+            idx[b, : c // 2] = -1
     if pattern == "invalid_entries":   # out-of-range entries inside the count are ignored
         for b in range(B):
             c = int(cnt[b])
