@@ -54,10 +54,10 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// The run result of this work-group (per head: max m, sum l, unnormalised acc[D]) is
-// in LDS: stored as the run's partial result for attn_combine.
-// A partial result (m, l, acc) per head. `last` marks a head's last partial: its l is
-// stored as -l - 1 (a real l is >= 0), and the merge stops after it.
+// The run result of this work-group (per head: max m, sum l, unnormalised acc[D]), held
+// in LDS, stored as the run's partial result for attn_combine. `last` marks a head's
+// last partial: its l is stored as -l - 1 (a real l is >= 0), and the merge stops after
+// it.
 template <int D, int G, int NT>
 __device__ void store_run(const float (&racc)[G][D], const float (&rm)[G], const float (&rl)[G],
                           size_t base, int nslot, float* __restrict__ ws_acc,
@@ -84,7 +84,8 @@ __device__ void store_empty_run(size_t base, int nslot, float2* __restrict__ ws_
     ws_ml[base + (size_t)threadIdx.x * nslot] = make_float2(-INFINITY, 0.f);
 }
 
-// An empty last partial (m = -inf, l = 0 stored as -1) for a query with no entry.
+// An empty last partial (m = -inf, l = 0 stored as -1): a query with no entry, or the
+// empty final run of a query.
 template <int G>
 __device__ void store_end_marker(size_t base, int nslot, float2* __restrict__ ws_ml) {
   if (threadIdx.x < G)
