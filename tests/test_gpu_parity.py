@@ -6,6 +6,7 @@ benchmark times (the split plan is a function of the sizes only), with outputs
 compared on sampled rows.
 """
 import math
+import random
 
 import numpy as np
 import pytest
@@ -347,6 +348,67 @@ def _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag, dirty_ws=False)
     used = [[int(x) for x in idx[b, : int(cnt[b])]] for b in range(B)]
     ref = O.sparse_attention(np64(q), np64(K), np64(V), used, block, scale)
     assert_out_close(np64(out), ref, tdt, tag=tag)
+
+
+def _batch_sweep(n=24, seed=4321):
+    """Seeded attention-only configurations at batch 2..64 (runs cut for the whole
+    batch): GQA ratio, head dim, block size, ragged L, K_max, and per-row counts drawn
+    from one of several spreads (equal, uniform, a few long rows among short or empty
+    ones), sometimes with ignored entries inside the count."""
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        B = rng.choice([2, 3, 5, 8, 13, 32, 64])
+        Hkv = rng.choice([1, 2, 4, 8])
+        G = rng.choice([1, 2, 4, 8])
+        d = rng.choice([64, 128])
+        block = rng.choice([16, 32, 64, 128])
+        L = rng.randint(2, 64) * block - rng.choice([0, rng.randint(0, block - 1)])
+        if B * Hkv * G * L > 2_000_000:
+            continue
+        nb = -(-L // block)
+        K_max = rng.randint(1, nb)
+        spread = rng.choice(["equal", "uniform", "skew", "skew_empty"])
+        invalid = rng.random() < 0.25
+        out.append((len(out), B, G * Hkv, Hkv, d, L, block, K_max, spread, invalid))
+    return out
+
+
+@pytest.mark.parametrize("case", _batch_sweep(), ids=lambda c: "sweep%d" % c[0])
+def test_sparse_attn_batch_sweep(case):
+    i, B, Hq, Hkv, d, L, block, K_max, spread, invalid = case
+    log(f"attn batch sweep {case}")
+    g = cpu_gen(9000 + i)
+    rng = random.Random(9000 + i)
+    q = torch.randn(B, Hq, d, generator=g).bfloat16()
+    K = torch.randn(B, Hkv, L, d, generator=g).bfloat16()
+    V = torch.randn(B, Hkv, L, d, generator=g).bfloat16()
+    nb = -(-L // block)
+    idx = torch.full((B, K_max), -1, dtype=torch.int32)
+    cnt = torch.zeros(B, dtype=torch.int32)
+    for b in range(B):
+        if spread == "equal":
+            c = K_max
+        elif spread == "uniform":
+            c = rng.randint(1, K_max)
+        else:
+            c = K_max if rng.random() < 0.2 else rng.randint(0 if spread == "skew_empty" else 1,
+                                                             max(1, K_max // 8))
+        s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
+        idx[b, :c] = torch.tensor(s, dtype=torch.int32)
+        if invalid and c > 1:
+            idx[b, rng.randrange(c)] = rng.choice([-3, nb, nb + 7])
+        cnt[b] = c
+    scale = 1.0 / math.sqrt(d)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV).bfloat16()
+    ws = torch.full((_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max),), 255,
+                    dtype=torch.uint8, device=DEV)
+    _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), cnt.to(DEV), out, ws,
+                          scale, block=block)
+    torch.cuda.synchronize()
+    used = [[int(x) for x in idx[b, : int(cnt[b])]] for b in range(B)]
+    ref = O.sparse_attention(np64(q), np64(K), np64(V), used, block, scale)
+    assert_out_close(np64(out), ref, torch.bfloat16, tag=str(case))
 
 
 def test_sparse_attn_deterministic():
