@@ -10,8 +10,10 @@
 // (query, KV head) gets the same number of runs, cut from that query's own count (runs
 // past its end store an empty partial). attn_combine then merges the slots of every
 // (query, head) in order (deterministic). Merging across work-groups inside one kernel
-// would need an agent-scope release/acquire per work-group, which on this multi-XCD
-// part is an L2 writeback plus invalidate; a second small kernel is cheaper.
+// needs an agent-scope release/acquire per work-group, which on this multi-XCD part is
+// an L2 writeback plus invalidate; a second small kernel is cheaper (measured: with the
+// last-arriving work-group of each query merging, the 128K batch-8 call took 108 us
+// instead of 84, and the 1024-block static top-K call 593 us instead of 334).
 //
 // Block sizes 16, 32, 64 and 128 tokens. The unit of work of a wave is a 64-token
 // chunk made of four 16-token tiles, each with its own start token: the four tiles of
