@@ -431,6 +431,48 @@ def calibration_copy():
     return n * 4
 
 
+def read_ceiling(nbytes, stream, reps=20):
+    """What a kernel that only reads sustains on this GPU for the attention's access
+    pattern: about `nbytes` as 16 KiB blocks (one 64-token block of one KV head at
+    d = 128 in bf16) picked in random order from a buffer twice that size, 16-byte
+    non-temporal loads, no compute. Best of 256, 512 and 1024 work-groups, HIP events
+    around `reps` back-to-back launches on `stream`."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(spot.__file__), "libspot_probe.so"))
+    lib.spot_probe_read_blocks.restype = ctypes.c_int
+    lib.spot_probe_read_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blk = 16384
+    n = nbytes // blk // 2048 * 2048
+    buf = torch.ones(2 * n * blk // 2, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator().manual_seed(7)
+    lst = torch.randperm(2 * n, generator=g)[:n].to(torch.int32).cuda()
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    per = {}
+    with torch.cuda.stream(stream):
+        for wgs in (256, 512, 1024):
+            def go():
+                st = lib.spot_probe_read_blocks(buf.data_ptr(), lst.data_ptr(), n, wgs,
+                                                sink.data_ptr(), stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError("spot_probe_read_blocks failed")
+            for _ in range(3):
+                go()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                go()
+            e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            per[wgs] = {"us": round(us, 3), "GBps": round(n * blk / (us * 1e-6) / 1e9, 1)}
+    del buf, lst, sink
+    best = max(v["GBps"] for v in per.values())
+    return {"GBps": best, "bytes": n * blk, "per_workgroups": per,
+            "what": "read-only kernel, the same bytes as 16 KiB blocks in random order, "
+                    "16-byte non-temporal loads, no compute (csrc/read_ceiling.hip)"}
+
+
 def cpu_baseline(wl, inp, b_sample=1, heads_sample=None):
     """The fp64 oracle (scoring, dual top-p, dense masked attention) on a bounded
     sample: batch rows [0, b_sample), all heads, full L. Scaled to one whole step."""
@@ -595,6 +637,11 @@ def main():
         "pages_context": "paper: 3.9x FlashAttention, 1.8x Twilight end-to-end decode tok/s "
                          "at 128K on one NVIDIA B200 (not comparable to this metric)",
     }
+    log("bench: read-only reference kernel over the attention's bytes")
+    rc = read_ceiling(budget["attn"], stream)
+    rc["attn_frac_of_it"] = round(attn_gbps / rc["GBps"], 4)
+    rc["step_frac_of_it"] = round(budget["step"] / (us_step * 1e-6) / 1e9 / rc["GBps"], 4)
+    result["read_ceiling"] = rc
     if a.extra_b1 and wl.name == "c3_128k_b8":
         wl1 = W.WORKLOADS["c3_128k_b1"]
         inp1 = {k: (v[:1].contiguous() if isinstance(v, torch.Tensor) else v)

@@ -30,6 +30,8 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 SOURCES = ["capi.cpp", "score.hip", "topp.hip", "attn.hip", "prefill.hip", "quant.hip"]
+PROBE_SRC = "read_ceiling.hip"
+PROBE_OUT = os.path.join(PKG, "libspot_probe.so")
 
 
 def _compile(src: str) -> str:
@@ -51,8 +53,15 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    # the benchmark's read-bandwidth reference, a library of its own
+    pobj = _compile(PROBE_SRC)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", PROBE_OUT + ".tmp", pobj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 
