@@ -220,7 +220,7 @@ class _KV:
 
 
 def _sequence_case(B, T, Tq, q_pos0, Hq, Hkv, p, n_sink, n_rec, K_min, seed, tiles_checked,
-                   heads_checked):
+                   heads_checked, K_max=None):
     """Whole-sequence prefill through the three tile-indexed calls, checked per tile
     against the oracle: every score of the checked tiles, their selection (on the GPU's
     own scores and end to end) and the outputs of the checked heads."""
@@ -238,7 +238,7 @@ def _sequence_case(B, T, Tq, q_pos0, Hq, Hkv, p, n_sink, n_rec, K_min, seed, til
     V = torch.randn(B, Hkv, L, d, generator=g, device=DEV).bfloat16()
     scores = torch.full((B, n_tiles, nb_seq), float("nan"), device=DEV)
     _lib.spot_prefill_select_score(sel_q, sel_w, sel_k, scores, q_pos0, Tq=Tq)
-    K_max = nb_seq
+    K_max = nb_seq if K_max is None else K_max
     idx = torch.full((B, n_tiles, K_max), 12345, dtype=torch.int32, device=DEV)
     cnt = torch.full((B, n_tiles), -1, dtype=torch.int32, device=DEV)
     _lib.spot_prefill_select_topp(scores, idx, cnt, None, p, K_min, K_max, n_sink, n_rec,
@@ -290,6 +290,14 @@ def test_prefill_sequence_two_heads_per_wave_ragged():
                    K_min=0, seed=33, tiles_checked=(0, 7, 14), heads_checked=(0, 1, 2, 3, 31))
     _sequence_case(B=1, T=4000, Tq=128, q_pos0=100, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
                    K_min=8, seed=34, tiles_checked=(0, 16, 31), heads_checked=(0, 1, 6, 7, 30))
+
+
+def test_prefill_sequence_long_list_stride():
+    """A list stride of 8192 entries (the longest list) on a grid of 1024 row tiles: the
+    list's LDS leaves room for three block buffers instead of four."""
+    _sequence_case(B=1, T=2048, Tq=128, q_pos0=0, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
+                   K_min=2, seed=36, tiles_checked=(0, 9, 15), heads_checked=(0, 3, 29),
+                   K_max=8192)
 
 
 def test_prefill_sequence_mid_grid():
