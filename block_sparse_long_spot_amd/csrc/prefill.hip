@@ -283,7 +283,9 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
   const int pos0 = q_pos0 + qs;
   const int my_pos = pos0 + my_q;
 
-  // B operand of S' = K.Q^T: column = query row, k = head dim
+  // B operand of S' = K.Q^T: column = query row, k = head dim. A negative scale negates
+  // q instead (one xor with a wave-uniform mask per register)
+  const uint32_t qsign = qscale < 0.f ? 0x80008000u : 0u;
   bf16x8_t qb[HPW][4];
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
@@ -291,8 +293,7 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
         Q + (((size_t)b * Hq + h0 + h) * T + qs + min(my_q, Tq_t - 1)) * D + kg * 8;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4_t w = *reinterpret_cast<const u32x4_t*>(qp + s * 32);
-      if (qscale < 0.f) w ^= 0x80008000u;  // negated q: the scores change sign instead
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qp + s * 32) ^ qsign;
       qb[h][s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -538,7 +539,8 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float lr = o[h][8][r];  // l of query kg*4 + r
-      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      // the hardware reciprocal (1 ulp): the result is rounded to bf16 below
+      const float inv = lr > 0.f ? __builtin_amdgcn_rcpf(lr) : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         st[(h * 16 + kg * 4 + r) * D + dt * 16 + row] =
