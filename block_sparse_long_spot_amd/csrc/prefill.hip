@@ -359,6 +359,9 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
           0, 0);
     }
   };
+  // no block consumed yet by this wave: O and l are still zero, so a first maximum needs
+  // no rescale of them (wave-uniform)
+  bool fresh = true;
   auto consume = [&](const uint16_t* Ks, int blk) {
     const uint16_t* Vs = Ks + TILE;
     const int t0 = blk * kBlk;
@@ -416,11 +419,13 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
           const float alpha = mn == m[h] ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
           m[h] = mn;
           // rescale O rows kg*4 + r by the alpha of those rows (held by lanes with that row)
+          if (!fresh) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float ar = __shfl(alpha, kg * 4 + r, 64);
+            for (int r = 0; r < 4; ++r) {
+              const float ar = __shfl(alpha, kg * 4 + r, 64);
 #pragma unroll
-            for (int dt = 0; dt < 9; ++dt) o[h][dt][r] *= ar;
+              for (int dt = 0; dt < 9; ++dt) o[h][dt][r] *= ar;
+            }
           }
         }
         // v_exp_f32 directly: arguments are at most kRescaleSlack and results below
@@ -461,6 +466,7 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
         for (int h = 0; h < HPW; ++h)
           o[h][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[h], ones, o[h][8], 0, 0, 0);
       }
+      fresh = false;
     }
   };
   // Each set of S blocks (the next S of the list) goes to the S wave groups, one block
