@@ -175,3 +175,22 @@ def test_prefill_validation(lib):
     assert lib.spot_prefill_attn(*{**b, "T": 32768, "q_pos0": 1}.values()) == INVALID
     assert lib.spot_prefill_attn(*{**b, "d": 64}.values()) == UNSUPPORTED
     assert lib.spot_prefill_attn(*{**b, "kv_dtype": F32}.values()) == UNSUPPORTED
+
+
+def test_read_reference_probe_validation():
+    """The benchmark's read-only reference kernel lives in its own library: it exports its
+    one entry point and rejects bad arguments before any launch (no GPU needed)."""
+    import os
+    path = os.path.join(os.path.dirname(_lib.__file__), "libspot_probe.so")
+    probe = ctypes.CDLL(path)
+    f = probe.spot_probe_read_blocks
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    p = ctypes.c_void_p(0x1000)
+    assert f(None, p, 512, 256, p, None) == -1           # no buffer
+    assert f(p, None, 512, 256, p, None) == -1           # no list
+    assert f(p, p, 512, 256, None, None) == -1           # no sink
+    assert f(p, p, 500, 256, p, None) == -1              # not a multiple of 2 * wgs
+    assert f(p, p, 0, 256, p, None) == -1
+    assert f(p, p, 512, 0, p, None) == -1
