@@ -344,19 +344,30 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
   auto swz = [](int r) { return ((r & 7) << 1) | ((r >> 3) & 1); };
   const int ksw = swz(row);                // K fragment rows T*16 + row
   const int vsw = swz(4 * kg + row / 4);   // V rows 32s + 4kg + row/4 (and 16 later)
+  // A block wholly inside the cache is addressed as its (wave-uniform) first row plus a
+  // per-lane offset fixed for the kernel; only a block crossing L clamps rows to L - 1.
   auto load_block = [&](uint16_t* slot, int blk) {
     const int t0 = blk * kBlk;
+    const bool inside = t0 + kBlk <= L;  // uniform
 #pragma unroll
     for (int n = 0; n < 16 / G; ++n) {
       const int piece = gw * (16 / G) + n;    // 1 KiB run: tile rows 4*piece .. +3
       const int ch = piece * 64 + lane;       // the LDS chunk this lane fills
       const int r = ch >> 4, c = (ch & 15) ^ swz(ch >> 4);
-      const size_t src = (size_t)min(t0 + r, L - 1) * D + c * 8;
+      const uint16_t* kp;
+      const uint16_t* vp;
+      if (inside) {
+        kp = Kg + (size_t)t0 * D + (r * D + c * 8);
+        vp = Vg + (size_t)t0 * D + (r * D + c * 8);
+      } else {
+        const size_t src = (size_t)min(t0 + r, L - 1) * D + c * 8;
+        kp = Kg + src;
+        vp = Vg + src;
+      }
       __builtin_amdgcn_global_load_lds(
-          Kg + src, (__attribute__((address_space(3))) void*)(slot + piece * 512), 16, 0, 0);
+          kp, (__attribute__((address_space(3))) void*)(slot + piece * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
-          Vg + src, (__attribute__((address_space(3))) void*)(slot + TILE + piece * 512), 16,
-          0, 0);
+          vp, (__attribute__((address_space(3))) void*)(slot + TILE + piece * 512), 16, 0, 0);
     }
   };
   // no block consumed yet by this wave: O and l are still zero, so a first maximum needs
