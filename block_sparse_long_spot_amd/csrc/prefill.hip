@@ -399,12 +399,13 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
 #pragma unroll
       for (int h = 0; h < HPW; ++h) bmax[h] = -INFINITY;
       if (!(t0 + kBlk - 1 <= pos0 + q0 && t0 + kBlk <= L)) {
+        // token t0 + T*16 + kg*4 + r is visible to this lane's query when T*16 + r <= lim
+        const int lim = min(my_pos, L - 1) - t0 - kg * 4;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int t = t0 + T * 16 + kg * 4 + r;
-            const bool vis = t <= my_pos && t < L;
+            const bool vis = T * 16 + r <= lim;
 #pragma unroll
             for (int h = 0; h < HPW; ++h) sc[h][T][r] = vis ? sc[h][T][r] : -INFINITY;
           }
