@@ -302,7 +302,7 @@ def static_topk_leg(inp, wl, steps, warmup, stream):
     attention bytes of the top-p headline."""
     K = wl.nb // 2
     ws = wl.with_(p=0.0, K_min=K, K_max=K, n_sink=0, n_rec=0)
-    bufs = DecodeBuffers(ws.B, ws.nb, ws.Hq, ws.d, ws.K_max, inp["q"].dtype)
+    bufs = DecodeBuffers.of(ws, inp["q"].dtype)
     us, _ = time_back_to_back(lambda: decode_step(inp, ws, bufs, stream=stream), steps,
                               warmup, stream)
     _, _, per = time_steps(inp, ws, bufs, max(10, steps // 10), warmup, stream)
@@ -321,7 +321,7 @@ def budgets_vary_leg(wl, steps, warmup, stream):
     step, the attention call and the per-row block counts."""
     ws = wl.with_(zipf_spread=(1.3, 2.0))
     inp = W.make_inputs(ws, device="cuda")
-    bufs = DecodeBuffers(ws.B, ws.nb, ws.Hq, ws.d, ws.K_max, inp["q"].dtype)
+    bufs = DecodeBuffers.of(ws, inp["q"].dtype)
     us, _ = time_back_to_back(lambda: decode_step(inp, ws, bufs, stream=stream), steps,
                               warmup, stream)
     scale = 1.0 / math.sqrt(ws.d)
@@ -350,7 +350,7 @@ def page_geometry_step(steps, warmup, stream):
     layer, on one NVIDIA B200 (context, not a target)."""
     wl = W.WORKLOADS["page_128k_b1"]
     inp = W.make_inputs(wl, device="cuda")
-    bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, inp["q"].dtype)
+    bufs = DecodeBuffers.of(wl, inp["q"].dtype)
     us, _ = time_back_to_back(lambda: decode_step(inp, wl, bufs, stream=stream), steps,
                               warmup, stream)
     _, _, per = time_steps(inp, wl, bufs, steps, warmup, stream)
@@ -558,7 +558,7 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     dt = inp["q"].dtype
-    bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, dt)
+    bufs = DecodeBuffers.of(wl, dt)
     log(f"bench: warmup {a.warmup}, timing {a.steps} steps")
     scale = 1.0 / math.sqrt(wl.d)
 
@@ -646,7 +646,7 @@ def main():
         wl1 = W.WORKLOADS["c3_128k_b1"]
         inp1 = {k: (v[:1].contiguous() if isinstance(v, torch.Tensor) else v)
                 for k, v in inp.items()}
-        bufs1 = DecodeBuffers(1, wl1.nb, wl1.Hq, wl1.d, wl1.K_max, dt)
+        bufs1 = DecodeBuffers.of(wl1, dt)
         u1, _ = time_back_to_back(lambda: decode_step(inp1, wl1, bufs1, stream=stream),
                                   a.steps, a.warmup, stream)
         w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
@@ -667,7 +667,7 @@ def main():
         del inp
         torch.cuda.empty_cache()
         inp4 = W.make_inputs(wl4, device="cuda")
-        bufs4 = DecodeBuffers(wl4.B, wl4.nb, wl4.Hq, wl4.d, wl4.K_max, dt)
+        bufs4 = DecodeBuffers.of(wl4, dt)
         u4, _ = time_back_to_back(lambda: decode_step(inp4, wl4, bufs4, stream=stream),
                                   a.steps, a.warmup, stream)
         w4, _, p4 = time_steps(inp4, wl4, bufs4, a.steps, a.warmup, stream)

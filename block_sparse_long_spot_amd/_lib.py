@@ -20,7 +20,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "spot.h")
 
 SPOT_OK, SPOT_ERR_INVALID, SPOT_ERR_UNSUPPORTED, SPOT_ERR_DEVICE = 0, -1, -2, -3
 SPOT_F32, SPOT_BF16, SPOT_INT4_G32, SPOT_INT8, SPOT_FP8_E4M3, SPOT_FP4_E2M1_G32 = range(6)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -47,7 +47,7 @@ def load() -> ctypes.CDLL:
     lib.spot_quantize_selector.restype = i
     lib.spot_select_topp.argtypes = [vp, vp, vp, vp, i, i, f, i, i, i, i, vp]
     lib.spot_select_topp.restype = i
-    lib.spot_sparse_attn_workspace_bytes.argtypes = [i, i, i, i]
+    lib.spot_sparse_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.spot_sparse_attn_workspace_bytes.restype = sz
     lib.spot_sparse_attn.argtypes = [vp, vp, vp, i, vp, vp, i, vp, vp, sz, i, i, i, i, i, i, f,
                                      vp]
@@ -181,8 +181,12 @@ def spot_select_topp(scores, sel_idx, sel_cnt, sel_mass, p: float, K_min: int, K
     _check("spot_select_topp", st)
 
 
-def spot_sparse_attn_workspace_bytes(B: int, Hq: int, d: int, K_max: int) -> int:
-    return int(load().spot_sparse_attn_workspace_bytes(B, Hq, d, K_max))
+def spot_sparse_attn_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, K_max: int,
+                                     block: int = 64, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace spot_sparse_attn needs for these arguments (0 when they are
+    invalid or unsupported); dtype is that of q, K and V."""
+    code = SPOT_BF16 if dtype == torch.bfloat16 else SPOT_F32
+    return int(load().spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, code))
 
 
 def spot_sparse_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, workspace, sm_scale: float,

@@ -37,6 +37,8 @@
 //    lane = token for q.K^T (64 tokens of a block at a time), lane = head dim for P.V,
 //    all in fp32.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
+#include <algorithm>
+
 #include "device_common.h"
 #include "spot_internal.h"
 
@@ -464,20 +466,25 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     const int total = __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)c), 63);
     const float maxf = wave_max_to_last((float)c);  // counts are exact in fp32
     const int maxc = (int)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(maxf), 63));
-    int chunk = max(1, (total + wg - 1) / wg);
+    // no query may have more runs than its nslot slots: chunk >= ceil(maxc / nslot),
+    // which is <= bps (nslot >= nsplit = ceil(K_max / bps) and maxc <= K_max)
+    const int lo = max(1, (maxc + nslot - 1) / nslot);
+    int chunk = max(lo, (total + wg - 1) / wg);
     const int per_query = (maxc + nsplit - 1) / nsplit;
     if (per_query > chunk) {
       // the ideal run length if it is feasible, else one between it and the always
       // feasible total / (wg - nz) (at most nz runs are partly empty); bps is feasible too
-      // (count <= K_max), and bounds a run by the kernel's per-wave list capacity
+      // (count <= K_max), and bounds a run by the kernel's per-wave list capacity. Longer
+      // runs mean fewer of them, so raising a candidate to lo keeps it feasible.
       auto runs_at = [&](int ch) {
         const int r = c > 0 ? (c + ch - 1) / ch : 0;
         return __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)r), 63);
       };
       const int nz = __popcll(__ballot(c > 0));
       if (runs_at(chunk) > wg) {
-        const int safe = wg > nz ? min(bps, max(1, (total + wg - nz - 1) / (wg - nz))) : bps;
-        const int mid = max(1, (2 * total + 2 * wg - nz - 1) / (2 * wg - nz));
+        const int safe =
+            max(lo, wg > nz ? min(bps, max(1, (total + wg - nz - 1) / (wg - nz))) : bps);
+        const int mid = max(lo, (2 * total + 2 * wg - nz - 1) / (2 * wg - nz));
         chunk = mid < safe && runs_at(mid) <= wg ? mid : safe;
       }
     }
@@ -627,7 +634,7 @@ hipError_t launch_mfma_bs(const void* q, const void* k, const void* v, const int
                                    : (sp.blocks_per_split + entries_per_chunk - 1) /
                                          entries_per_chunk;
   if ((chunks + kMfmaWaves - 1) / kMfmaWaves * entries_per_chunk > 64)
-    return hipErrorInvalidValue;
+    return hipErrorNotSupported;  // a plan this kernel cannot hold (the plan never makes one)
 #define SPOT_MFMA(FLAT, GRID)                                                                 \
   hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves, BS, FLAT>), GRID, dim3(kMfmaWaves * 64), 0, \
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), \
@@ -705,7 +712,8 @@ AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_p
   AttnSplit sp;
   const long units = (long)B * Hkv;
   if (!bf16_fast_path) {
-    sp.blocks_per_split = 4;
+    // one wave per run: 4 blocks, or longer runs so that a row has at most 64 of them
+    sp.blocks_per_split = K_max > 256 ? (K_max + 63) / 64 : 4;
   } else {
     // the longest run (<= 4096 tokens, i.e. 64 chunks: at most 16 per wave, and at
     // most 64 list entries per wave) that still gives >= 256 work-groups
@@ -717,19 +725,20 @@ AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_p
     sp.blocks_per_split = bps > 0 ? bps : 256 / block;
   }
   sp.nsplit = (K_max + sp.blocks_per_split - 1) / sp.blocks_per_split;
-  // Runs across queries (MFMA path, B <= kFlatMaxB): nsplit * B work-groups per KV head,
-  // so a query's partials take at most nsplit * B slots; used when that fits the
-  // workspace.
-  sp.flat = bf16_fast_path && B >= 2 && B <= kFlatMaxB &&
-            (long)sp.nsplit * B <= (long)K_max + 32;
-  sp.nslot = sp.flat ? sp.nsplit * B : sp.nsplit;
+  // Runs across queries (MFMA path, 2 <= B <= kFlatMaxB): a query's runs fill its slots
+  // from 0, at most nslot of them. nsplit * B slots would let one long query take every
+  // work-group of the batch; max(nsplit, 32) keeps that freedom at small batches (it is
+  // nsplit * B up to batch 8 at 256 work-groups) and bounds the workspace at large ones.
+  sp.flat = bf16_fast_path && B >= 2 && B <= kFlatMaxB;
+  sp.nslot = sp.flat ? (int)std::min<long>((long)sp.nsplit * B, std::max(sp.nsplit, 32))
+                     : sp.nsplit;
   return sp;
 }
 
-size_t attn_workspace_bytes(int B, int Hq, int d, int K_max) {
-  // slots per (query, head): at most K_max runs of one block (the fp32 path), or up
-  // to K_max + 32 (runs across queries, used only when they fit)
-  return (size_t)B * Hq * ((size_t)K_max + 32) * ((size_t)d + 2) * sizeof(float);
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block, bool bf16) {
+  // fp32 partial results and (m, l) per slot: nslot slots per (query, head)
+  const AttnSplit sp = attn_split_plan(B, Hkv, K_max, block, bf16);
+  return (size_t)B * Hq * (size_t)sp.nslot * ((size_t)d + 2) * sizeof(float);
 }
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -69,7 +69,7 @@ int check_selector(const void* sel_q, int q_dtype, const void* sel_q_scale, cons
 
 extern "C" {
 
-int spot_abi_version(void) { return 2; }
+int spot_abi_version(void) { return 3; }
 
 const char* spot_status_string(int status) {
   switch (status) {
@@ -142,9 +142,21 @@ int spot_quantize_selector(const void* src, int src_dtype, int n_rows, int row_l
                                                  as_stream(stream)));
 }
 
-size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max) {
-  if (B <= 0 || Hq <= 0 || d <= 0 || K_max <= 0) return 0;
-  return spot::attn_workspace_bytes(B, Hq, d, K_max);
+// The attention shapes this build has kernels for (after the argument checks).
+int attn_support(int Hq, int Hkv, int d, int block) {
+  const int G = Hq / Hkv;
+  if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;
+  if (block != 16 && block != 32 && block != 64 && block != 128) return SPOT_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
+  return SPOT_OK;
+}
+
+size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block,
+                                        int kv_dtype) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || K_max <= 0 || block <= 0) return 0;
+  if (Hq % Hkv != 0 || (kv_dtype != SPOT_F32 && kv_dtype != SPOT_BF16)) return 0;
+  if (attn_support(Hq, Hkv, d, block) != SPOT_OK) return 0;
+  return spot::attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, kv_dtype == SPOT_BF16);
 }
 
 int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, int kv_dtype,
@@ -160,13 +172,12 @@ int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, in
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || L <= 0 || block <= 0 || K_max <= 0)
     return SPOT_ERR_INVALID;
   if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
-  if (workspace_bytes < spot_sparse_attn_workspace_bytes(B, Hq, d, K_max))
-    return SPOT_ERR_INVALID;
-  const int G = Hq / Hkv;
-  if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;
-  if (block != 16 && block != 32 && block != 64 && block != 128) return SPOT_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
+  const int sup = attn_support(Hq, Hkv, d, block);
+  if (sup != SPOT_OK) return sup;
   if (B > kMaxGrid || Hkv > kMaxGrid || (long)B * Hq > 2147483647L) return SPOT_ERR_UNSUPPORTED;
+  if (workspace_bytes <
+      spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, kv_dtype))
+    return SPOT_ERR_INVALID;
   return from_hip(spot::launch_sparse_attn(q, k_cache, v_cache, kv_dtype == SPOT_BF16, sel_idx,
                                            sel_cnt, K_max, out, workspace, B, Hq, Hkv, d, L,
                                            block, sm_scale, as_stream(stream)));

@@ -37,7 +37,7 @@ struct AttnSplit {
   int nslot;  // partial-result slots per (query, head)
 };
 AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path);
-size_t attn_workspace_bytes(int B, int Hq, int d, int K_max);
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block, bool bf16);
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,

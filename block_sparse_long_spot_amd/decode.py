@@ -12,14 +12,22 @@ class DecodeBuffers:
     """Device buffers a decode step writes: scores, the selected set, the attention
     workspace and the output. Allocated once and reused across steps."""
 
-    def __init__(self, B, nb, Hq, d, K_max, out_dtype, device="cuda"):
+    def __init__(self, B, nb, Hq, Hkv, d, K_max, block, out_dtype, device="cuda"):
         self.scores = torch.empty(B, nb, dtype=torch.float32, device=device)
         self.sel_idx = torch.empty(B, K_max, dtype=torch.int32, device=device)
         self.sel_cnt = torch.empty(B, dtype=torch.int32, device=device)
         self.sel_mass = torch.empty(B, dtype=torch.float32, device=device)
-        ws = _lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max)
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        ws = _lib.spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, out_dtype)
+        if ws <= 0:
+            raise ValueError("no attention kernel for these sizes")
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.out = torch.empty(B, Hq, d, dtype=out_dtype, device=device)
+
+    @classmethod
+    def of(cls, wl, out_dtype, B=None, device="cuda"):
+        """Buffers for a decode step of workload `wl` (batch B, default wl.B)."""
+        return cls(wl.B if B is None else B, wl.nb, wl.Hq, wl.Hkv, wl.d, wl.K_max, wl.block,
+                   out_dtype, device=device)
 
 
 def decode_step(inp: dict, wl, bufs: DecodeBuffers, stream=None):

@@ -164,9 +164,13 @@ SPOT_API int spot_quantize_selector(const void* src, int src_dtype, int n_rows, 
 
 /*
  * spot_sparse_attn_workspace_bytes — size of the workspace spot_sparse_attn needs for
- * these sizes (split-K partial results). Returns 0 for non-positive sizes.
+ * these arguments (the same values passed to it): the split-K partial results of the
+ * split plan the call will use, B * Hq * nslot * (d + 2) fp32 values, nslot being the
+ * partial-result slots of one (query, head). Returns 0 for a non-positive size, an
+ * unknown kv_dtype or a shape spot_sparse_attn does not support.
  */
-SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max);
+SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max,
+                                                 int block, int kv_dtype);
 
 /*
  * spot_sparse_attn — decode attention over the selected blocks only (§2.3: the layer
@@ -181,9 +185,10 @@ SPOT_API size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int d, int K_max
  *                (SPOT_F32 or SPOT_BF16; bf16 output is rounded to nearest even);
  *                16-byte aligned.
  *   sel_idx      int32 [B][K_max], sel_cnt int32 [B] (as written by spot_select_topp).
- *   workspace    device scratch of at least spot_sparse_attn_workspace_bytes(B, Hq, d,
- *                K_max) bytes, 256-byte aligned; contents on entry do not matter. Calls
- *                that run at the same time must not share a workspace.
+ *   workspace    device scratch of at least spot_sparse_attn_workspace_bytes(B, Hq, Hkv,
+ *                d, K_max, block, kv_dtype) bytes, 256-byte aligned; contents on entry
+ *                do not matter. Calls that run at the same time must not share a
+ *                workspace.
  * Split-K: each work-group reduces a run of selected blocks with an online softmax (for
  * bf16 at batch 2..64 the runs are cut from all queries' lists together, so rows with
  * very different counts stay balanced); a second kernel merges the runs of every

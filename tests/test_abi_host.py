@@ -6,6 +6,7 @@ import ctypes
 import subprocess
 
 import pytest
+import torch
 
 from block_sparse_long_spot_amd import _lib
 
@@ -39,7 +40,7 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "SPOT_OK"
     for s in (INVALID, UNSUPPORTED, _lib.SPOT_ERR_DEVICE, 12345):
         assert isinstance(_lib.status_string(s), str) and _lib.status_string(s)
-    assert lib.spot_abi_version() == 2
+    assert lib.spot_abi_version() == 3
 
 
 def score(lib, **kw):
@@ -139,9 +140,24 @@ def test_sparse_attn_validation(lib):
     assert attn(lib, block=48) == UNSUPPORTED
     assert attn(lib, block=256) == UNSUPPORTED
     assert attn(lib, Hq=48, Hkv=3) == UNSUPPORTED           # 16 heads per KV head
-    ws = _lib.spot_sparse_attn_workspace_bytes(8, 32, 128, 256)
-    assert ws == 8 * 32 * (256 + 32) * 130 * 4  # fp32 partial results and (m, l) per slot
-    assert _lib.spot_sparse_attn_workspace_bytes(0, 32, 128, 256) == 0
+    assert attn(lib, ws_bytes=4259839, B=8, Hq=32, Hkv=8, K_max=256) == INVALID   # one short
+
+
+def test_sparse_attn_workspace_follows_the_split_plan(lib):
+    """fp32 partial results and (m, l) per slot, nslot slots per (query, head) as the
+    split plan uses them: batch 8 at 128K (256 work-groups of 64-block runs, runs cut
+    for the whole batch in up to 32 slots), batch 1 (32 runs of 8 blocks), batch 64 with
+    8192 selected blocks (128 runs per query, not 128 * 64)."""
+    ws = _lib.spot_sparse_attn_workspace_bytes
+    assert ws(8, 32, 8, 128, 256, 64) == 8 * 32 * 32 * 130 * 4
+    assert ws(1, 32, 8, 128, 256, 64) == 1 * 32 * 32 * 130 * 4
+    assert ws(64, 32, 8, 128, 8192, 64) == 64 * 32 * 128 * 130 * 4
+    assert ws(1, 8, 2, 64, 16, 64, torch.float32) == 1 * 8 * 4 * 66 * 4      # 4-block runs
+    assert ws(1, 8, 2, 64, 8192, 64, torch.float32) == 1 * 8 * 64 * 66 * 4   # <= 64 runs
+    assert ws(0, 32, 8, 128, 256) == 0
+    assert ws(8, 32, 8, 128, 256, 48) == 0                                  # no kernel
+    assert ws(8, 32, 8, 96, 256) == 0
+    assert ws(8, 30, 8, 128, 256) == 0
 
 
 def test_prefill_validation(lib):

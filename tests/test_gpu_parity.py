@@ -17,8 +17,8 @@ from block_sparse_long_spot_amd import workloads as W
 from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
 from oracle import spot_oracle as O
 from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
-                    assert_topp_unit, decode_selector, decoded_keys, decoded_query,
-                    gpu_sets, np64, score_magnitude)
+                    assert_topp_unit, attention_magnitude, decode_selector, decoded_keys,
+                    decoded_query, gpu_sets, np64, score_magnitude)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -339,7 +339,7 @@ def _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag, dirty_ws=False)
     scale = 1.0 / math.sqrt(d)
     out = torch.full((B, Hq, d), float("nan"), device=DEV).to(tdt)
     # workspace contents on entry do not matter: optionally start from all-NaN bytes
-    ws = torch.full((_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max),),
+    ws = torch.full((_lib.spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, tdt),),
                     255 if dirty_ws else 0, dtype=torch.uint8, device=DEV)
     idx_d, cnt_d = idx.to(DEV), cnt.to(DEV)
     _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx_d, cnt_d, out, ws, scale,
@@ -347,7 +347,16 @@ def _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag, dirty_ws=False)
     torch.cuda.synchronize()
     used = [[int(x) for x in idx[b, : int(cnt[b])]] for b in range(B)]
     ref = O.sparse_attention(np64(q), np64(K), np64(V), used, block, scale)
-    assert_out_close(np64(out), ref, tdt, tag=tag)
+    mag = _magnitudes(q, K, V, used, block, scale) if tdt == torch.bfloat16 else None
+    assert_out_close(np64(out), ref, tdt, tag=tag, mag=mag)
+
+
+def _magnitudes(q, K, V, used, block, scale, rows=None):
+    """(A, S, ez) of every (b, hq) row in order, for the bf16 rounding bound."""
+    B, Hq = q.shape[0], q.shape[1]
+    rows = [(b, h) for b in range(B) for h in range(Hq)] if rows is None else rows
+    m = attention_magnitude(q.float(), K, V, used, block, scale, rows)
+    return [m[r] for r in rows]
 
 
 def _batch_sweep(n=24, seed=4321):
@@ -401,14 +410,15 @@ def test_sparse_attn_batch_sweep(case):
         cnt[b] = c
     scale = 1.0 / math.sqrt(d)
     out = torch.full((B, Hq, d), float("nan"), device=DEV).bfloat16()
-    ws = torch.full((_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max),), 255,
+    ws = torch.full((_lib.spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block),), 255,
                     dtype=torch.uint8, device=DEV)
     _lib.spot_sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), cnt.to(DEV), out, ws,
                           scale, block=block)
     torch.cuda.synchronize()
     used = [[int(x) for x in idx[b, : int(cnt[b])]] for b in range(B)]
     ref = O.sparse_attention(np64(q), np64(K), np64(V), used, block, scale)
-    assert_out_close(np64(out), ref, torch.bfloat16, tag=str(case))
+    assert_out_close(np64(out), ref, torch.bfloat16, tag=str(case),
+                     mag=_magnitudes(q, K, V, used, block, scale))
 
 
 def test_sparse_attn_deterministic():
@@ -420,7 +430,7 @@ def test_sparse_attn_deterministic():
     idx = torch.stack([torch.randperm(256, generator=g)[:K_max].sort().values
                        for _ in range(B)]).int().to(DEV)
     cnt = torch.full((B,), K_max, dtype=torch.int32, device=DEV)
-    ws = torch.zeros(_lib.spot_sparse_attn_workspace_bytes(B, Hq, d, K_max), dtype=torch.uint8,
+    ws = torch.zeros(_lib.spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max), dtype=torch.uint8,
                      device=DEV)
     outs = []
     for _ in range(3):
@@ -435,7 +445,7 @@ def run_e2e(wl, inp_dev, check_rows=None, tag=""):
     """Run the three calls, then check scores, selection and (sampled) outputs."""
     B = inp_dev["q"].shape[0]
     dt = inp_dev["q"].dtype
-    bufs = DecodeBuffers(B, wl.nb, wl.Hq, wl.d, wl.K_max, dt)
+    bufs = DecodeBuffers.of(wl, dt, B=B)
     decode_step(inp_dev, wl, bufs)
     torch.cuda.synchronize()
     log(f"{tag}: GPU step done")
@@ -463,13 +473,24 @@ def run_e2e(wl, inp_dev, check_rows=None, tag=""):
     ref = O.sparse_attention(np64(inp_dev["q"]), Kr, Vr, sets, wl.block,
                              1.0 / math.sqrt(wl.d), heads=heads)
     got = np64(bufs.out)
-    if heads is None:
-        assert_out_close(got, ref, dt, tag=tag)
-    else:
-        for (b, h) in heads:
-            assert_out_close(got[b, h][None], ref[b, h][None], dt, tag=f"{tag} ({b},{h})")
+    scale = 1.0 / math.sqrt(wl.d)
+    rows = sorted(heads) if heads is not None else \
+        [(b, h) for b in range(B) for h in range(wl.Hq)]
+    mag = attention_magnitude(inp_dev["q"].float(), inp_dev["K"], inp_dev["V"], sets, wl.block,
+                              scale, rows) if dt == torch.bfloat16 else None
+    for (b, h) in rows:
+        assert_out_close(got[b, h][None], ref[b, h][None], dt, tag=f"{tag} ({b},{h})",
+                         mag=None if mag is None else [mag[(b, h)]])
     log(f"{tag}: outputs match")
     return bufs, sets
+
+
+def _every_kv_head(wl, B=None):
+    """One query head of every KV head group of every query (a different one of the
+    group from query to query), and the first and last heads."""
+    B = wl.B if B is None else B
+    rows = {(b, g * wl.G + (b + g) % wl.G) for b in range(B) for g in range(wl.Hkv)}
+    return sorted(rows | {(0, 0), (B - 1, wl.Hq - 1)})
 
 
 class _lazy_kv:
@@ -520,9 +541,7 @@ def big_inputs():
 def test_workload_full_size(name, big_inputs):
     wl = W.WORKLOADS[name]
     inp = big_inputs(name)
-    B = wl.B
-    rows = [(b, (5 * b + 3) % wl.Hq) for b in range(B)] + [(0, 0), (B - 1, wl.Hq - 1)]
-    bufs, sets = run_e2e(wl, inp, check_rows=rows, tag=name)
+    bufs, sets = run_e2e(wl, inp, check_rows=_every_kv_head(wl), tag=name)
     for s in sets:
         if wl.sel_k_dtype == "int4":
             # 4-bit keys add score noise that sharpens the distribution: the nucleus
@@ -538,8 +557,7 @@ def test_workload_static_topk_half(big_inputs):
     base = W.WORKLOADS["c3_128k_b8"]
     inp = big_inputs(base.name)
     wl = base.with_(p=0.0, K_min=base.nb // 2, K_max=base.nb // 2, n_sink=0, n_rec=0)
-    rows = [(b, (7 * b + 1) % wl.Hq) for b in range(wl.B)]
-    bufs, sets = run_e2e(wl, inp, check_rows=rows, tag="c3-static-half")
+    bufs, sets = run_e2e(wl, inp, check_rows=_every_kv_head(wl), tag="c3-static-half")
     assert all(len(s) == wl.nb // 2 for s in sets)
 
 
@@ -550,8 +568,7 @@ def test_workload_page_geometry(big_inputs):
     of the output."""
     wl = W.WORKLOADS["page_128k_b1"]
     inp = big_inputs(wl.name)
-    rows = [(0, 0), (0, 13), (0, 31)]
-    bufs, sets = run_e2e(wl, inp, check_rows=rows, tag=wl.name)
+    bufs, sets = run_e2e(wl, inp, check_rows=_every_kv_head(wl), tag=wl.name)
     n = len(sets[0])
     assert wl.K_min <= n < wl.nb // 2, n
 
@@ -565,7 +582,7 @@ def test_workload_selector_formats(kf, qf):
     wl = W.WORKLOADS["c3_128k_b8"].with_(B=2, sel_k_dtype=kf, sel_q_dtype=qf,
                                          name=f"c3_128k_b2_{kf}_{qf}")
     inp = W.make_inputs(wl, device=DEV)
-    bufs, sets = run_e2e(wl, inp, check_rows=[(0, 3), (1, 30)], tag=wl.name)
+    bufs, sets = run_e2e(wl, inp, check_rows=_every_kv_head(wl), tag=wl.name)
     assert all(wl.K_min <= len(s) <= wl.K_max for s in sets)
 
 
@@ -573,7 +590,7 @@ def test_workload_budgets_vary(big_inputs):
     """Zipf exponents spread over [1.3, 2.0] across the batch give different budgets."""
     wl = W.WORKLOADS["c3_128k_b8"].with_(zipf_spread=(1.3, 2.0), L=32768)
     inp = W.make_inputs(wl, device=DEV)
-    bufs, sets = run_e2e(wl, inp, check_rows=[(0, 1), (7, 30)], tag="c3-spread")
+    bufs, sets = run_e2e(wl, inp, check_rows=_every_kv_head(wl), tag="c3-spread")
     sizes = [len(s) for s in sets]
     assert len(set(sizes)) >= 4, sizes
 
@@ -583,7 +600,7 @@ def test_decode_step_bit_reproducible():
     inp = W.make_inputs(wl, device=DEV, seed=7)
     outs = []
     for _ in range(2):
-        bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+        bufs = DecodeBuffers.of(wl, torch.bfloat16)
         decode_step(inp, wl, bufs)
         outs.append((bufs.scores.cpu(), bufs.sel_idx.cpu(), bufs.out.cpu()))
     for a, b in zip(outs[0], outs[1]):
@@ -595,11 +612,11 @@ def test_graph_replay_matches_eager():
     synchronisations in between, reproduces the eager result bit for bit."""
     wl = W.WORKLOADS["c2_32k_b4"]
     inp = W.make_inputs(wl, device=DEV, seed=11)
-    eager = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+    eager = DecodeBuffers.of(wl, torch.bfloat16)
     decode_step(inp, wl, eager)
     torch.cuda.synchronize()
     ref = (eager.sel_idx.clone(), eager.sel_cnt.clone(), eager.out.clone())
-    bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+    bufs = DecodeBuffers.of(wl, torch.bfloat16)
     stream = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):

@@ -81,13 +81,13 @@ def test_two_streams_concurrently():
     ia, ib = W.make_inputs(wa, device=DEV, seed=5), W.make_inputs(wb, device=DEV, seed=6)
     ref = []
     for wl, inp in ((wa, ia), (wb, ib)):
-        bufs = DecodeBuffers(wl.B, wl.nb, wl.Hq, wl.d, wl.K_max, torch.bfloat16)
+        bufs = DecodeBuffers.of(wl, torch.bfloat16)
         decode_step(inp, wl, bufs)
         torch.cuda.synchronize()
         ref.append((bufs.sel_idx.clone(), bufs.out.clone()))
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    ba = DecodeBuffers(wa.B, wa.nb, wa.Hq, wa.d, wa.K_max, torch.bfloat16)
-    bb = DecodeBuffers(wb.B, wb.nb, wb.Hq, wb.d, wb.K_max, torch.bfloat16)
+    ba = DecodeBuffers.of(wa, torch.bfloat16)
+    bb = DecodeBuffers.of(wb, torch.bfloat16)
     for _ in range(20):
         decode_step(ia, wa, ba, stream=sa)
         decode_step(ib, wb, bb, stream=sb)

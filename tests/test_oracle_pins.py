@@ -238,6 +238,36 @@ def test_quantize_int4_roundtrip_and_recipe():
     assert (cz == 0).all() and (sz == 0).all()
 
 
+def test_quantize_int4_ties_to_even():
+    """Exact halves: a group whose largest magnitude is 7 has the scale fp16(7 / 7) = 1,
+    so x / scale = x and the tie rule decides the codes. Round half to even gives
+    0.5 -> 0, 1.5 -> 2, 2.5 -> 2, 3.5 -> 4, 4.5 -> 4, 5.5 -> 6, 6.5 -> 6 (and the
+    negatives mirrored); rounding half away from zero would give 1, 2, 3, 4, 5, 6, 7."""
+    vals = [7.0, 0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5, -0.5, -1.5, -2.5, -3.5, -4.5, -5.5,
+            -6.5, -7.0, 0.49, 0.51, -0.51, 2.4999998]
+    x = np.zeros((1, 32), np.float32)
+    x[0, :len(vals)] = vals
+    codes, scales = O.quantize_int4_g32(x)
+    assert scales[0, 0] == np.float16(1.0)
+    got = O.dequant_int4_g32(codes, scales)[0, :len(vals)]
+    want = [7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6, -7, 0, 1, -1, 2]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_quantize_int4_clamp_with_subnormal_scale():
+    """The clamp to [-8, 7] binds only when the fp16 scale rounds well below amax / 7,
+    which happens among fp16 subnormals (spacing 2^-24): amax = 9.8 * 2^-24 gives
+    amax / 7 = 1.4 * 2^-24, stored as 2^-24, so x / scale = +-9.8 rounds to +-10 and is
+    clamped to 7 and -8 (not to -7, and not left to wrap in a nibble)."""
+    a = np.float32(9.8 * 2.0 ** -24)
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [a, -a, np.float32(3.0 * 2.0 ** -24), np.float32(-2.5 * 2.0 ** -24)]
+    codes, scales = O.quantize_int4_g32(x)
+    assert scales[0, 0] == np.float16(2.0 ** -24)
+    got = O.dequant_int4_g32(codes, scales)[0, :4] / 2.0 ** -24
+    np.testing.assert_array_equal(got, [7, -8, 3, -2])
+
+
 def test_fp4_group_exponent_is_minimal():
     rng = np.random.default_rng(2)
     a = np.concatenate([rng.uniform(1e-3, 1e3, 500), 6.0 * 2.0 ** np.arange(-5, 6),
