@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     spot_select_score,
     spot_select_topp,
     spot_sparse_attn,
+    spot_sparse_attn_noalloc,
     spot_sparse_attn_workspace_bytes,
     status_string,
 )

@@ -52,6 +52,9 @@ def load() -> ctypes.CDLL:
     lib.spot_sparse_attn.argtypes = [vp, vp, vp, i, vp, vp, i, vp, vp, sz, i, i, i, i, i, i, f,
                                      vp]
     lib.spot_sparse_attn.restype = i
+    lib.spot_sparse_attn_noalloc.argtypes = [vp, vp, vp, i, vp, vp, i, vp, i, i, i, i, i, i, f,
+                                             vp]
+    lib.spot_sparse_attn_noalloc.restype = i
     lib.spot_prefill_select_score.argtypes = [vp, i, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i,
                                               i, vp]
     lib.spot_prefill_select_score.restype = i
@@ -200,6 +203,23 @@ def spot_sparse_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, workspace, sm_s
                                  workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, L,
                                  block, float(sm_scale), _stream(stream))
     _check("spot_sparse_attn", st)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SPOT_NOALLOC_SCRATCH_BYTES
+
+
+def spot_sparse_attn_noalloc(q, k_cache, v_cache, sel_idx, sel_cnt, out, sm_scale: float,
+                             block: int = 64, stream=None):
+    """spot_sparse_attn without a workspace argument: the library's per-GPU scratch array
+    holds the partial results, and nothing is allocated. Calls that may overlap on one
+    GPU must be ordered by the caller."""
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    K_max = sel_idx.shape[1]
+    st = load().spot_sparse_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
+                                         _ptr(sel_idx), _ptr(sel_cnt), K_max, _ptr(out), B, Hq,
+                                         Hkv, d, L, block, float(sm_scale), _stream(stream))
+    _check("spot_sparse_attn_noalloc", st)
 
 
 def _tiles(T: int, Tq) -> tuple:

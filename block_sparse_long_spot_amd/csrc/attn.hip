@@ -38,6 +38,7 @@
 //    all in fp32.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "spot_internal.h"
@@ -758,6 +759,44 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
                                        out, B, Hq, Hkv, L, block, qscale, sp, stream)
                  : launch_d<float, 128>(q, k_cache, v_cache, false, sel_idx, sel_cnt, K_max, ws,
                                         out, B, Hq, Hkv, L, block, qscale, sp, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free form
+// The workspace of spot_sparse_attn_noalloc: a file-scope device array (each GPU holds its
+// own copy from the moment the library's code is loaded on it until the process ends).
+// In host code `scratch` names a host-side stand-in, not a device address: the device
+// address of a GPU's copy comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    // the lookup runs with the stream's device current, then the caller's is restored
+    int cur = -1;
+    scratch_err[dev] = hipGetDevice(&cur);
+    if (scratch_err[dev] == hipSuccess && cur != dev) scratch_err[dev] = hipSetDevice(dev);
+    if (scratch_err[dev] == hipSuccess) {
+      void* p = nullptr;
+      scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      scratch_ptr[dev] = p;
+    }
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (scratch_err[dev] == hipSuccess) scratch_err[dev] = r;
+    }
+  });
+  *ptr = scratch_ptr[dev];
+  return scratch_err[dev];
 }
 
 }  // namespace spot

@@ -65,6 +65,35 @@ int check_selector(const void* sel_q, int q_dtype, const void* sel_q_scale, cons
   return SPOT_OK;
 }
 
+// The attention shapes this build has kernels for (after the argument checks).
+int attn_support(int Hq, int Hkv, int d, int block) {
+  const int G = Hq / Hkv;
+  if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;
+  if (block != 16 && block != 32 && block != 64 && block != 128) return SPOT_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
+  return SPOT_OK;
+}
+
+// Argument checks shared by spot_sparse_attn and spot_sparse_attn_noalloc (the
+// workspace pointer and size are checked by the caller).
+int check_sparse_attn(const void* q, const void* k_cache, const void* v_cache, int kv_dtype,
+                      const int32_t* sel_idx, const int32_t* sel_cnt, int K_max,
+                      const void* out, int B, int Hq, int Hkv, int d, int L, int block,
+                      float sm_scale) {
+  if (!q || !k_cache || !v_cache || !sel_idx || !sel_cnt || !out) return SPOT_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(sel_idx, 4) || !aligned(sel_cnt, 4))
+    return SPOT_ERR_INVALID;
+  if (kv_dtype != SPOT_F32 && kv_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || L <= 0 || block <= 0 || K_max <= 0)
+    return SPOT_ERR_INVALID;
+  if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
+  const int sup = attn_support(Hq, Hkv, d, block);
+  if (sup != SPOT_OK) return sup;
+  if (B > kMaxGrid || Hkv > kMaxGrid || (long)B * Hq > 2147483647L) return SPOT_ERR_UNSUPPORTED;
+  return SPOT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,15 +171,6 @@ int spot_quantize_selector(const void* src, int src_dtype, int n_rows, int row_l
                                                  as_stream(stream)));
 }
 
-// The attention shapes this build has kernels for (after the argument checks).
-int attn_support(int Hq, int Hkv, int d, int block) {
-  const int G = Hq / Hkv;
-  if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;
-  if (block != 16 && block != 32 && block != 64 && block != 128) return SPOT_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return SPOT_ERR_UNSUPPORTED;
-  return SPOT_OK;
-}
-
 size_t spot_sparse_attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block,
                                         int kv_dtype) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || K_max <= 0 || block <= 0) return 0;
@@ -163,24 +183,34 @@ int spot_sparse_attn(const void* q, const void* k_cache, const void* v_cache, in
                      const int32_t* sel_idx, const int32_t* sel_cnt, int K_max, void* out,
                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
                      int L, int block, float sm_scale, void* stream) {
-  if (!q || !k_cache || !v_cache || !sel_idx || !sel_cnt || !out || !workspace)
-    return SPOT_ERR_INVALID;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(sel_idx, 4) || !aligned(sel_cnt, 4) || !aligned(workspace, 256))
-    return SPOT_ERR_INVALID;
-  if (kv_dtype != SPOT_F32 && kv_dtype != SPOT_BF16) return SPOT_ERR_INVALID;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || L <= 0 || block <= 0 || K_max <= 0)
-    return SPOT_ERR_INVALID;
-  if (Hq % Hkv != 0 || !isfinite(sm_scale)) return SPOT_ERR_INVALID;
-  const int sup = attn_support(Hq, Hkv, d, block);
-  if (sup != SPOT_OK) return sup;
-  if (B > kMaxGrid || Hkv > kMaxGrid || (long)B * Hq > 2147483647L) return SPOT_ERR_UNSUPPORTED;
+  const int c = check_sparse_attn(q, k_cache, v_cache, kv_dtype, sel_idx, sel_cnt, K_max, out,
+                                  B, Hq, Hkv, d, L, block, sm_scale);
+  if (c != SPOT_OK) return c;
+  if (!workspace || !aligned(workspace, 256)) return SPOT_ERR_INVALID;
   if (workspace_bytes <
       spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, kv_dtype))
     return SPOT_ERR_INVALID;
   return from_hip(spot::launch_sparse_attn(q, k_cache, v_cache, kv_dtype == SPOT_BF16, sel_idx,
                                            sel_cnt, K_max, out, workspace, B, Hq, Hkv, d, L,
                                            block, sm_scale, as_stream(stream)));
+}
+
+int spot_sparse_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             int kv_dtype, const int32_t* sel_idx, const int32_t* sel_cnt,
+                             int K_max, void* out, int B, int Hq, int Hkv, int d, int L,
+                             int block, float sm_scale, void* stream) {
+  const int c = check_sparse_attn(q, k_cache, v_cache, kv_dtype, sel_idx, sel_cnt, K_max, out,
+                                  B, Hq, Hkv, d, L, block, sm_scale);
+  if (c != SPOT_OK) return c;
+  if (spot_sparse_attn_workspace_bytes(B, Hq, Hkv, d, K_max, block, kv_dtype) >
+      spot::kNoallocScratchBytes)
+    return SPOT_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const hipError_t e = spot::noalloc_scratch(as_stream(stream), &ws);
+  if (e != hipSuccess || !ws) return SPOT_ERR_DEVICE;
+  return from_hip(spot::launch_sparse_attn(q, k_cache, v_cache, kv_dtype == SPOT_BF16, sel_idx,
+                                           sel_cnt, K_max, out, ws, B, Hq, Hkv, d, L, block,
+                                           sm_scale, as_stream(stream)));
 }
 
 int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "spot.h"
+
 namespace spot {
 
 // Selector element formats (the values of the C ABI's spot_dtype codes).
@@ -38,6 +40,11 @@ struct AttnSplit {
 };
 AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path);
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block, bool bf16);
+
+// Size of the per-GPU device array behind spot_sparse_attn_noalloc, and its device
+// address on the stream's GPU (looked up on the first call for that GPU).
+constexpr size_t kNoallocScratchBytes = SPOT_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,

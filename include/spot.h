@@ -203,6 +203,27 @@ SPOT_API int spot_sparse_attn(const void* q, const void* k_cache, const void* v_
                               float sm_scale, void* stream);
 
 /*
+ * spot_sparse_attn_noalloc — for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, checks and result as spot_sparse_attn, without the workspace. The partial
+ * results go to a device array of SPOT_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on, from when its code is loaded there until the process ends; the
+ * first call for a GPU looks up that GPU's copy. No call allocates memory.
+ * Errors: as spot_sparse_attn; SPOT_ERR_UNSUPPORTED when the workspace these sizes need
+ * (spot_sparse_attn_workspace_bytes) exceeds the array (at 32 query heads of 128 dims
+ * and 256 selected blocks, batches up to 30); SPOT_ERR_DEVICE when the array's address
+ * cannot be found. All calls on one GPU share its array and nothing in it has to start
+ * at a given value: calls that can overlap on one GPU (other streams, other host
+ * threads) race with each other, and the caller must order them.
+ */
+#define SPOT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+SPOT_API int spot_sparse_attn_noalloc(const void* q, const void* k_cache,
+                                      const void* v_cache, int kv_dtype,
+                                      const int32_t* sel_idx, const int32_t* sel_cnt,
+                                      int K_max, void* out, int B, int Hq, int Hkv, int d,
+                                      int L, int block, float sm_scale, void* stream);
+
+/*
  * Prefill (§2.1 tile scoring; §6 names sparse prefill as the open direction). A batch
  * element holds T consecutive queries at positions q_pos0 .. q_pos0+T-1, cut into
  * tiles of Tq queries (the last one shorter): n_tiles = ceil(T / Tq). Tile t holds

@@ -27,7 +27,7 @@ def fake(addr=0x10000):
 
 def test_exports_match_header(lib):
     declared = _lib.declared_symbols()
-    assert len(declared) == 10
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -141,6 +141,28 @@ def test_sparse_attn_validation(lib):
     assert attn(lib, block=256) == UNSUPPORTED
     assert attn(lib, Hq=48, Hkv=3) == UNSUPPORTED           # 16 heads per KV head
     assert attn(lib, ws_bytes=4259839, B=8, Hq=32, Hkv=8, K_max=256) == INVALID   # one short
+
+
+def test_sparse_attn_noalloc_validation(lib):
+    """The allocation-free form checks what spot_sparse_attn checks, and refuses sizes
+    whose workspace would not fit its scratch array, before any HIP call."""
+    def na(**kw):
+        a = dict(q=fake(), k=fake(), v=fake(), kv_dtype=BF16, sel_idx=fake(), sel_cnt=fake(),
+                 K_max=16, out=fake(), B=1, Hq=8, Hkv=2, d=128, L=4096, block=64,
+                 sm_scale=0.125, stream=None)
+        a.update(kw)
+        return lib.spot_sparse_attn_noalloc(*a.values())
+    assert na(q=None) == INVALID
+    assert na(out=fake(0x10008)) == INVALID
+    assert na(Hq=6, Hkv=4) == INVALID
+    assert na(sm_scale=float("inf")) == INVALID
+    assert na(d=96) == UNSUPPORTED
+    assert na(block=48) == UNSUPPORTED
+    # 64 x 32 heads x 32 slots x 130 floats = 34 MB > 32 MiB
+    assert _lib.spot_sparse_attn_workspace_bytes(64, 32, 8, 128, 256) > _lib.NOALLOC_SCRATCH_BYTES
+    assert na(B=64, Hq=32, Hkv=8, K_max=256) == UNSUPPORTED
+    assert _lib.spot_sparse_attn_workspace_bytes(30, 32, 8, 128, 256) <= \
+        _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_sparse_attn_workspace_follows_the_split_plan(lib):
