@@ -29,7 +29,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
-SOURCES = ["capi.cpp", "score.hip", "topp.hip", "attn.hip", "prefill.hip", "quant.hip"]
+SOURCES = ["capi.cpp", "attn_plan.cpp", "score.hip", "topp.hip", "attn.hip", "prefill.hip",
+           "quant.hip"]
 PROBE_SRC = "read_ceiling.hip"
 PROBE_OUT = os.path.join(PKG, "libspot_probe.so")
 

@@ -37,7 +37,6 @@
 //    lane = token for q.K^T (64 tokens of a block at a time), lane = head dim for P.V,
 //    all in fp32.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
-#include <algorithm>
 #include <mutex>
 
 #include "device_common.h"
@@ -48,7 +47,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 64;  // tokens a wave consumes at a time (four 16-token tiles)
-constexpr int kFlatMaxB = 64;  // batches up to this size cut runs across queries
 
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(uint16_t x) { return bf16_to_f(x); }
@@ -708,39 +706,6 @@ hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
 }
 
 }  // namespace
-
-AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path) {
-  AttnSplit sp;
-  const long units = (long)B * Hkv;
-  if (!bf16_fast_path) {
-    // one wave per run: 4 blocks, or longer runs so that a row has at most 64 of them
-    sp.blocks_per_split = K_max > 256 ? (K_max + 63) / 64 : 4;
-  } else {
-    // the longest run (<= 4096 tokens, i.e. 64 chunks: at most 16 per wave, and at
-    // most 64 list entries per wave) that still gives >= 256 work-groups
-    int bps = 0;
-    for (int tokens = 4096; tokens >= 256 && bps == 0; tokens >>= 1) {
-      const int c = tokens / block;
-      if (units * ((K_max + c - 1) / c) >= 256) bps = c;
-    }
-    sp.blocks_per_split = bps > 0 ? bps : 256 / block;
-  }
-  sp.nsplit = (K_max + sp.blocks_per_split - 1) / sp.blocks_per_split;
-  // Runs across queries (MFMA path, 2 <= B <= kFlatMaxB): a query's runs fill its slots
-  // from 0, at most nslot of them. nsplit * B slots would let one long query take every
-  // work-group of the batch; max(nsplit, 32) keeps that freedom at small batches (it is
-  // nsplit * B up to batch 8 at 256 work-groups) and bounds the workspace at large ones.
-  sp.flat = bf16_fast_path && B >= 2 && B <= kFlatMaxB;
-  sp.nslot = sp.flat ? (int)std::min<long>((long)sp.nsplit * B, std::max(sp.nsplit, 32))
-                     : sp.nsplit;
-  return sp;
-}
-
-size_t attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block, bool bf16) {
-  // fp32 partial results and (m, l) per slot: nslot slots per (query, head)
-  const AttnSplit sp = attn_split_plan(B, Hkv, K_max, block, bf16);
-  return (size_t)B * Hq * (size_t)sp.nslot * ((size_t)d + 2) * sizeof(float);
-}
 
 hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                               bool bf16, const int32_t* sel_idx, const int32_t* sel_cnt,

@@ -223,6 +223,7 @@ int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w
   const int c = check_selector(sel_q, q_dtype, nullptr, sel_w, sel_k, sel_k_scale, k_dtype,
                                H_idx, d_idx, kpb);
   if (c != SPOT_OK) return c;
+  if ((long)q_pos0 + T > 2147483647L) return SPOT_ERR_INVALID;  // positions are int
   const long nb_seq = ((long)q_pos0 + T + block - 1) / block;
   if (nb_seq > nb_cache) return SPOT_ERR_INVALID;
   if (q_dtype != SPOT_BF16 || k_dtype != SPOT_BF16) return SPOT_ERR_UNSUPPORTED;
@@ -244,6 +245,7 @@ int spot_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel
   if (B <= 0 || T <= 0 || Tq <= 0 || q_pos0 < 0 || block <= 0 || K_max <= 0)
     return SPOT_ERR_INVALID;
   if (!isfinite(p) || n_sink < 0 || n_rec < 0 || K_min < 0) return SPOT_ERR_INVALID;
+  if ((long)q_pos0 + T > 2147483647L) return SPOT_ERR_INVALID;  // positions are int
   const long nb_seq = ((long)q_pos0 + T + block - 1) / block;
   if (nb_seq > 16384) return SPOT_ERR_UNSUPPORTED;
   const int nb = (int)nb_seq;

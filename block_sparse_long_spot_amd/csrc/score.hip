@@ -240,7 +240,7 @@ hipError_t launch_kf(const void* sel_q, int q_fmt, const void* sel_q_scale, cons
   int lpr_log2 = 0;
   while ((1 << lpr_log2) < lpr) ++lpr_log2;
   const int per_wg = 4 * (64 >> lpr_log2);
-  dim3 grid((nb + per_wg - 1) / per_wg, B), block(256);
+  dim3 grid((unsigned)(((long)nb + per_wg - 1) / per_wg), B), block(256);
 #define SPOT_SCORE(DIDX)                                                                   \
   hipLaunchKernelGGL((select_score_kernel<QF, KF, DIDX>), grid, block, 0, stream, sel_q,     \
                      q_fmt,                                                                 \

@@ -30,8 +30,9 @@ hipError_t launch_select_topp(const float* scores, int32_t* sel_idx, int32_t* se
                               float* sel_mass, int B, int nb, float p, int K_min, int K_max,
                               int n_sink, int n_rec, hipStream_t stream);
 
-// Split geometry of the decode attention: blocks per split (a power of two) and the
-// number of splits; a pure function of the sizes so the workspace bound holds.
+// Split geometry of the decode attention (attn_plan.cpp): blocks per run and the number
+// of runs per (query, KV head); a pure function of the sizes so the workspace bound holds.
+constexpr int kFlatMaxB = 64;  // bf16 batches up to this size cut runs across queries
 struct AttnSplit {
   int blocks_per_split;
   int nsplit;

@@ -244,7 +244,7 @@ SPOT_API int spot_sparse_attn_noalloc(const void* q, const void* k_cache,
  *   sel_k   [B][nb_cache][kpb][H_idx][d_idx] (16-byte aligned), sel_k_scale must be
  *           NULL;
  *   scores  out fp32 [B][n_tiles][nb_seq], nb_seq = ceil((q_pos0 + T) / block).
- * Errors: SPOT_ERR_INVALID when nb_seq > nb_cache or q_pos0 < 0.
+ * Errors: SPOT_ERR_INVALID when nb_seq > nb_cache, q_pos0 < 0 or q_pos0 + T > INT_MAX.
  * Supported: d_idx in {32, 64, 128}; bf16 queries and keys; 1 <= Tq <= 128;
  * B * n_tiles <= 65535.
  */
@@ -261,7 +261,8 @@ SPOT_API int spot_prefill_select_score(const void* sel_q, int q_dtype, const flo
  * tile"), and its sink the first n_sink blocks.
  *   sel_idx  out int32 [B][n_tiles][K_max]; sel_cnt out [B][n_tiles]; sel_mass optional
  *            out [B][n_tiles].
- * Errors and ordering as spot_select_topp (K_max must hold the largest reserved set).
+ * Errors and ordering as spot_select_topp (K_max must hold the largest reserved set);
+ * also SPOT_ERR_INVALID when q_pos0 + T > INT_MAX.
  * Supported: nb_seq <= 16384.
  */
 SPOT_API int spot_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,
