@@ -185,6 +185,34 @@ def time_flushed(inp, wl, bufs, reps, stream):
     return times
 
 
+def time_step_distribution(fn, n, warmup, stream):
+    """Per-step times of n back-to-back steps: one HIP event recorded on `stream` at every
+    step boundary (each adds a small gap, so the mean sits a little above the headline's
+    wall-clock mean). Returns median, p10, p90 and mean in us."""
+    torch.cuda.synchronize()  # inputs made on torch's default stream are complete
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+    return {"median": round(float(np.median(t)), 3), "p10": round(float(np.percentile(t, 10)), 3),
+            "p90": round(float(np.percentile(t, 90)), 3), "mean": round(float(t.mean()), 3),
+            "n": n}
+
+
+def quantiles(xs):
+    return {"median": round(statistics.median(xs), 3),
+            "p10": round(float(np.percentile(xs, 10)), 3),
+            "p90": round(float(np.percentile(xs, 90)), 3), "reps": len(xs)}
+
+
 def prefill_leg(steps, warmup, stream):
     """The 128-query prefill tile at 32K: tile scoring, top-p, causal sparse attention.
     Returns per-call µs and the attention's achieved TFLOP/s (algorithmic flops:
@@ -473,46 +501,55 @@ def read_ceiling(nbytes, stream, reps=20):
                     "16-byte non-temporal loads, no compute (csrc/read_ceiling.hip)"}
 
 
-def cpu_baseline(wl, inp, b_sample=1, heads_sample=None):
-    """The fp64 oracle (scoring, dual top-p, dense masked attention) on a bounded
-    sample: batch rows [0, b_sample), all heads, full L. Scaled to one whole step."""
+def cpu_baseline(wl, inp, b_sample, b_single=None):
+    """The fp64 oracle (scoring, dual top-p, dense masked attention over all L keys) on
+    batch rows [0, b_sample), all heads, full L: the median of 3 runs with the BLAS
+    thread pool at every core this process may run on, plus one run with a single thread
+    on rows [0, b_single). Inputs are copied to the host and widened to fp64 before the
+    clock starts, so only the oracle's arithmetic is timed; times are scaled to one whole
+    step of the batch."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import spot_oracle as O   # test infrastructure, CPU baseline only
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    sel_q = inp["sel_q"][:b_sample].to("cpu", torch.float64).numpy()
-    sel_w = inp["sel_w"][:b_sample].to("cpu", torch.float64).numpy()
+    cores = len(os.sched_getaffinity(0))
+    b_single = b_single or max(1, b_sample // 4)
+    f64 = lambda t: t[:b_sample].to("cpu").to(torch.float64).numpy()
+    sel_q, sel_w, q = f64(inp["sel_q"]), f64(inp["sel_w"]), f64(inp["q"])
     if inp["sel_k"].dtype == torch.uint8:
-        codes = inp["sel_k"][:b_sample].cpu().numpy()
-        scales = inp["sel_k_scale"][:b_sample].cpu().numpy()
+        keys = O.dequant_int4_g32(inp["sel_k"][:b_sample].cpu().numpy(),
+                                  inp["sel_k_scale"][:b_sample].cpu().numpy())
     else:
-        keys = inp["sel_k"][:b_sample].to("cpu", torch.float64).numpy()
-    q = inp["q"][:b_sample].to("cpu", torch.float64).numpy()
+        keys = f64(inp["sel_k"])
+    K, V = f64(inp["K"]), f64(inp["V"])
+    pf = float(np.float32(wl.p))
 
-    class KV:
-        def __init__(self, t):
-            self.t, self.shape = t, (b_sample,) + tuple(t.shape[1:])
+    def run(nb_rows):
+        t0 = time.perf_counter()
+        s = O.select_score(sel_q[:nb_rows], sel_w[:nb_rows], keys[:nb_rows])
+        sels, _ = O.select_topp(s, pf, wl.K_min, wl.K_max, wl.n_sink, wl.n_rec)
+        O.sparse_attention(q[:nb_rows], K[:nb_rows], V[:nb_rows], sels, wl.block,
+                           1 / math.sqrt(wl.d))
+        return time.perf_counter() - t0
 
-        def __getitem__(self, key):
-            b, g = key
-            return self.t[b, g].to("cpu", torch.float64).numpy()
-
-    t0 = time.perf_counter()
-    if inp["sel_k"].dtype == torch.uint8:
-        keys = O.dequant_int4_g32(codes, scales)
-    s = O.select_score(sel_q, sel_w, keys)
-    sels, _ = O.select_topp(s, float(np.float32(wl.p)), wl.K_min, wl.K_max, wl.n_sink, wl.n_rec)
-    O.sparse_attention(q, KV(inp["K"]), KV(inp["V"]), sels, wl.block, 1 / math.sqrt(wl.d))
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        runs = [run(b_sample) for _ in range(3)]
+    with threadpool_limits(limits=1):
+        one = run(b_single)
+    del K, V
     B = inp["q"].shape[0]
-    return {"value": dt * 1e6 * B / b_sample, "unit": "us", "cores": int(threads),
+    med = statistics.median(runs)
+    return {"value": round(med * 1e6 * B / b_sample, 1), "unit": "us", "cores": int(threads),
             "kind": "oracle",
+            "runs_s": [round(r, 3) for r in runs],
+            "single_thread": {"value": round(one * 1e6 * B / b_single, 1), "unit": "us",
+                              "cores": 1, "sample": f"batch rows 0..{b_single - 1}, one run "
+                                                    f"({one:.2f} s), scaled x{B / b_single:g}"},
             "sample": f"batch rows 0..{b_sample - 1} of {B} (all {wl.Hq} heads, L={wl.L}): "
-                      f"{dt:.2f} s measured, scaled x{B / b_sample:g} to one step; fp64 "
-                      "scoring, sort-based top-p and dense masked attention over all L keys, "
-                      "including the device-to-host copy of each K/V row it reads"}
+                      f"median of 3 runs ({med:.2f} s) with the BLAS pool at {threads} "
+                      f"threads ({cores} cores in the process affinity), scaled "
+                      f"x{B / b_sample:g} to one step; fp64 scoring, sort-based top-p and "
+                      "dense masked attention over all L keys; inputs copied to the host and "
+                      "widened to fp64 before timing"}
 
 
 def main():
@@ -577,6 +614,8 @@ def main():
     # headline: K whole steps launched back to back on one stream
     us_step, us_step_events = time_back_to_back(step, a.steps, a.warmup, stream)
     log(f"bench: {us_step:.1f} us/step wall, {us_step_events:.1f} us/step events")
+    step_stats = time_step_distribution(step, max(200, a.steps), a.warmup, stream)
+    log(f"bench: per-step events {step_stats}")
     tokens = selected_tokens(bufs.sel_idx, bufs.sel_cnt, wl.L, wl.block)
     budget = byte_budget(wl, wl.B, tokens)
     # dominant call: K attention calls back to back on the same stream, same selection
@@ -614,6 +653,8 @@ def main():
                      "GBps": round(budget["step"] / (us_step * 1e-6) / 1e9, 1),
                      "frac": round(budget["step"] / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                      "selected_tokens": tokens},
+        "queries_per_s": round(wl.B / (us_step * 1e-6), 1),
+        "step_us_stats": step_stats,
         "timing": "value = wall time of K steps launched back to back on one stream "
                   "(three library calls each, no host synchronisation or events between "
                   "them), bracketed by device synchronisations, divided by K; "
@@ -630,10 +671,7 @@ def main():
         "graph_replay_us_per_step": {"wall": round(g_wall, 3), "events": round(g_event, 3),
                                      "note": "one step per HIP graph; each graph launch "
                                              "adds a gap before its first kernel"},
-        "flushed_step_us": ({"median": round(statistics.median(flushed), 3),
-                             "p10": round(float(np.percentile(flushed, 10)), 3),
-                             "p90": round(float(np.percentile(flushed, 90)), 3),
-                             "reps": len(flushed)} if flushed else None),
+        "flushed_step_us": quantiles(flushed) if flushed else None,
         "pages_context": "paper: 3.9x FlashAttention, 1.8x Twilight end-to-end decode tok/s "
                          "at 128K on one NVIDIA B200 (not comparable to this metric)",
     }
@@ -647,16 +685,29 @@ def main():
         inp1 = {k: (v[:1].contiguous() if isinstance(v, torch.Tensor) else v)
                 for k, v in inp.items()}
         bufs1 = DecodeBuffers.of(wl1, dt)
-        u1, _ = time_back_to_back(lambda: decode_step(inp1, wl1, bufs1, stream=stream),
-                                  a.steps, a.warmup, stream)
+        step1 = lambda: decode_step(inp1, wl1, bufs1, stream=stream)
+        u1, _ = time_back_to_back(step1, a.steps, a.warmup, stream)
         w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
+        st1 = time_step_distribution(step1, max(200, a.steps), a.warmup, stream)
+        fl1 = time_flushed(inp1, wl1, bufs1, max(50, a.flushed_reps), stream)
         tok1 = selected_tokens(bufs1.sel_idx, bufs1.sel_cnt, wl1.L, wl1.block)
         b1 = byte_budget(wl1, 1, tok1)
-        result["batch1"] = {"us_per_step": round(u1, 3),
-                            "GBps": round(b1["step"] / (u1 * 1e-6) / 1e9, 1),
-                            "per_call_us_mean": {k: round(statistics.fmean(v), 3)
-                                                 for k, v in p1.items()},
-                            "note": "batch row 0 of the same inputs"}
+        fl1q = quantiles(fl1)
+        result["batch1"] = {
+            "us_per_step": round(u1, 3),
+            "GBps": round(b1["step"] / (u1 * 1e-6) / 1e9, 1),
+            "step_us_stats": st1,
+            "flushed_step_us": fl1q,
+            "flushed_hbm": {"algorithmic_bytes": b1["step"],
+                            "GBps": round(b1["step"] / (fl1q["median"] * 1e-6) / 1e9, 1),
+                            "frac": round(b1["step"] / (fl1q["median"] * 1e-6) / 1e9
+                                          / HBM_PEAK_GBPS, 4)},
+            "queries_per_s": round(1 / (u1 * 1e-6), 1),
+            "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in p1.items()},
+            "note": "batch row 0 of the same inputs. us_per_step / GBps: steps back to "
+                    "back, so the 68 MB a step reads partly come from the 256 MB last-level "
+                    "cache; flushed_step_us / flushed_hbm: a 1 GiB write between steps "
+                    "(outside the events), the HBM figure"}
         del inp1, bufs1
     if a.static and wl.name == "c3_128k_b8":
         log("bench: static top-K at half the context")
@@ -700,7 +751,8 @@ def main():
     result["calibration_copy_bytes"] = calibration_copy()
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, inp, b_sample=wl.B)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, b_sample=wl.B,
+                                              b_single=max(1, wl.B // 4))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
