@@ -28,7 +28,7 @@ import torch
 
 import block_sparse_long_spot_amd as spot
 from block_sparse_long_spot_amd import workloads as W
-from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
+from block_sparse_long_spot_amd.decode import DecodeBuffers, DecodeStep
 
 METRIC = "decode step µs (select+top-p+sparse attn) at L=128K; achieved HBM GB/s %peak"
 HBM_PEAK_GBPS = 8000.0
@@ -109,25 +109,22 @@ def time_back_to_back(fn, steps, warmup, stream):
 def time_steps(inp, wl, bufs, steps, warmup, stream):
     """Per-call breakdown: events between the three calls of every step. Each event adds
     a gap on the stream, so these per-call times are diagnostics, not the step time."""
+    step = DecodeStep(inp, wl, bufs, stream=stream)
     torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     for _ in range(warmup):
-        decode_step(inp, wl, bufs, stream=stream)
+        step()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    score, topp, attn = step.calls
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(steps):
             ev[i][0].record(stream)
-            spot.spot_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"],
-                                   inp.get("sel_k_scale"), bufs.scores, kpb=wl.kpb,
-                                   stream=stream, sel_q_scale=inp.get("sel_q_scale"))
+            score()
             ev[i][1].record(stream)
-            spot.spot_select_topp(bufs.scores, bufs.sel_idx, bufs.sel_cnt, bufs.sel_mass, wl.p,
-                                  wl.K_min, wl.K_max, wl.n_sink, wl.n_rec, stream=stream)
+            topp()
             ev[i][2].record(stream)
-            spot.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx, bufs.sel_cnt,
-                                  bufs.out, bufs.workspace, 1.0 / math.sqrt(wl.d),
-                                  block=wl.block, stream=stream)
+            attn()
             ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -145,11 +142,12 @@ def time_graph(inp, wl, bufs, steps, warmup, stream):
     """The same step captured once as a HIP graph and replayed: identical kernels and
     arguments, without per-launch host work between them."""
     g = torch.cuda.CUDAGraph()
+    step = DecodeStep(inp, wl, bufs, stream=stream)
     torch.cuda.synchronize()  # inputs made on torch's default stream are complete
-    decode_step(inp, wl, bufs, stream=stream)   # warm the code objects before capture
+    step()   # warm the code objects before capture
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=stream):
-        decode_step(inp, wl, bufs, stream=stream)
+        step()
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -169,6 +167,7 @@ def time_flushed(inp, wl, bufs, reps, stream):
     """Per-step time with a 1 GiB write between steps (outside the events), so that no
     step reads data left in the last-level caches by the previous one."""
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    step = DecodeStep(inp, wl, bufs, stream=stream)
     times = []
     torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     with torch.cuda.stream(stream):
@@ -177,7 +176,7 @@ def time_flushed(inp, wl, bufs, reps, stream):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            decode_step(inp, wl, bufs, stream=stream)
+            step()
             b.record(stream)
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) * 1e3)
@@ -205,6 +204,14 @@ def time_step_distribution(fn, n, warmup, stream):
     return {"median": round(float(np.median(t)), 3), "p10": round(float(np.percentile(t, 10)), 3),
             "p90": round(float(np.percentile(t, 90)), 3), "mean": round(float(t.mean()), 3),
             "n": n}
+
+
+def burst_stats(fn, steps, stream, reps=None):
+    """The headline measurement repeated: `reps` bursts of `steps` back-to-back steps, each
+    after one warm-up step and bracketed by device synchronisations; quantiles of the
+    per-step wall time over the bursts (no events inside a burst)."""
+    reps = reps or min(100, max(10, 2000 // steps))
+    return quantiles([time_back_to_back(fn, steps, 1, stream)[0] for _ in range(reps)])
 
 
 def quantiles(xs):
@@ -331,8 +338,7 @@ def static_topk_leg(inp, wl, steps, warmup, stream):
     K = wl.nb // 2
     ws = wl.with_(p=0.0, K_min=K, K_max=K, n_sink=0, n_rec=0)
     bufs = DecodeBuffers.of(ws, inp["q"].dtype)
-    us, _ = time_back_to_back(lambda: decode_step(inp, ws, bufs, stream=stream), steps,
-                              warmup, stream)
+    us, _ = time_back_to_back(DecodeStep(inp, ws, bufs, stream=stream), steps, warmup, stream)
     _, _, per = time_steps(inp, ws, bufs, max(10, steps // 10), warmup, stream)
     tok = selected_tokens(bufs.sel_idx, bufs.sel_cnt, ws.L, ws.block)
     bb = byte_budget(ws, ws.B, tok)
@@ -350,8 +356,7 @@ def budgets_vary_leg(wl, steps, warmup, stream):
     ws = wl.with_(zipf_spread=(1.3, 2.0))
     inp = W.make_inputs(ws, device="cuda")
     bufs = DecodeBuffers.of(ws, inp["q"].dtype)
-    us, _ = time_back_to_back(lambda: decode_step(inp, ws, bufs, stream=stream), steps,
-                              warmup, stream)
+    us, _ = time_back_to_back(DecodeStep(inp, ws, bufs, stream=stream), steps, warmup, stream)
     scale = 1.0 / math.sqrt(ws.d)
     attn_us, _ = time_back_to_back(
         lambda: spot.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx,
@@ -379,8 +384,7 @@ def page_geometry_step(steps, warmup, stream):
     wl = W.WORKLOADS["page_128k_b1"]
     inp = W.make_inputs(wl, device="cuda")
     bufs = DecodeBuffers.of(wl, inp["q"].dtype)
-    us, _ = time_back_to_back(lambda: decode_step(inp, wl, bufs, stream=stream), steps,
-                              warmup, stream)
+    us, _ = time_back_to_back(DecodeStep(inp, wl, bufs, stream=stream), steps, warmup, stream)
     _, _, per = time_steps(inp, wl, bufs, steps, warmup, stream)
     tok = selected_tokens(bufs.sel_idx, bufs.sel_cnt, wl.L, wl.block)
     bb = byte_budget(wl, wl.B, tok)
@@ -599,12 +603,9 @@ def main():
     log(f"bench: warmup {a.warmup}, timing {a.steps} steps")
     scale = 1.0 / math.sqrt(wl.d)
 
-    def step():
-        decode_step(inp, wl, bufs, stream=stream)
+    step = DecodeStep(inp, wl, bufs, stream=stream)
 
-    def attn_call():
-        spot.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx, bufs.sel_cnt,
-                              bufs.out, bufs.workspace, scale, block=wl.block, stream=stream)
+    attn_call = step.calls[2]
 
     # per-call breakdown first: a diagnostic pass of at least 500 steps (~50 ms), which
     # also brings the GPU out of its idle clocks before the headline pass
@@ -614,8 +615,10 @@ def main():
     # headline: K whole steps launched back to back on one stream
     us_step, us_step_events = time_back_to_back(step, a.steps, a.warmup, stream)
     log(f"bench: {us_step:.1f} us/step wall, {us_step_events:.1f} us/step events")
-    step_stats = time_step_distribution(step, max(200, a.steps), a.warmup, stream)
-    log(f"bench: per-step events {step_stats}")
+    step_stats = {"bursts": burst_stats(step, a.steps, stream),
+                  "per_step_events": time_step_distribution(step, max(200, a.steps), a.warmup,
+                                                            stream)}
+    log(f"bench: step statistics {step_stats}")
     tokens = selected_tokens(bufs.sel_idx, bufs.sel_cnt, wl.L, wl.block)
     budget = byte_budget(wl, wl.B, tokens)
     # dominant call: K attention calls back to back on the same stream, same selection
@@ -656,8 +659,11 @@ def main():
         "queries_per_s": round(wl.B / (us_step * 1e-6), 1),
         "step_us_stats": step_stats,
         "timing": "value = wall time of K steps launched back to back on one stream "
-                  "(three library calls each, no host synchronisation or events between "
-                  "them), bracketed by device synchronisations, divided by K; "
+                  "(three library calls each, arguments marshalled once, no host "
+                  "synchronisation or events between them), bracketed by device "
+                  "synchronisations, divided by K; step_us_stats.bursts = that "
+                  "measurement repeated; step_us_stats.per_step_events = an event at every "
+                  "step boundary (each event adds a gap of about 2 us); "
                   "roofline.avg_launch_us = HIP events on the same stream around K "
                   "back-to-back spot_sparse_attn calls, divided by K; per_call_us = a "
                   "separate pass with events between the calls (each event adds a gap)",
@@ -685,10 +691,12 @@ def main():
         inp1 = {k: (v[:1].contiguous() if isinstance(v, torch.Tensor) else v)
                 for k, v in inp.items()}
         bufs1 = DecodeBuffers.of(wl1, dt)
-        step1 = lambda: decode_step(inp1, wl1, bufs1, stream=stream)
+        step1 = DecodeStep(inp1, wl1, bufs1, stream=stream)
         u1, _ = time_back_to_back(step1, a.steps, a.warmup, stream)
         w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
-        st1 = time_step_distribution(step1, max(200, a.steps), a.warmup, stream)
+        st1 = {"bursts": burst_stats(step1, a.steps, stream),
+               "per_step_events": time_step_distribution(step1, max(200, a.steps), a.warmup,
+                                                         stream)}
         fl1 = time_flushed(inp1, wl1, bufs1, max(50, a.flushed_reps), stream)
         tok1 = selected_tokens(bufs1.sel_idx, bufs1.sel_cnt, wl1.L, wl1.block)
         b1 = byte_budget(wl1, 1, tok1)
@@ -719,8 +727,8 @@ def main():
         torch.cuda.empty_cache()
         inp4 = W.make_inputs(wl4, device="cuda")
         bufs4 = DecodeBuffers.of(wl4, dt)
-        u4, _ = time_back_to_back(lambda: decode_step(inp4, wl4, bufs4, stream=stream),
-                                  a.steps, a.warmup, stream)
+        u4, _ = time_back_to_back(DecodeStep(inp4, wl4, bufs4, stream=stream), a.steps,
+                                  a.warmup, stream)
         w4, _, p4 = time_steps(inp4, wl4, bufs4, a.steps, a.warmup, stream)
         g4, _ = time_graph(inp4, wl4, bufs4, a.steps, a.warmup, stream)
         tok4 = selected_tokens(bufs4.sel_idx, bufs4.sel_cnt, wl4.L, wl4.block)

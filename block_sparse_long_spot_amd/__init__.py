@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     SPOT_FP8_E4M3,
     SPOT_INT4_G32,
     SPOT_INT8,
+    Prepared,
     SpotError,
     load,
     selector_format,
@@ -25,4 +26,4 @@ from ._lib import (  # noqa: F401
     spot_sparse_attn_workspace_bytes,
     status_string,
 )
-from .decode import decode_step  # noqa: F401
+from .decode import DecodeStep, decode_step  # noqa: F401

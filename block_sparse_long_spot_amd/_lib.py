@@ -89,6 +89,30 @@ def _check(fn: str, status: int):
         raise SpotError(fn, status)
 
 
+class Prepared:
+    """One library call with its arguments marshalled once (pointers, sizes, stream).
+    Calling it issues the same C call again, argument checks and launches included,
+    without re-reading the tensors: for a caller that repeats a call on the same
+    buffers, as a decode loop does. The tensors must stay alive and in place."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name: str, args: tuple, keep: tuple = ()):
+        self.name, self.fn, self.args, self.keep = name, getattr(load(), name), args, keep
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SPOT_OK:
+            raise SpotError(self.name, st)
+
+
+def _issue(name: str, args: tuple, prepare: bool, keep: tuple = ()):
+    """Call entry point `name` with `args`, or return it as a Prepared call."""
+    if prepare:
+        return Prepared(name, args, keep)
+    _check(name, getattr(load(), name)(*args))
+
+
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
@@ -139,10 +163,11 @@ def selector_format(codes: torch.Tensor, scale: Optional[torch.Tensor]):
 
 
 def spot_select_score(sel_q, sel_w, sel_k, sel_k_scale, scores, kpb: int = 1, stream=None,
-                      sel_q_scale=None):
+                      sel_q_scale=None, prepare: bool = False):
     """scores[B][nb] <- selector block scores. sel_q [B][H][d_idx] and sel_k
     [B][nb][kpb][H][d_idx] in any selector format (see selector_format; 4-bit formats
-    store d_idx/2 bytes per row), each with its scale tensor or None."""
+    store d_idx/2 bytes per row), each with its scale tensor or None. prepare=True
+    returns the call as a Prepared object instead of issuing it."""
     B, H = sel_w.shape
     q_fmt, q_per = selector_format(sel_q, sel_q_scale)
     k_fmt, k_per = selector_format(sel_k, sel_k_scale)
@@ -150,10 +175,11 @@ def spot_select_score(sel_q, sel_w, sel_k, sel_k_scale, scores, kpb: int = 1, st
     assert sel_q.shape == (B, H, d_idx // q_per) and sel_k.shape[-1] * k_per == d_idx
     nb = scores.shape[1]
     assert scores.dtype == torch.float32 and sel_w.dtype == torch.float32
-    st = load().spot_select_score(_ptr(sel_q), q_fmt, _ptr(sel_q_scale), _ptr(sel_w),
-                                  _ptr(sel_k), _ptr(sel_k_scale), k_fmt, _ptr(scores), B, nb,
-                                  kpb, H, d_idx, _stream(stream))
-    _check("spot_select_score", st)
+    return _issue("spot_select_score",
+                  (_ptr(sel_q), q_fmt, _ptr(sel_q_scale), _ptr(sel_w), _ptr(sel_k),
+                   _ptr(sel_k_scale), k_fmt, _ptr(scores), B, nb, kpb, H, d_idx,
+                   _stream(stream)), prepare, (sel_q, sel_q_scale, sel_w, sel_k, sel_k_scale,
+                                               scores))
 
 
 _FORMATS = {"int4": SPOT_INT4_G32, "fp4": SPOT_FP4_E2M1_G32, "int8": SPOT_INT8,
@@ -174,14 +200,15 @@ def spot_quantize_selector(src, fmt: str, codes, scales=None, tensor_scale=None,
 
 
 def spot_select_topp(scores, sel_idx, sel_cnt, sel_mass, p: float, K_min: int, K_max: int,
-                     n_sink: int, n_rec: int, stream=None):
+                     n_sink: int, n_rec: int, stream=None, prepare: bool = False):
     """sel_idx[B][K_max] (ascending, -1 padded), sel_cnt[B], optional sel_mass[B]."""
     B, nb = scores.shape
     assert sel_idx.dtype == torch.int32 and sel_idx.shape == (B, K_max)
     assert sel_cnt.dtype == torch.int32
-    st = load().spot_select_topp(_ptr(scores), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_mass), B,
-                                 nb, float(p), K_min, K_max, n_sink, n_rec, _stream(stream))
-    _check("spot_select_topp", st)
+    return _issue("spot_select_topp",
+                  (_ptr(scores), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_mass), B, nb, float(p),
+                   K_min, K_max, n_sink, n_rec, _stream(stream)), prepare,
+                  (scores, sel_idx, sel_cnt, sel_mass))
 
 
 def spot_sparse_attn_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, K_max: int,
@@ -193,16 +220,17 @@ def spot_sparse_attn_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, K_max: i
 
 
 def spot_sparse_attn(q, k_cache, v_cache, sel_idx, sel_cnt, out, workspace, sm_scale: float,
-                     block: int = 64, stream=None):
+                     block: int = 64, stream=None, prepare: bool = False):
     """out[B][Hq][d] <- attention of q over the selected blocks of K/V [B][Hkv][L][d]."""
     B, Hq, d = q.shape
     Hkv, L = k_cache.shape[1], k_cache.shape[2]
     K_max = sel_idx.shape[1]
-    st = load().spot_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q),
-                                 _ptr(sel_idx), _ptr(sel_cnt), K_max, _ptr(out), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, L,
-                                 block, float(sm_scale), _stream(stream))
-    _check("spot_sparse_attn", st)
+    return _issue("spot_sparse_attn",
+                  (_ptr(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(q), _ptr(sel_idx),
+                   _ptr(sel_cnt), K_max, _ptr(out), _ptr(workspace),
+                   workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, L, block,
+                   float(sm_scale), _stream(stream)), prepare,
+                  (q, k_cache, v_cache, sel_idx, sel_cnt, out, workspace))
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # SPOT_NOALLOC_SCRATCH_BYTES

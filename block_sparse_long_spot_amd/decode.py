@@ -30,6 +30,28 @@ class DecodeBuffers:
                    out_dtype, device=device)
 
 
+class DecodeStep:
+    """The three calls of a decode step on fixed inputs and buffers, marshalled once
+    (each call still validates its arguments and launches its kernels every time)."""
+
+    def __init__(self, inp: dict, wl, bufs: DecodeBuffers, stream=None):
+        self.calls = (
+            _lib.spot_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"],
+                                   inp.get("sel_k_scale"), bufs.scores, kpb=wl.kpb,
+                                   stream=stream, sel_q_scale=inp.get("sel_q_scale"),
+                                   prepare=True),
+            _lib.spot_select_topp(bufs.scores, bufs.sel_idx, bufs.sel_cnt, bufs.sel_mass, wl.p,
+                                  wl.K_min, wl.K_max, wl.n_sink, wl.n_rec, stream=stream,
+                                  prepare=True),
+            _lib.spot_sparse_attn(inp["q"], inp["K"], inp["V"], bufs.sel_idx, bufs.sel_cnt,
+                                  bufs.out, bufs.workspace, 1.0 / math.sqrt(wl.d),
+                                  block=wl.block, stream=stream, prepare=True))
+
+    def __call__(self):
+        for c in self.calls:
+            c()
+
+
 def decode_step(inp: dict, wl, bufs: DecodeBuffers, stream=None):
     """Score every block, select each query's block set, attend over it."""
     _lib.spot_select_score(inp["sel_q"], inp["sel_w"], inp["sel_k"], inp.get("sel_k_scale"),

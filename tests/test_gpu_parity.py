@@ -14,7 +14,7 @@ import torch
 
 from block_sparse_long_spot_amd import _lib
 from block_sparse_long_spot_amd import workloads as W
-from block_sparse_long_spot_amd.decode import DecodeBuffers, decode_step
+from block_sparse_long_spot_amd.decode import DecodeBuffers, DecodeStep, decode_step
 from oracle import spot_oracle as O
 from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
                     assert_topp_unit, attention_magnitude, decode_selector, decoded_keys,
@@ -605,6 +605,27 @@ def test_decode_step_bit_reproducible():
         outs.append((bufs.scores.cpu(), bufs.sel_idx.cpu(), bufs.out.cpu()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_prepared_step_matches_decode_step():
+    """The decode step with its calls marshalled once (DecodeStep, what the benchmark
+    times) writes exactly what decode_step writes, call after call."""
+    wl = W.WORKLOADS["c2_32k_b4"]
+    inp = W.make_inputs(wl, device=DEV, seed=13)
+    ref = DecodeBuffers.of(wl, torch.bfloat16)
+    decode_step(inp, wl, ref)
+    bufs = DecodeBuffers.of(wl, torch.bfloat16)
+    stream = torch.cuda.Stream()
+    step = DecodeStep(inp, wl, bufs, stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        bufs.out.fill_(float("nan"))
+        bufs.sel_idx.fill_(-5)
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        for name in ("scores", "sel_idx", "sel_cnt", "sel_mass", "out"):
+            assert torch.equal(getattr(bufs, name), getattr(ref, name)), name
 
 
 def test_graph_replay_matches_eager():
