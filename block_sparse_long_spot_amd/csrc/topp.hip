@@ -198,15 +198,16 @@ __device__ void radix_select(const uint32_t (&key)[EPT], const u64 (&mass)[EPT],
 }
 
 // exp(s - mx) in 2^-29 fixed point. s - mx and its split into an integer and a
-// fraction are exact in fp64; only the fractional power of two is evaluated in fp32
-// (about 1 ulp), so the mass carries a relative error near 1e-7.
+// fraction are exact in fp64; only the fractional power of two is evaluated in fp32, by
+// the hardware exponential on [0, 1) (about 1 ulp), so the mass carries a relative error
+// near 1e-7. The result is at most 2^29.
 __device__ __forceinline__ u64 fixed_mass(float s, float mx) {
   const double t = (static_cast<double>(s) - static_cast<double>(mx)) * 1.4426950408889634;
   const double n = floor(t);
   if (n < -60.0) return 0ull;
   const float f = static_cast<float>(t - n);                            // in [0, 1)
-  const float v = ldexpf(exp2f(f), static_cast<int>(n) + kMassBits);   // <= 2^29
-  return static_cast<u64>(__float2ll_rn(v));
+  const float v = ldexpf(__builtin_amdgcn_exp2f(f), static_cast<int>(n) + kMassBits);
+  return static_cast<u64>(static_cast<uint32_t>(__builtin_rintf(v)));
 }
 
 // Rows of prefill tiles (n_tiles > 0): row b is tile b % n_tiles of a sequence of T
@@ -346,58 +347,79 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
     }
   }
   {
-    u64 P = before + incl - loc;  // packed prefix above this thread's first bin
+    // Target t (0: mass T, 1: count tl, 2: count th) is reached in the one bin whose
+    // prefix is below it and whose prefix plus content is not. Each thread finds its
+    // hit, if any, with selects over its bins; only the wave holding a hit stores it.
+    u64 Ps[BPT];  // packed prefix above each of this thread's bins
+    {
+      u64 P = before + incl - loc;
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int bin = tid * BPT + i;
-      const u64 pc = P >> kCntShift, pm = P & kMassMask;
-      const u64 c = hb[i] >> kCntShift, m = hb[i] & kMassMask;
-      if (T > 0 && pm < T && T <= pm + m) {
-        sh.f_bin[0] = bin;
-        sh.f_pre[0] = P;
-        sh.f_cnt[0] = c;
+      for (int i = 0; i < BPT; ++i) {
+        Ps[i] = P;
+        P += hb[i];
       }
-      if (tl > 0 && pc < (u64)tl && (u64)tl <= pc + c) {
-        sh.f_bin[1] = bin;
-        sh.f_pre[1] = P;
-        sh.f_cnt[1] = c;
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const u64 X = t == 0 ? T : static_cast<u64>(t == 1 ? tl : th);
+      if (X == 0) continue;  // uniform
+      int hit = -1;
+      u64 hpre = 0, hcnt = 0;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        const u64 below = t == 0 ? (Ps[i] & kMassMask) : (Ps[i] >> kCntShift);
+        const u64 in = t == 0 ? (hb[i] & kMassMask) : (hb[i] >> kCntShift);
+        const bool h = below < X && X <= below + in;
+        hit = h ? i : hit;
+        hpre = h ? Ps[i] : hpre;
+        hcnt = h ? (hb[i] >> kCntShift) : hcnt;
       }
-      if (th > 0 && pc < (u64)th && (u64)th <= pc + c) {
-        sh.f_bin[2] = bin;
-        sh.f_pre[2] = P;
-        sh.f_cnt[2] = c;
+      if (__ballot(hit >= 0) != 0 && hit >= 0) {
+        sh.f_bin[t] = tid * BPT + hit;
+        sh.f_pre[t] = hpre;
+        sh.f_cnt[t] = hcnt;
       }
-      P += hb[i];
     }
   }
   __syncthreads();  // barrier 4
   // ---- decide k, or the bin where it is decided
+  // the three found bins, read together
+  int fbin[3];
+  u64 fpre[3], fcnt[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    fbin[t] = sh.f_bin[t];
+    fpre[t] = sh.f_pre[t];
+    fcnt[t] = sh.f_cnt[t];
+  }
   int bk = -1;           // bin holding the k-th residual block in score order
   int fs = 0;            // which found slot describes bin bk
   bool need_kp = false;  // k still depends on the exact nucleus size inside bin bk
   if (n_res > 0) {
     if (T == 0) {
       if (k > 0) {
-        bk = sh.f_bin[1];
+        bk = fbin[1];
         fs = 1;
       }
     } else {
-      const int A0 = static_cast<int>(sh.f_pre[0] >> kCntShift);
-      const int C0 = static_cast<int>(sh.f_cnt[0]);
+      const int A0 = static_cast<int>(fpre[0] >> kCntShift);
+      const int C0 = static_cast<int>(fcnt[0]);
       const int k1 = clampk(A0 + 1), k2 = clampk(A0 + C0);
       if (k1 != k2) {
-        bk = sh.f_bin[0];
+        bk = fbin[0];
         need_kp = true;
       } else {
         k = k1;
         fs = k == th ? 2 : (k == tl ? 1 : 0);
-        if (k > 0) bk = sh.f_bin[fs];
+        if (k > 0) bk = fs == 2 ? fbin[2] : (fs == 1 ? fbin[1] : fbin[0]);
       }
     }
   }
-  const int A = bk >= 0 ? static_cast<int>(sh.f_pre[fs] >> kCntShift) : 0;
-  const int C = bk >= 0 ? static_cast<int>(sh.f_cnt[fs]) : 0;
-  const u64 PM = bk >= 0 ? (sh.f_pre[fs] & kMassMask) : 0;
+  const u64 fpre_s = fs == 2 ? fpre[2] : (fs == 1 ? fpre[1] : fpre[0]);
+  const u64 fcnt_s = fs == 2 ? fcnt[2] : (fs == 1 ? fcnt[1] : fcnt[0]);
+  const int A = bk >= 0 ? static_cast<int>(fpre_s >> kCntShift) : 0;
+  const int C = bk >= 0 ? static_cast<int>(fcnt_s) : 0;
+  const u64 PM = bk >= 0 ? (fpre_s & kMassMask) : 0;
 
   // ---- 4. exact order inside the boundary bin
   uint32_t tau = 0;
@@ -431,9 +453,15 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
       const int mi = act ? sh.gi[lane] : 0x7fffffff;
       const u64 mm = act ? sh.gm[lane] : 0ull;
       int rank = 0;
-      u64 cm = 0;  // mass of the blocks ranked before this one
-      if (C <= kRankRedundant) {
+      u64 cm = 0;  // mass of the blocks ranked before this one (needed for k_p only)
+      if (C <= kRankRedundant && !need_kp) {
         for (int j = 0; j < C; ++j) {  // j is uniform: broadcast block j from lane j
+          const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
+          const int ij = __builtin_amdgcn_readlane(mi, j);
+          rank += (kj > mk || (kj == mk && ij < mi)) ? 1 : 0;
+        }
+      } else if (C <= kRankRedundant) {
+        for (int j = 0; j < C; ++j) {
           const uint32_t kj = __builtin_amdgcn_readlane(mk, j);
           const int ij = __builtin_amdgcn_readlane(mi, j);
           const u64 gj = lane_value(mm, j);
@@ -467,7 +495,14 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
       }
       const bool chosen = act && rank < k - A;
       chosen_mask = __ballot(chosen);
-      inbin_mass = lane_value(wave_incl_scan(chosen ? mm : 0ull), 63);
+      if (sel_mass != nullptr) {  // the chosen lanes' masses (at most C <= 64 of them)
+        if (C <= kRankRedundant) {
+          for (u64 bits = chosen_mask; bits != 0; bits &= bits - 1)
+            inbin_mass += lane_value(mm, __builtin_ctzll(bits));
+        } else {
+          inbin_mass = lane_value(wave_incl_scan(chosen ? mm : 0ull), 63);
+        }
+      }
     } else {
       // dense boundary bin: exact radix select over the keys of that bin only
       fallback = true;
