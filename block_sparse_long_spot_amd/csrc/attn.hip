@@ -32,7 +32,10 @@
 //    B operand through gfx950's transposing LDS read. K and V are read once, so their
 //    loads are non-temporal (measured: ~7% more HBM throughput on this random-block
 //    gather than cached loads), and each wave loads the next chunk's K while it
-//    consumes the current one (~5% more).
+//    consumes the current one (~5% more). Runs of at most 8 chunks (one query at 128K:
+//    8 KV heads x 32 runs) use 8 waves of one chunk each instead, K and V issued
+//    together (206 registers, two waves per SIMD): one exposed load latency per wave
+//    instead of two (batch-1 split kernel 14.8 -> 14.2 us).
 //  * attn_generic (fp32 or bf16, any supported shape): one wave per run;
 //    lane = token for q.K^T (64 tokens of a block at a time), lane = head dim for P.V,
 //    all in fp32.
@@ -219,9 +222,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   const int row = lane & 15, kg = lane >> 4;  // MFMA operand coordinates
   const int dc = lane % DC, tg = lane / DC;   // V load coordinates
 
+  // With 8 waves there is no next-chunk K in flight: each wave loads K and V of its
+  // chunk together (one chunk per wave in the plans that use 8 waves).
+  constexpr bool PREFETCH = NW <= 4;
+  static_assert(G * D * 4 <= kChunk * VP * 2, "a wave's O fits in its V tile");
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NW][kChunk * VP];
   __shared__ float mm[NW][G], ll[NW][G];
-  __shared__ float accs[NW][G][D];
+  // a wave's final O goes to its own V tile, which it no longer reads
+  auto accs = [&](int w, int h, int dd) -> float& {
+    return reinterpret_cast<float*>(Vs[w])[h * D + dd];
+  };
   __shared__ float racc[G][D];
   __shared__ float rm[G], rl[G];
 
@@ -385,29 +395,41 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // Software pipeline over this wave's chunks: the next chunk's K loads are in flight
-    // while the current chunk is consumed.
-    int st[4] = {-1, -1, -1, -1};
-    bf16x8_t kb[4][KS];
-    if (n_mine > 0) {
-      tile_starts(0, st);
-      load_k(st, kb);
-    }
-    for (int i = 0; i < n_mine; ++i) {
-      u32x4_t vv[TPL];
-      load_v(st, vv);
-      int stn[4] = {-1, -1, -1, -1};
-      bf16x8_t kn[4][KS];
-      if (i + 1 < n_mine) {
-        tile_starts(i + 1, stn);
-        load_k(stn, kn);
+    if constexpr (PREFETCH) {
+      // Software pipeline over this wave's chunks: the next chunk's K loads are in
+      // flight while the current chunk is consumed.
+      int st[4] = {-1, -1, -1, -1};
+      bf16x8_t kb[4][KS];
+      if (n_mine > 0) {
+        tile_starts(0, st);
+        load_k(st, kb);
       }
-      if (any_token(st)) consume(st, kb, vv);
+      for (int i = 0; i < n_mine; ++i) {
+        u32x4_t vv[TPL];
+        load_v(st, vv);
+        int stn[4] = {-1, -1, -1, -1};
+        bf16x8_t kn[4][KS];
+        if (i + 1 < n_mine) {
+          tile_starts(i + 1, stn);
+          load_k(stn, kn);
+        }
+        if (any_token(st)) consume(st, kb, vv);
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        st[T] = stn[T];
+        for (int T = 0; T < 4; ++T) {
+          st[T] = stn[T];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
+          for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
+        }
+      }
+    } else {
+      for (int i = 0; i < n_mine; ++i) {
+        int st[4];
+        tile_starts(i, st);
+        bf16x8_t kb[4][KS];
+        load_k(st, kb);
+        u32x4_t vv[TPL];
+        load_v(st, vv);
+        if (any_token(st)) consume(st, kb, vv);
       }
     }
 
@@ -421,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
       const int h = 4 * kg + r;
       if (h < G) {
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) accs[wave][h][dt * 16 + row] = o[dt][r];
+        for (int dt = 0; dt < NT; ++dt) accs(wave, h, dt * 16 + row) = o[dt][r];
       }
     }
     __syncthreads();
@@ -436,7 +458,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
       for (int w = 0; w < NW; ++w) {
         const float sc = mm[w][h] == -INFINITY ? 0.f : exp2f(mm[w][h] - M);
         ls += sc * ll[w][h];
-        a += sc * accs[w][h][dd];
+        a += sc * accs(w, h, dd);
       }
       racc[h][dd] = a;
       if (dd == 0) {
@@ -537,17 +559,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
 
 // ---------------------------------------------------------------- merge of the runs
 // One work-group per (query, head); thread = head dim. The head's slots are read CH at
-// a time -- one memory round trip per CH runs -- and merged with an online rescale in
+// a time (32 when every slot holds a run, 8 when runs are marked) -- one memory round
+// trip per CH slots -- and merged with an online rescale in
 // slot order, up to nslot slots or (MARKED) the partial marked last, whichever comes
 // first; empty runs carry m = -inf. A row with no selected token (every m = -inf) gets
 // zeros. Marked slots are read 8 at a time: a query usually has few runs, and every
 // slot read past its last one is wasted bandwidth (measured: 16 at a time cost the
 // 128K batch-8 call 0.5 us).
-template <typename T, int D, bool MARKED>
+template <typename T, int D, bool MARKED, int CH>
 __global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ ws_acc,
                                                   const float2* __restrict__ ws_ml,
                                                   T* __restrict__ out, int nslot) {
-  constexpr int CH = MARKED ? 8 : 16;
   const int rowi = blockIdx.x;  // b * Hq + hq
   const float2* ml = ws_ml + (size_t)rowi * nslot;
   const float* ap = ws_acc + (size_t)rowi * nslot * D + threadIdx.x;
@@ -621,8 +643,6 @@ hipError_t launch_generic(const void* q, const void* k, const void* v, const int
   return hipGetLastError();
 }
 
-constexpr int kMfmaWaves = 4;
-
 template <int D, int G, int BS>
 hipError_t launch_mfma_bs(const void* q, const void* k, const void* v, const int32_t* sel_idx,
                           const int32_t* sel_cnt, int K_max, Ws ws, int B, int Hq, int Hkv,
@@ -632,17 +652,24 @@ hipError_t launch_mfma_bs(const void* q, const void* k, const void* v, const int
   const long chunks = BS >= kChunk ? (long)sp.blocks_per_split * (BS / kChunk)
                                    : (sp.blocks_per_split + entries_per_chunk - 1) /
                                          entries_per_chunk;
-  if ((chunks + kMfmaWaves - 1) / kMfmaWaves * entries_per_chunk > 64)
+  if ((chunks + sp.waves - 1) / sp.waves * entries_per_chunk > 64)
     return hipErrorNotSupported;  // a plan this kernel cannot hold (the plan never makes one)
-#define SPOT_MFMA(FLAT, GRID)                                                                 \
-  hipLaunchKernelGGL((attn_mfma<D, G, kMfmaWaves, BS, FLAT>), GRID, dim3(kMfmaWaves * 64), 0, \
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), \
+#define SPOT_MFMA(NW, FLAT, GRID)                                                             \
+  hipLaunchKernelGGL((attn_mfma<D, G, NW, BS, FLAT>), GRID, dim3(NW * 64), 0, stream,         \
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),        \
                      static_cast<const uint16_t*>(v), sel_idx, sel_cnt, K_max, ws.acc, ws.ml, \
                      Hq, Hkv, L, qscale, sp.blocks_per_split, sp.nsplit, B, sp.nslot)
-  if (sp.flat)
-    SPOT_MFMA(true, dim3(sp.nsplit, Hkv, B));
-  else
-    SPOT_MFMA(false, dim3(sp.nsplit, Hkv, B));
+  const dim3 grid(sp.nsplit, Hkv, B);
+  if (sp.waves == 8) {
+    if (sp.flat)
+      SPOT_MFMA(8, true, grid);
+    else
+      SPOT_MFMA(8, false, grid);
+  } else if (sp.flat) {
+    SPOT_MFMA(4, true, grid);
+  } else {
+    SPOT_MFMA(4, false, grid);
+  }
 #undef SPOT_MFMA
   return hipGetLastError();
 }
@@ -695,13 +722,17 @@ hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
 #undef SPOT_ARGS
   if (e != hipSuccess) return e;
   // runs across queries mark each query's last partial; per-query runs fill all nsplit
-  // slots (a fixed trip count, so the loads of every batch issue together)
+  // slots (a fixed trip count, so the loads of every batch issue together: up to 32
+  // slots in one round trip)
   if (sp.flat)
-    hipLaunchKernelGGL((attn_combine<T, D, true>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
+    hipLaunchKernelGGL((attn_combine<T, D, true, 8>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
                        ws.ml, static_cast<T*>(out), sp.nslot);
+  else if (sp.nslot <= 32)
+    hipLaunchKernelGGL((attn_combine<T, D, false, 32>), dim3(B * Hq), dim3(D), 0, stream,
+                       ws.acc, ws.ml, static_cast<T*>(out), sp.nslot);
   else
-    hipLaunchKernelGGL((attn_combine<T, D, false>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
-                       ws.ml, static_cast<T*>(out), sp.nslot);
+    hipLaunchKernelGGL((attn_combine<T, D, false, 16>), dim3(B * Hq), dim3(D), 0, stream,
+                       ws.acc, ws.ml, static_cast<T*>(out), sp.nslot);
   return hipGetLastError();
 }
 

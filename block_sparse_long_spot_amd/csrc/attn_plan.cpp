@@ -28,6 +28,10 @@ AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_p
   // from 0, at most nslot of them. nsplit * B slots would let one long query take every
   // work-group of the batch; max(nsplit, 32) keeps that freedom at small batches (it is
   // nsplit * B up to batch 8 at 256 work-groups) and bounds the workspace at large ones.
+  // Runs of at most 8 64-token chunks (few queries and KV heads, e.g. one query at 128K)
+  // go to 8 waves of one chunk each, K and V loaded together, instead of 4 waves of two
+  // chunks with the next K prefetched: every wave has one load latency instead of two.
+  sp.waves = bf16_fast_path && (long)sp.blocks_per_split * block <= 8 * 64 ? 8 : 4;
   sp.flat = bf16_fast_path && B >= 2 && B <= kFlatMaxB;
   sp.nslot = sp.flat ? (int)std::min<long>((long)sp.nsplit * B, std::max(sp.nsplit, 32))
                      : sp.nsplit;

@@ -70,8 +70,11 @@ __device__ __forceinline__ float fp4_dot2(uint32_t w, const float* q, float a) {
   return fmaf(q[2 * J + 1], v[1], a);
 }
 
-// QF: kF32 or kBF16 (vector loads of the query) or -1 (any format, element by element)
-template <int QF, int KF, int DIDX>
+// QF: kF32 or kBF16 (vector loads of the query) or -1 (any format, element by element).
+// R > 1 (one key per block only): each wave scores R consecutive groups of blocks, all
+// their key loads issued before any is used, so a launch needs R times fewer
+// work-groups for the same bytes in flight.
+template <int QF, int KF, int DIDX, int R>
 __global__ __launch_bounds__(256) void select_score_kernel(
     const void* __restrict__ sel_q, int q_fmt, const void* __restrict__ sel_q_scale,
     const float* __restrict__ sel_w, const void* __restrict__ sel_k,
@@ -87,7 +90,8 @@ __global__ __launch_bounds__(256) void select_score_kernel(
   const int part = gl % LPH;
   const int per_wave = 64 >> lpr_log2;
   const int b = blockIdx.y;
-  const int blk = (blockIdx.x * 4 + wave) * per_wave + (lane >> lpr_log2);
+  // first block of this lane group; round r adds r * per_wave
+  const int blk = ((blockIdx.x * 4 + wave) * R) * per_wave + (lane >> lpr_log2);
   const bool valid = blk < nb;
   const int blk_c = valid ? blk : nb - 1;  // lanes past the end read a valid row
 
@@ -175,9 +179,9 @@ __global__ __launch_bounds__(256) void select_score_kernel(
     // every lane of a head now holds that head's term; add the heads of the row
     return group_sum_dpp_rt<LPH>(wh * fmaxf(dot, 0.f), lpr_log2);
   };
-  // this lane's 16-byte chunk (two for fp32 keys) of key j, and its group scale
-  auto load_key = [&](int j, u32x4_t& raw, u32x4_t& raw2, uint32_t& sh) {
-    const size_t row = ((size_t)b * nb + blk_c) * kpb + j;
+  // this lane's 16-byte chunk (two for fp32 keys) of key j of block bc, and its group scale
+  auto load_key_of = [&](int bc, int j, u32x4_t& raw, u32x4_t& raw2, uint32_t& sh) {
+    const size_t row = ((size_t)b * nb + bc) * kpb + j;
     if constexpr (KF == kInt4 || KF == kFp4) {
       const uint8_t* cp = static_cast<const uint8_t*>(sel_k) + (row * H + head) * (DIDX / 2) +
                           part * 16;
@@ -200,6 +204,26 @@ __global__ __launch_bounds__(256) void select_score_kernel(
     }
   };
 
+  auto load_key = [&](int j, u32x4_t& raw, u32x4_t& raw2, uint32_t& sh) {
+    load_key_of(blk_c, j, raw, raw2, sh);
+  };
+  if constexpr (R > 1) {
+    // one key per block: R groups of blocks, loads first
+    u32x4_t r[R], r2[R];
+    uint32_t sc[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int bu = blk + u * per_wave;
+      load_key_of(bu < nb ? bu : nb - 1, 0, r[u], r2[u], sc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int bu = blk + u * per_wave;
+      const float v = key_score(r[u], r2[u], sc[u]);
+      if (bu < nb && gl == 0) scores[(size_t)b * nb + bu] = v;
+    }
+    return;
+  }
   // Keys of a block are read KU at a time so their loads overlap (per-token keys): 8
   // (16 for the 4-bit formats, whose key rows are shortest) keep enough bytes in flight
   // per wave (measured at 16 bf16 keys of 4 x 128 per block: 8 at a time 5 % faster
@@ -240,16 +264,25 @@ hipError_t launch_kf(const void* sel_q, int q_fmt, const void* sel_q_scale, cons
   int lpr_log2 = 0;
   while ((1 << lpr_log2) < lpr) ++lpr_log2;
   const int per_wg = 4 * (64 >> lpr_log2);
-  dim3 grid((unsigned)(((long)nb + per_wg - 1) / per_wg), B), block(256);
-#define SPOT_SCORE(DIDX)                                                                   \
-  hipLaunchKernelGGL((select_score_kernel<QF, KF, DIDX>), grid, block, 0, stream, sel_q,     \
-                     q_fmt,                                                                 \
-                     sel_q_scale, sel_w, sel_k, sel_k_scale, scores, nb, kpb, H, lpr_log2)
+  // one key per block and more than 1024 work-groups of one round: 4 rounds per wave
+  const long wg1 = ((long)nb + per_wg - 1) / per_wg * B;
+  const int R = kpb == 1 && wg1 > 1024 ? 4 : 1;
+  dim3 grid((unsigned)(((long)nb + per_wg * R - 1) / (per_wg * R)), B), block(256);
+#define SPOT_SCORE(DIDX, RR)                                                                 \
+  hipLaunchKernelGGL((select_score_kernel<QF, KF, DIDX, RR>), grid, block, 0, stream, sel_q,   \
+                     q_fmt, sel_q_scale, sel_w, sel_k, sel_k_scale, scores, nb, kpb, H,       \
+                     lpr_log2)
+#define SPOT_SCORE_R(DIDX) \
+  if (R == 4)              \
+    SPOT_SCORE(DIDX, 4);   \
+  else                     \
+    SPOT_SCORE(DIDX, 1);
   switch (d_idx) {
-    case 32: SPOT_SCORE(32); break;
-    case 64: SPOT_SCORE(64); break;
-    default: SPOT_SCORE(128); break;
+    case 32: SPOT_SCORE_R(32); break;
+    case 64: SPOT_SCORE_R(64); break;
+    default: SPOT_SCORE_R(128); break;
   }
+#undef SPOT_SCORE_R
 #undef SPOT_SCORE
   return hipGetLastError();
 }

@@ -38,6 +38,7 @@ struct AttnSplit {
   int nsplit;
   bool flat;  // runs cut across queries (the MFMA path at small batch)
   int nslot;  // partial-result slots per (query, head)
+  int waves;  // waves per work-group of the MFMA path: 8 (one chunk each) or 4
 };
 AttnSplit attn_split_plan(int B, int Hkv, int K_max, int block, bool bf16_fast_path);
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int d, int K_max, int block, bool bf16);
