@@ -313,6 +313,19 @@ def prefill_sequence_leg(steps, warmup, stream):
 
     us_total, _ = time_back_to_back(whole, steps, warmup, stream)
     per = {k: round(time_back_to_back(f, steps, warmup, stream)[0], 3) for k, f in calls.items()}
+    # the same whole-prompt tile scoring with the selector key cache quantised (§5.3)
+    fmts = {}
+    raw_k = sel_k.float()
+    for fmt in ("int4", "fp4", "int8", "fp8"):
+        codes, ks = W.quantize_selector(raw_k, fmt)
+        nbytes = codes.numel() * codes.element_size() + (
+            ks.numel() * ks.element_size() if ks.numel() > 1 else 0)
+        us, _ = time_back_to_back(
+            lambda: spot.spot_prefill_select_score(sel_q, sel_w, codes, scores, 0, Tq=Tq,
+                                                   stream=stream, sel_k_scale=ks),
+            steps, warmup, stream)
+        fmts[fmt] = {"us": round(us, 3), "key_bytes": nbytes}
+    fmts["bf16"] = {"us": per["score"], "key_bytes": sel_k.numel() * 2}
     whole()
     torch.cuda.synchronize()
     ic, cc = idx.cpu().numpy()[0], cnt.cpu().numpy()[0]
@@ -325,6 +338,7 @@ def prefill_sequence_leg(steps, warmup, stream):
     flops = 4.0 * d * vis * wl.Hq
     dense = 4.0 * d * wl.Hq * T * (T + 1) / 2
     return {"T": T, "tiles": n_tiles, "us_total": round(us_total, 3), "per_call_us": per,
+            "score_by_key_format": fmts,
             "selected_blocks_mean": round(float(cc.mean()), 2),
             "attn_flops": flops, "dense_causal_flops": dense,
             "flop_fraction_of_dense": round(flops / dense, 5),

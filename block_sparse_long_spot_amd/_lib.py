@@ -256,18 +256,22 @@ def _tiles(T: int, Tq) -> tuple:
 
 
 def spot_prefill_select_score(sel_q, sel_w, sel_k, scores, q_pos0: int, block: int = 64,
-                              kpb: int = 1, Tq: Optional[int] = None, stream=None):
+                              kpb: int = 1, Tq: Optional[int] = None, stream=None,
+                              sel_k_scale=None):
     """scores[B][n_tiles][nb_seq] (or [B][nb_seq] for one tile) <- tile block scores of
-    the T queries of sel_q [B][T][H][d_idx] at positions q_pos0.., in tiles of Tq
-    (default: one tile of T)."""
+    the T queries of sel_q [B][T][H][d_idx] (bf16) at positions q_pos0.., in tiles of Tq
+    (default: one tile of T). sel_k [B][nb_cache][kpb][H][..] in bf16 or a quantised
+    selector format with its scale tensor (see selector_format)."""
     B, T, H, d_idx = sel_q.shape
     Tq, n_tiles = _tiles(T, Tq)
     nb_cache = sel_k.shape[1]
     nb_seq = -(-(q_pos0 + T) // block)
     assert scores.numel() == B * n_tiles * nb_seq and scores.dtype == torch.float32
+    k_fmt, k_per = selector_format(sel_k, sel_k_scale)
+    assert sel_k.shape[-1] * k_per == d_idx
     st = load().spot_prefill_select_score(_ptr(sel_q), _dtype_code(sel_q), _ptr(sel_w),
-                                          _ptr(sel_k), None, _dtype_code(sel_k), _ptr(scores), B,
-                                          T, Tq, q_pos0, nb_cache, kpb, H, d_idx, block,
+                                          _ptr(sel_k), _ptr(sel_k_scale), k_fmt, _ptr(scores),
+                                          B, T, Tq, q_pos0, nb_cache, kpb, H, d_idx, block,
                                           _stream(stream))
     _check("spot_prefill_select_score", st)
 

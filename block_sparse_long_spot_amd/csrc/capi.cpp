@@ -226,12 +226,13 @@ int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w
   if ((long)q_pos0 + T > 2147483647L) return SPOT_ERR_INVALID;  // positions are int
   const long nb_seq = ((long)q_pos0 + T + block - 1) / block;
   if (nb_seq > nb_cache) return SPOT_ERR_INVALID;
-  if (q_dtype != SPOT_BF16 || k_dtype != SPOT_BF16) return SPOT_ERR_UNSUPPORTED;
+  if (q_dtype != SPOT_BF16 || k_dtype == SPOT_F32) return SPOT_ERR_UNSUPPORTED;
   const long rows = (long)B * ((T + Tq - 1) / Tq);
   if (Tq > 128 || rows > kMaxGrid) return SPOT_ERR_UNSUPPORTED;
-  return from_hip(spot::launch_prefill_select_score(sel_q, sel_w, sel_k, scores, B, T, Tq,
-                                                    q_pos0, nb_cache, (int)nb_seq, kpb, H_idx,
-                                                    d_idx, block, as_stream(stream)));
+  return from_hip(spot::launch_prefill_select_score(sel_q, sel_w, sel_k, sel_k_scale, k_dtype,
+                                                    scores, B, T, Tq, q_pos0, nb_cache,
+                                                    (int)nb_seq, kpb, H_idx, d_idx, block,
+                                                    as_stream(stream)));
 }
 
 int spot_prefill_select_topp(const float* scores, int32_t* sel_idx, int32_t* sel_cnt,

@@ -58,12 +58,101 @@ __device__ __forceinline__ TileRow tile_row(int r, int n_tiles, int T, int Tq, i
 // 128: 49 us with 4 groups, 42 with 8, 38 with 16, 37 with 32).
 constexpr int kScoreMaxCG = 32;
 
-template <int DIDX>
+// The B operand of one MFMA k-step of a key row: this lane's 8 elements of d_idx
+// (32s + 8kg .. +7), held as loaded and turned into exact bf16 values before use.
+// bf16 keys load 16 bytes; 4-bit codes 4 bytes (8 nibbles, even element low); 8-bit
+// codes 8 bytes. INT4 codes, FP4 (E2M1) and FP8 (E4M3) values and INT8 codes are all
+// exact in bf16, so the product with a bf16 query is exact in the fp32 accumulator and
+// the scale is applied to the k-step's dot (per 32-element group) or to the head's dot
+// (per tensor), as the format defines the value: code * scale.
+template <int KF>
+struct KeyRaw {
+  typedef typename std::conditional<
+      KF == kBF16, bf16x8_t,
+      typename std::conditional<KF == kInt4 || KF == kFp4, uint32_t, u32x2_t>::type>::type T;
+};
+
+template <int KF>
+__device__ __forceinline__ typename KeyRaw<KF>::T load_key_raw(const void* sel_k, size_t row,
+                                                              int didx, int s, int kg) {
+  // row = index of (b, block, key, head); element offset of this lane's 8 values
+  const size_t e = row * didx + s * 32 + kg * 8;
+  if constexpr (KF == kBF16) {
+    return *reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(sel_k) + e);
+  } else if constexpr (KF == kInt4 || KF == kFp4) {
+    return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(sel_k) + e / 2);
+  } else {
+    return *reinterpret_cast<const u32x2_t*>(static_cast<const uint8_t*>(sel_k) + e);
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_of_small_int(int v) {  // |v| <= 256: exact
+  return static_cast<uint16_t>(__float_as_uint(static_cast<float>(v)) >> 16);
+}
+
+template <int KF>
+__device__ __forceinline__ bf16x8_t decode_key(typename KeyRaw<KF>::T w) {
+  if constexpr (KF == kBF16) {
+    return w;
+  } else if constexpr (KF == kFp4) {
+    u32x4_t o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+    return __builtin_bit_cast(bf16x8_t, o);
+  } else if constexpr (KF == kFp8) {
+    u32x4_t o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
+    return __builtin_bit_cast(bf16x8_t, o);
+  } else {
+    u32x4_t o;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      int lo, hi;
+      if constexpr (KF == kInt4) {  // nibbles 2n (low) and 2n + 1, sign-extended
+        lo = static_cast<int>(w << (28 - 8 * n)) >> 28;
+        hi = static_cast<int>(w << (24 - 8 * n)) >> 28;
+      } else {                      // kInt8: bytes 2n and 2n + 1 of the 8
+        const uint32_t word = w[n / 2];
+        lo = static_cast<int8_t>((word >> (16 * (n % 2))) & 0xff);
+        hi = static_cast<int8_t>((word >> (16 * (n % 2) + 8)) & 0xff);
+      }
+      o[n] = static_cast<uint32_t>(bf16_of_small_int(lo)) |
+             (static_cast<uint32_t>(bf16_of_small_int(hi)) << 16);
+    }
+    return __builtin_bit_cast(bf16x8_t, o);
+  }
+}
+
+// The group scale of key row `row` (b, block, key, head), group s, for the group formats
+// (INT4: IEEE fp16; FP4: E8M0); 1 otherwise.
+template <int KF>
+__device__ __forceinline__ float key_group_scale(const void* scale, size_t row, int didx,
+                                                 int s) {
+  if constexpr (KF == kInt4) {
+    return half_bits_to_f(static_cast<const uint16_t*>(scale)[row * (didx / 32) + s]);
+  } else if constexpr (KF == kFp4) {
+    const uint32_t x = static_cast<const uint8_t*>(scale)[row * (didx / 32) + s];
+    return __uint_as_float(x ? (x << 23) : 0x00400000u);  // 2^(x - 127)
+  } else {
+    return 1.f;
+  }
+}
+
+template <int KF, int DIDX>
 __global__ __launch_bounds__(256) void prefill_score_kernel(
     const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
-    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int T, int Tq,
-    int n_tiles, int q_pos0, int nb_cache, int nb_stride, int kpb, int block, int CG) {
+    const void* __restrict__ sel_k, const void* __restrict__ sel_k_scale,
+    float* __restrict__ scores, int T, int Tq, int n_tiles, int q_pos0, int nb_cache,
+    int nb_stride, int kpb, int block, int CG) {
   constexpr int H = 4, KS = DIDX / 32, NWV = 4, RPW = 2;
+  constexpr bool GROUPS = KF == kInt4 || KF == kFp4;   // one scale per 32 elements
+  constexpr bool TENSOR = KF == kInt8 || KF == kFp8;   // one scale for the tensor
+  typedef typename KeyRaw<KF>::T Raw;
   __shared__ float colmax[NWV][kScoreMaxCG * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
@@ -76,6 +165,8 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   const uint16_t* qb = sel_q + ((size_t)b * T + tr.qs) * H * DIDX;
   const float* wb = sel_w + ((size_t)b * T + tr.qs) * H;
   const bool w16 = (reinterpret_cast<uintptr_t>(sel_w) & 15) == 0;
+  float tscale = 1.f;
+  if constexpr (TENSOR) tscale = *static_cast<const float*>(sel_k_scale);
 
   // A operands (query row = lane % 16) and weights (queries kg*4 + r) of row tiles
   // wave and wave + NWV
@@ -107,26 +198,35 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     }
   }
   // B operands of item i = (column group i / kpb, key i % kpb): column = block
-  auto load_keys = [&](int i, bf16x8_t (&kop)[H][KS]) {
+  auto load_keys = [&](int i, Raw (&kop)[H][KS], float (&ksc)[H][KS]) {
     const int cg = i / kpb, j = i - cg * kpb;
     const int blk_c = min(base + cg * 16 + col, nb_vis - 1);
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const uint16_t* kp =
-          sel_k + ((((size_t)b * nb_cache + blk_c) * kpb + j) * H + h) * DIDX + kg * 8;
+      const size_t row = (((size_t)b * nb_cache + blk_c) * kpb + j) * H + h;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kop[h][s] = *reinterpret_cast<const bf16x8_t*>(kp + s * 32);
+      for (int s = 0; s < KS; ++s) {
+        kop[h][s] = load_key_raw<KF>(sel_k, row, DIDX, s, kg);
+        if constexpr (GROUPS) ksc[h][s] = key_group_scale<KF>(sel_k_scale, row, DIDX, s);
+      }
     }
   };
   const int n_items = n_cg * kpb;
-  bf16x8_t kop[H][KS];
-  load_keys(0, kop);
+  Raw kop[H][KS];
+  float ksc[H][KS];
+  load_keys(0, kop, ksc);
   float cur = -INFINITY;  // max over (visible query, key) of the current column group
   for (int i = 0; i < n_items; ++i) {  // uniform
-    bf16x8_t kn[H][KS];
-    if (i + 1 < n_items) load_keys(i + 1, kn);
+    Raw kn[H][KS];
+    float kns[H][KS];
+    if (i + 1 < n_items) load_keys(i + 1, kn, kns);
     const int cg = i / kpb;
     const int blk = base + cg * 16 + col;
+    bf16x8_t kd[H][KS];
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kd[h][s] = decode_key<KF>(kop[h][s]);
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
       const int rt = wave + u * NWV;
@@ -135,9 +235,24 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 #pragma unroll
       for (int h = 0; h < H; ++h) {
         floatx4_t c = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GROUPS) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[u][h][s], kop[h][s], c, 0, 0, 0);
+          for (int s = 0; s < KS; ++s) {
+            const floatx4_t z = {0.f, 0.f, 0.f, 0.f};
+            const floatx4_t cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[u][h][s], kd[h][s],
+                                                                         z, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c[r] = fmaf(cs[r], ksc[h][s], c[r]);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[u][h][s], kd[h][s], c, 0, 0, 0);
+          if constexpr (TENSOR) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c[r] *= tscale;
+          }
+        }
         // c[r] = S_h[query rt*16 + kg*4 + r][column col]
 #pragma unroll
         for (int r = 0; r < 4; ++r) tot[r] += wq[u][r][h] * fmaxf(c[r], 0.f);
@@ -157,7 +272,10 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 #pragma unroll
     for (int h = 0; h < H; ++h)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kop[h][s] = kn[h][s];
+      for (int s = 0; s < KS; ++s) {
+        kop[h][s] = kn[h][s];
+        if constexpr (GROUPS) ksc[h][s] = kns[h][s];
+      }
   }
   __syncthreads();
   if (wave == 0 && kg == 0) {
@@ -174,12 +292,15 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
 }
 
 // Any H: heads looped at run time (slower path for selector head counts other than 4).
-template <int DIDX>
+template <int KF, int DIDX>
 __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
     const uint16_t* __restrict__ sel_q, const float* __restrict__ sel_w,
-    const uint16_t* __restrict__ sel_k, float* __restrict__ scores, int T, int Tq,
-    int n_tiles, int q_pos0, int nb_cache, int nb_stride, int kpb, int H, int block) {
+    const void* __restrict__ sel_k, const void* __restrict__ sel_k_scale,
+    float* __restrict__ scores, int T, int Tq, int n_tiles, int q_pos0, int nb_cache,
+    int nb_stride, int kpb, int H, int block) {
   constexpr int KS = DIDX / 32;
+  constexpr bool GROUPS = KF == kInt4 || KF == kFp4;
+  constexpr bool TENSOR = KF == kInt8 || KF == kFp8;
   const int lane = threadIdx.x;
   const int col = lane & 15, kg = lane >> 4;
   const TileRow tr = tile_row(blockIdx.y, n_tiles, T, Tq, q_pos0, block, nb_stride);
@@ -190,25 +311,35 @@ __global__ __launch_bounds__(64) void prefill_score_kernel_anyh(
   const int n_rt = (Tq_t + 15) / 16;
   const uint16_t* qb = sel_q + ((size_t)b * T + tr.qs) * H * DIDX;
   const float* wb = sel_w + ((size_t)b * T + tr.qs) * H;
+  float tscale = 1.f;
+  if constexpr (TENSOR) tscale = *static_cast<const float*>(sel_k_scale);
   float best = -INFINITY;
   for (int j = 0; j < kpb; ++j) {
     for (int rt = 0; rt < n_rt; ++rt) {
       floatx4_t tot = {0.f, 0.f, 0.f, 0.f};
       for (int h = 0; h < H; ++h) {
-        const uint16_t* kp =
-            sel_k + ((((size_t)b * nb_cache + blk_c) * kpb + j) * H + h) * DIDX + kg * 8;
+        const size_t row = (((size_t)b * nb_cache + blk_c) * kpb + j) * H + h;
         const int qr = min(rt * 16 + col, Tq_t - 1);
         const uint16_t* qp = qb + ((size_t)qr * H + h) * DIDX + kg * 8;
         floatx4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              *reinterpret_cast<const bf16x8_t*>(qp + s * 32),
-              *reinterpret_cast<const bf16x8_t*>(kp + s * 32), c, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8_t kd = decode_key<KF>(load_key_raw<KF>(sel_k, row, DIDX, s, kg));
+          const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qp + s * 32);
+          if constexpr (GROUPS) {
+            const floatx4_t z = {0.f, 0.f, 0.f, 0.f};
+            const floatx4_t cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kd, z, 0, 0, 0);
+            const float sc = key_group_scale<KF>(sel_k_scale, row, DIDX, s);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c[r] = fmaf(cs[r], sc, c[r]);
+          } else {
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kd, c, 0, 0, 0);
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qi = min(rt * 16 + kg * 4 + r, Tq_t - 1);
-          tot[r] += wb[(size_t)qi * H + h] * fmaxf(c[r], 0.f);
+          tot[r] += wb[(size_t)qi * H + h] * fmaxf(c[r] * tscale, 0.f);
         }
       }
 #pragma unroll
@@ -578,23 +709,21 @@ __global__ __launch_bounds__(G * S * 64, G * S == 4 ? 2 : 1) void prefill_attn_k
   }
 }
 
-}  // namespace
-
-hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
-                                       const void* sel_k, float* scores, int B, int T, int Tq,
-                                       int q_pos0, int nb_cache, int nb_stride, int kpb, int H,
-                                       int d_idx, int block, hipStream_t stream) {
+template <int KF>
+hipError_t launch_prefill_score_kf(const uint16_t* q, const float* sel_w, const void* k,
+                                   const void* k_scale, float* scores, int B, int T, int Tq,
+                                   int q_pos0, int nb_cache, int nb_stride, int kpb, int H,
+                                   int d_idx, int block, hipStream_t stream) {
   const int n_tiles = (T + Tq - 1) / Tq;
-  const uint16_t* q = static_cast<const uint16_t*>(sel_q);
-  const uint16_t* k = static_cast<const uint16_t*>(sel_k);
   const long groups = (nb_stride + 15) / 16;  // 16-block column groups
   if (H == 4) {
     // several column groups per work-group once there are work-groups to spare
     const int CG = (long)B * n_tiles * groups >= 2048 ? kScoreMaxCG : 1;
     dim3 grid(static_cast<unsigned>((groups + CG - 1) / CG), B * n_tiles);
-#define SPOT_PS4(DI)                                                                          \
-  hipLaunchKernelGGL((prefill_score_kernel<DI>), grid, dim3(256), 0, stream, q, sel_w, k,     \
-                     scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, block, CG)
+#define SPOT_PS4(DI)                                                                         \
+  hipLaunchKernelGGL((prefill_score_kernel<KF, DI>), grid, dim3(256), 0, stream, q, sel_w, k, \
+                     k_scale, scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb,      \
+                     block, CG)
     switch (d_idx) {
       case 32: SPOT_PS4(32); break;
       case 64: SPOT_PS4(64); break;
@@ -603,17 +732,39 @@ hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
 #undef SPOT_PS4
   } else {
     dim3 grid(static_cast<unsigned>(groups), B * n_tiles);
-#define SPOT_PSA(DI)                                                                       \
-  hipLaunchKernelGGL((prefill_score_kernel_anyh<DI>), grid, dim3(64), 0, stream, q, sel_w, \
-                     k, scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, kpb, H, block)
+#define SPOT_PSA(DI)                                                                          \
+  hipLaunchKernelGGL((prefill_score_kernel_anyh<KF, DI>), grid, dim3(64), 0, stream, q,       \
+                     sel_w, k, k_scale, scores, T, Tq, n_tiles, q_pos0, nb_cache, nb_stride, \
+                     kpb, H, block)
     switch (d_idx) {
       case 32: SPOT_PSA(32); break;
       case 64: SPOT_PSA(64); break;
       default: SPOT_PSA(128); break;
     }
-  }
 #undef SPOT_PSA
+  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
+                                       const void* sel_k, const void* sel_k_scale, int k_fmt,
+                                       float* scores, int B, int T, int Tq, int q_pos0,
+                                       int nb_cache, int nb_stride, int kpb, int H, int d_idx,
+                                       int block, hipStream_t stream) {
+  const uint16_t* q = static_cast<const uint16_t*>(sel_q);
+#define SPOT_PKF(KF)                                                                         \
+  return launch_prefill_score_kf<KF>(q, sel_w, sel_k, sel_k_scale, scores, B, T, Tq, q_pos0, \
+                                     nb_cache, nb_stride, kpb, H, d_idx, block, stream)
+  switch (k_fmt) {
+    case kInt4: SPOT_PKF(kInt4);
+    case kFp4: SPOT_PKF(kFp4);
+    case kInt8: SPOT_PKF(kInt8);
+    case kFp8: SPOT_PKF(kFp8);
+    default: SPOT_PKF(kBF16);
+  }
+#undef SPOT_PKF
 }
 
 hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v_cache,

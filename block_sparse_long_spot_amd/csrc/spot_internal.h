@@ -56,9 +56,10 @@ hipError_t launch_sparse_attn(const void* q, const void* k_cache, const void* v_
 // Prefill: a sequence of T query rows per batch element, cut into tiles of Tq rows
 // (T == Tq: one tile); score rows are [B][n_tiles][nb_stride].
 hipError_t launch_prefill_select_score(const void* sel_q, const float* sel_w,
-                                       const void* sel_k, float* scores, int B, int T, int Tq,
-                                       int q_pos0, int nb_cache, int nb_stride, int kpb, int H,
-                                       int d_idx, int block, hipStream_t stream);
+                                       const void* sel_k, const void* sel_k_scale, int k_fmt,
+                                       float* scores, int B, int T, int Tq, int q_pos0,
+                                       int nb_cache, int nb_stride, int kpb, int H, int d_idx,
+                                       int block, hipStream_t stream);
 
 hipError_t launch_prefill_attn(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* sel_idx, const int32_t* sel_cnt, int K_max,

@@ -241,12 +241,15 @@ SPOT_API int spot_sparse_attn_noalloc(const void* q, const void* k_cache,
  * Entries blk >= nb_t of a row are not written. Computed as one matrix product per
  * selector head on the MFMA units.
  *   sel_q   [B][T][H_idx][d_idx] (q_dtype), sel_w fp32 [B][T][H_idx];
- *   sel_k   [B][nb_cache][kpb][H_idx][d_idx] (16-byte aligned), sel_k_scale must be
- *           NULL;
+ *   sel_k   [B][nb_cache][kpb][H_idx][..] in k_dtype with sel_k_scale, laid out as for
+ *           spot_select_score (16-byte aligned): bf16, or the quantised cache formats
+ *           SPOT_INT4_G32, SPOT_FP4_E2M1_G32, SPOT_INT8, SPOT_FP8_E4M3 (§5.3: the
+ *           quantised selector's savings apply in prefill too);
  *   scores  out fp32 [B][n_tiles][nb_seq], nb_seq = ceil((q_pos0 + T) / block).
- * Errors: SPOT_ERR_INVALID when nb_seq > nb_cache, q_pos0 < 0 or q_pos0 + T > INT_MAX.
- * Supported: d_idx in {32, 64, 128}; bf16 queries and keys; 1 <= Tq <= 128;
- * B * n_tiles <= 65535.
+ * Errors: SPOT_ERR_INVALID when nb_seq > nb_cache, q_pos0 < 0 or q_pos0 + T > INT_MAX,
+ * or as spot_select_score for the formats and scales.
+ * Supported: d_idx in {32, 64, 128}; bf16 queries; keys in any format but fp32;
+ * 1 <= Tq <= 128; B * n_tiles <= 65535.
  */
 SPOT_API int spot_prefill_select_score(const void* sel_q, int q_dtype, const float* sel_w,
                                        const void* sel_k, const void* sel_k_scale,

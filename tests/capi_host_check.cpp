@@ -57,9 +57,9 @@ hipError_t launch_sparse_attn(const void*, const void*, const void*, bool, const
   g_last_B = B;
   return hipSuccess;
 }
-hipError_t launch_prefill_select_score(const void*, const float*, const void*, float*, int B,
-                                       int, int, int, int, int, int, int, int, int,
-                                       hipStream_t) {
+hipError_t launch_prefill_select_score(const void*, const float*, const void*, const void*,
+                                       int, float*, int B, int, int, int, int, int, int, int,
+                                       int, int, hipStream_t) {
   ++g_launches;
   g_last_B = B;
   return hipSuccess;
@@ -289,6 +289,11 @@ int main() {
   expect("prefill score pos0 + T overflow", INV, 0, [] {
     PScore a; a.pos0 = big; a.nb_cache = big; return a(); });
   expect("prefill score fp32", UNS, 0, [] { PScore a; a.qd = SPOT_F32; return a(); });
+  expect("prefill score fp32 keys", UNS, 0, [] { PScore a; a.kd = SPOT_F32; return a(); });
+  expect("prefill score int4 keys", OK, 1, [] { PScore a; a.kd = SPOT_INT4_G32; a.ks = P();
+                                                return a(); });
+  expect("prefill score int4 keys without scales", INV, 0, [] { PScore a; a.kd = SPOT_INT4_G32;
+                                                                return a(); });
   expect("prefill topp ok", OK, 1, PTopp{});
   expect("prefill topp K_max < r", INV, 0, [] { PTopp a; a.K_max = 4; return a(); });
   expect("prefill topp long", UNS, 0, [] { PTopp a; a.T = big - 64; return a(); });

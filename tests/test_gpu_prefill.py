@@ -10,7 +10,7 @@ from block_sparse_long_spot_amd import _lib
 from block_sparse_long_spot_amd import workloads as W
 from oracle import spot_oracle as O
 from parity import (assert_out_close, assert_scores_close, assert_selection_e2e,
-                    assert_topp_unit, gpu_sets, np64, tile_score_magnitude)
+                    assert_topp_unit, decode_selector, gpu_sets, np64, tile_score_magnitude)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -54,6 +54,52 @@ def test_prefill_score_parity(case):
     ref = O.prefill_tile_score(np64(sel_q), np64(sel_w), np64(sel_k), q_pos0, 64)
     mag = tile_score_magnitude(np64(sel_q), np64(sel_w), np64(sel_k), q_pos0, 64)
     assert_scores_close(np64(scores), ref, mag)
+
+
+QUANT_SCORE_CASES = [
+    # key format, B, T, Tq, q_pos0, nb_cache, kpb, H, d_idx (T == Tq: one tile)
+    ("int4", 1, 128, 128, 32640, 512, 1, 4, 64),
+    ("fp4", 1, 128, 128, 32640, 512, 1, 4, 64),
+    ("int8", 2, 40, 40, 1000, 20, 1, 4, 64),
+    ("fp8", 2, 40, 40, 1000, 20, 2, 4, 128),
+    ("int4", 1, 100, 100, 5000, 100, 3, 4, 32),
+    ("fp4", 1, 64, 64, 4095, 70, 1, 8, 32),          # any-H path
+    ("int4", 1, 17, 17, 0, 1, 2, 2, 128),             # any-H path, one block
+    # a whole sequence in tiles (>= 2048 tile x column-group pairs: many groups per
+    # work-group)
+    ("int4", 1, 8192, 128, 24576, 512, 1, 4, 64),
+    ("fp4", 1, 8192, 128, 24576, 512, 1, 4, 64),
+    ("fp8", 2, 4000, 100, 28000, 500, 1, 4, 64),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_SCORE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_score_quantised_keys(case):
+    """Tile scores with the selector key cache in the quantised formats of §5.3, against
+    the oracle's tile scores on the same codes decoded (a bf16 query)."""
+    fmt, B, T, Tq, q_pos0, nb_cache, kpb, H, di = case
+    log(f"prefill score quantised {case}")
+    if T > Tq:   # the launch takes the path with many column groups per work-group
+        assert B * (-(-T // Tq)) * -(-(-(-(q_pos0 + T) // 64)) // 16) >= 2048
+    g = torch.Generator().manual_seed(T + q_pos0 + di)
+    sel_q = torch.randn(B, T, H, di, generator=g).bfloat16()
+    sel_w = torch.randn(B, T, H, generator=g)                 # signed weights
+    codes, kscale = W.quantize_selector(torch.randn(B, nb_cache, kpb, H, di, generator=g), fmt)
+    n_tiles = -(-T // Tq)
+    nb_seq = -(-(q_pos0 + T) // 64)
+    scores = torch.full((B, n_tiles, nb_seq), float("nan"), device=DEV)
+    _lib.spot_prefill_select_score(sel_q.to(DEV), sel_w.to(DEV), codes.to(DEV), scores, q_pos0,
+                                   block=64, kpb=kpb, Tq=Tq, sel_k_scale=kscale.to(DEV))
+    torch.cuda.synchronize()
+    keys = decode_selector(codes, kscale)
+    sq, sw, gs = np64(sel_q), np64(sel_w), np64(scores)
+    for t in sorted({0, n_tiles // 2, n_tiles - 1}):
+        q0, q1 = t * Tq, min((t + 1) * Tq, T)
+        nb_t = -(-(q_pos0 + q1) // 64)
+        ref = O.prefill_tile_score(sq[:, q0:q1], sw[:, q0:q1], keys, q_pos0 + q0, 64)
+        assert_scores_close(gs[:, t, :nb_t], ref,
+                            tile_score_magnitude(sq[:, q0:q1], sw[:, q0:q1], keys, q_pos0 + q0,
+                                                 64))
 
 
 SEQ_SCORE_CASES = [
