@@ -477,6 +477,30 @@ def calibration_copy():
     return n * 4
 
 
+PROBE_SRC = os.path.join(ROOT, "read_ceiling.hip")
+PROBE_LIB = os.path.join(ROOT, "libspot_probe.so")
+
+
+def build_read_ceiling(verbose=False):
+    """Compile the read-only reference kernel (read_ceiling.hip, beside this file) into
+    libspot_probe.so, a library of its own: it is the benchmark's yardstick, not part of
+    the decode path."""
+    import shutil
+    import subprocess
+    hipcc = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 def read_ceiling(nbytes, stream, reps=20):
     """What a kernel that only reads sustains on this GPU for the attention's access
     pattern: about `nbytes` as 16 KiB blocks (one 64-token block of one KV head at
@@ -484,7 +508,7 @@ def read_ceiling(nbytes, stream, reps=20):
     non-temporal loads, no compute. Best of 256, 512 and 1024 work-groups, HIP events
     around `reps` back-to-back launches on `stream`."""
     import ctypes
-    lib = ctypes.CDLL(os.path.join(os.path.dirname(spot.__file__), "libspot_probe.so"))
+    lib = ctypes.CDLL(PROBE_LIB)
     lib.spot_probe_read_blocks.restype = ctypes.c_int
     lib.spot_probe_read_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -516,7 +540,7 @@ def read_ceiling(nbytes, stream, reps=20):
     best = max(v["GBps"] for v in per.values())
     return {"GBps": best, "bytes": n * blk, "per_workgroups": per,
             "what": "read-only kernel, the same bytes as 16 KiB blocks in random order, "
-                    "16-byte non-temporal loads, no compute (csrc/read_ceiling.hip)"}
+                    "16-byte non-temporal loads, no compute (read_ceiling.hip)"}
 
 
 def cpu_baseline(wl, inp, b_sample, b_single=None):

@@ -31,8 +31,6 @@ FLAGS = [
 ]
 SOURCES = ["capi.cpp", "attn_plan.cpp", "score.hip", "topp.hip", "attn.hip", "prefill.hip",
            "quant.hip"]
-PROBE_SRC = "read_ceiling.hip"
-PROBE_OUT = os.path.join(PKG, "libspot_probe.so")
 
 
 def _compile(src: str) -> str:
@@ -54,15 +52,8 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
-    # the benchmark's read-bandwidth reference, a library of its own
-    pobj = _compile(PROBE_SRC)
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", PROBE_OUT + ".tmp", pobj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
     if verbose:
-        print(f"built {OUT} and {PROBE_OUT}")
+        print(f"built {OUT}")
     return OUT
 
 

@@ -219,7 +219,7 @@ def test_read_reference_probe_validation():
     """The benchmark's read-only reference kernel lives in its own library: it exports its
     one entry point and rejects bad arguments before any launch (no GPU needed)."""
     import os
-    path = os.path.join(os.path.dirname(_lib.__file__), "libspot_probe.so")
+    path = os.path.join(os.path.dirname(os.path.dirname(_lib.__file__)), "libspot_probe.so")
     probe = ctypes.CDLL(path)
     f = probe.spot_probe_read_blocks
     f.restype = ctypes.c_int
