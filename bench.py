@@ -84,26 +84,44 @@ def profiled_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def time_back_to_back(fn, steps, warmup, stream):
+def time_back_to_back(fn, steps, warmup, stream, events=True):
     """K calls of `fn` enqueued back to back on `stream`, after `warmup` untimed ones,
     bracketed by device synchronisations. Returns (wall us per call, HIP-event us per
-    call) with the two events recorded on `stream` around the K calls."""
+    call) with the two events recorded on `stream` around the K calls; with
+    events=False none are recorded (each adds a gap on the stream) and the second value
+    is None."""
     torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        a.record(stream)
+        torch.cuda.synchronize()
+        if events:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        if events:
+            a.record(stream)
         for _ in range(steps):
             fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall * 1e6 / steps, a.elapsed_time(b) * 1e3 / steps
+        if events:
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return wall * 1e6 / steps, (a.elapsed_time(b) * 1e3 / steps if events else None)
+
+
+def settle(fn, seconds, stream, chunk=500):
+    """Untimed calls of `fn` back to back on `stream` for about `seconds`; returns how
+    many were made."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        with torch.cuda.stream(stream):
+            for _ in range(chunk):
+                fn()
+        torch.cuda.synchronize()
+        n += chunk
+    return n
 
 
 def time_steps(inp, wl, bufs, steps, warmup, stream):
@@ -211,7 +229,8 @@ def burst_stats(fn, steps, stream, reps=None):
     after one warm-up step and bracketed by device synchronisations; quantiles of the
     per-step wall time over the bursts (no events inside a burst)."""
     reps = reps or min(100, max(10, 2000 // steps))
-    return quantiles([time_back_to_back(fn, steps, 1, stream)[0] for _ in range(reps)])
+    return quantiles([time_back_to_back(fn, steps, 1, stream, events=False)[0]
+                      for _ in range(reps)])
 
 
 def quantiles(xs):
@@ -501,6 +520,38 @@ def build_read_ceiling(verbose=False):
     return PROBE_LIB
 
 
+def launch_floor(stream, reps=2000):
+    """Per-launch time of back-to-back launches that do (almost) nothing: an empty kernel
+    of 256 work-groups, and a kernel reading and writing 65536 floats (one memory round
+    trip). HIP events around `reps` launches on `stream`; what any one dependent kernel
+    of a step costs at least."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.spot_probe_empty.restype = ctypes.c_int
+    lib.spot_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.spot_probe_touch.restype = ctypes.c_int
+    lib.spot_probe_touch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p]
+    n = 1 << 16
+    a = torch.ones(n, device="cuda")
+    b = torch.empty(n, device="cuda")
+    torch.cuda.synchronize()
+    res = {}
+    for name, go in (("empty_us", lambda k: lib.spot_probe_empty(256, k, stream.cuda_stream)),
+                     ("read_write_us", lambda k: lib.spot_probe_touch(
+                         a.data_ptr(), b.data_ptr(), n, k, stream.cuda_stream))):
+        if go(50) != 0:
+            raise RuntimeError("launch-floor probe failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if go(reps) != 0:
+            raise RuntimeError("launch-floor probe failed")
+        e1.record(stream)
+        e1.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 3)
+    return res
+
+
 def read_ceiling(nbytes, stream, reps=20):
     """What a kernel that only reads sustains on this GPU for the attention's access
     pattern: about `nbytes` as 16 KiB blocks (one 64-token block of one KV head at
@@ -602,6 +653,8 @@ def main():
     ap.add_argument("--workload", default="c3_128k_b8", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flushed-reps", type=int, default=50)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed back-to-back steps before any timing")
     ap.add_argument("--extra-b1", action="store_true", default=True)
     ap.add_argument("--no-extra-b1", dest="extra_b1", action="store_false")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false", default=True)
@@ -645,13 +698,18 @@ def main():
 
     attn_call = step.calls[2]
 
-    # per-call breakdown first: a diagnostic pass of at least 500 steps (~50 ms), which
-    # also brings the GPU out of its idle clocks before the headline pass
+    # about a second of untimed steps first, so that every timed pass starts from the
+    # GPU's steady state under load (in 20-step runs, 0, 0.3, 1 and 3 s of it gave the
+    # same step times within noise)
+    settled = settle(step, a.settle_s, stream)
+    log(f"bench: {settled} untimed steps to settle the clocks")
+    # per-call breakdown first: a diagnostic pass of at least 500 steps (~50 ms)
     n_diag = max(a.steps, 500)
     wall, gpu_total_us, per = time_steps(inp, wl, bufs, n_diag, a.warmup, stream)
     us_step_percall = wall * 1e6 / n_diag
     # headline: K whole steps launched back to back on one stream
-    us_step, us_step_events = time_back_to_back(step, a.steps, a.warmup, stream)
+    us_step, _ = time_back_to_back(step, a.steps, a.warmup, stream, events=False)
+    _, us_step_events = time_back_to_back(step, a.steps, 1, stream)
     log(f"bench: {us_step:.1f} us/step wall, {us_step_events:.1f} us/step events")
     step_stats = {"bursts": burst_stats(step, a.steps, stream),
                   "per_step_events": time_step_distribution(step, max(200, a.steps), a.warmup,
@@ -675,6 +733,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "settle_steps": settled,
         "ms_per_step": round(us_step / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
@@ -698,9 +757,11 @@ def main():
         "step_us_stats": step_stats,
         "timing": "value = wall time of K steps launched back to back on one stream "
                   "(three library calls each, arguments marshalled once, no host "
-                  "synchronisation or events between them), bracketed by device "
-                  "synchronisations, divided by K; step_us_stats.bursts = that "
-                  "measurement repeated; step_us_stats.per_step_events = an event at every "
+                  "synchronisation or events between or around them), bracketed by device "
+                  "synchronisations, divided by K, after settle_steps untimed steps; "
+                  "events_us_per_step = a second such pass with a HIP event on each side; "
+                  "step_us_stats.bursts = the wall-time measurement repeated; "
+                  "step_us_stats.per_step_events = an event at every "
                   "step boundary (each event adds a gap of about 2 us); "
                   "roofline.avg_launch_us = HIP events on the same stream around K "
                   "back-to-back spot_sparse_attn calls, divided by K; per_call_us = a "
@@ -724,13 +785,14 @@ def main():
     rc["attn_frac_of_it"] = round(attn_gbps / rc["GBps"], 4)
     rc["step_frac_of_it"] = round(budget["step"] / (us_step * 1e-6) / 1e9 / rc["GBps"], 4)
     result["read_ceiling"] = rc
+    result["launch_floor"] = launch_floor(stream)
     if a.extra_b1 and wl.name == "c3_128k_b8":
         wl1 = W.WORKLOADS["c3_128k_b1"]
         inp1 = {k: (v[:1].contiguous() if isinstance(v, torch.Tensor) else v)
                 for k, v in inp.items()}
         bufs1 = DecodeBuffers.of(wl1, dt)
         step1 = DecodeStep(inp1, wl1, bufs1, stream=stream)
-        u1, _ = time_back_to_back(step1, a.steps, a.warmup, stream)
+        u1, _ = time_back_to_back(step1, a.steps, a.warmup, stream, events=False)
         w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
         st1 = {"bursts": burst_stats(step1, a.steps, stream),
                "per_step_events": time_step_distribution(step1, max(200, a.steps), a.warmup,

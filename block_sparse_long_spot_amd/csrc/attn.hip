@@ -8,12 +8,16 @@
 // and start the next one's, one partial each), so queries that select very different
 // numbers of blocks still keep every work-group equally busy; otherwise each
 // (query, KV head) gets the same number of runs, cut from that query's own count (runs
-// past its end store an empty partial). attn_combine then merges the slots of every
-// (query, head) in order (deterministic). Merging across work-groups inside one kernel
-// needs an agent-scope release/acquire per work-group, which on this multi-XCD part is
-// an L2 writeback plus invalidate; a second small kernel is cheaper (measured: with the
-// last-arriving work-group of each query merging, the 128K batch-8 call took 108 us
-// instead of 84, and the 1024-block static top-K call 593 us instead of 334).
+// past its end store an empty partial). A second kernel then merges the slots of every
+// (query, head) (attn_merge32 for up to 32 slots, attn_combine above that; both
+// deterministic). Merging inside the run kernel, in the last work-group of each
+// (query, KV head) to finish, was measured twice and is slower on this multi-XCD part:
+// with agent-scope release/acquire (an L2 writeback plus invalidate per work-group) the
+// 128K batch-8 call took 108 us instead of 84 and the 1024-block static top-K call 593
+// instead of 334; with write-through partials, one atomic ticket per work-group and the
+// partials read back past L2 it took 90 instead of ~87 us per batch-8 call and 25.4
+// instead of ~19 at batch 1 (the last work-group's chain of round trips costs more than
+// the kernel boundary).
 //
 // Block sizes 16, 32, 64 and 128 tokens. The unit of work of a wave is a 64-token
 // chunk made of four 16-token tiles, each with its own start token: the four tiles of
@@ -60,8 +64,20 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Partial results are stored with agent-scope (relaxed atomic) stores, which write
+// through the XCD's L2 to the device-coherent level: the kernel's end then has fewer
+// dirty L2 lines to write back before the merge kernel may start (measured: 0.1 us
+// less per 128K call at batch 1 and 8).
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_partial(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The run result of this work-group (per head: max m, sum l, unnormalised acc[D]), held
-// in LDS, stored as the run's partial result for attn_combine. `last` marks a head's
+// in LDS, stored as the run's partial result for the merge. `last` marks a head's
 // last partial: its l is stored as -l - 1 (a real l is >= 0), and the merge stops after
 // it.
 template <int D, int G, int NT>
@@ -71,8 +87,8 @@ __device__ void store_run(const float (&racc)[G][D], const float (&rm)[G], const
   for (int o = threadIdx.x; o < G * D; o += NT) {
     const int h = o / D, dd = o % D;
     const size_t idx = base + (size_t)h * nslot;
-    ws_acc[idx * D + dd] = racc[h][dd];
-    if (dd == 0) ws_ml[idx] = make_float2(rm[h], last ? -rl[h] - 1.f : rl[h]);
+    store_partial(&ws_acc[idx * D + dd], racc[h][dd]);
+    if (dd == 0) store_partial(&ws_ml[idx], make_float2(rm[h], last ? -rl[h] - 1.f : rl[h]));
   }
 }
 
@@ -87,7 +103,7 @@ __host__ __device__ inline size_t slot_base(int b, int g, int G, int Hq, int nsl
 template <int G>
 __device__ void store_empty_run(size_t base, int nslot, float2* __restrict__ ws_ml) {
   if (threadIdx.x < G)
-    ws_ml[base + (size_t)threadIdx.x * nslot] = make_float2(-INFINITY, 0.f);
+    store_partial(&ws_ml[base + (size_t)threadIdx.x * nslot], make_float2(-INFINITY, 0.f));
 }
 
 // An empty last partial (m = -inf, l = 0 stored as -1): a query with no entry, or the
@@ -95,7 +111,7 @@ __device__ void store_empty_run(size_t base, int nslot, float2* __restrict__ ws_
 template <int G>
 __device__ void store_end_marker(size_t base, int nslot, float2* __restrict__ ws_ml) {
   if (threadIdx.x < G)
-    ws_ml[base + (size_t)threadIdx.x * nslot] = make_float2(-INFINITY, -1.f);
+    store_partial(&ws_ml[base + (size_t)threadIdx.x * nslot], make_float2(-INFINITY, -1.f));
 }
 
 // ---------------------------------------------------------------- generic pass 1
@@ -318,22 +334,37 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
       }
     };
     uint16_t* const vs = Vs[wave];
+    // after_v runs once the chunk's V registers are stored to LDS (they may be reloaded
+    // then), after_s once the score MFMAs have read the K registers
+    // (a chunk with no token below L, active false, only stores V and runs the hooks:
+    // the reloads then have one place in the code, which keeps the compiler from
+    // hoisting them out of two branches above the uses of the registers they refill)
     auto consume = [&](const int (&st)[4], const bf16x8_t (&kb)[4][KS],
-                       const u32x4_t (&vv)[TPL]) {
+                       const u32x4_t (&vv)[TPL], bool active, auto&& after_v,
+                       auto&& after_s) {
       // the chunk's V rows to this wave's LDS tile, row t = chunk token t
 #pragma unroll
       for (int i = 0; i < TPL; ++i)
         *reinterpret_cast<u32x4_t*>(&vs[(i * TG + tg) * VP + dc * 8]) = vv[i];
+      // the reloads stay where they are: hoisted above these uses they would need a
+      // second register set
+      __builtin_amdgcn_sched_barrier(0);
+      after_v();
       // S'[token][head] for the 4 tiles: sc[T][r] = S'[chunk token 16T + 4kg + r][head row]
       floatx4_t sc[4];
+      if (active) {
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        floatx4_t a = {0.f, 0.f, 0.f, 0.f};
+        for (int T = 0; T < 4; ++T) {
+          floatx4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[T][s], qb[s], a, 0, 0, 0);
-        sc[T] = a;
+          for (int s = 0; s < KS; ++s)
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[T][s], qb[s], a, 0, 0, 0);
+          sc[T] = a;
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      after_s();
+      if (!active) return;
       float bm = -INFINITY;
 #pragma unroll
       for (int T = 0; T < 4; ++T)
@@ -396,31 +427,30 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     };
 
     if constexpr (PREFETCH) {
-      // Software pipeline over this wave's chunks: the next chunk's K loads are in
-      // flight while the current chunk is consumed.
+      // Software pipeline over this wave's chunks, one register set for K and one for
+      // V: the next chunk's V is loaded into the V registers as soon as the current V
+      // is in LDS, and its K into the K registers as soon as the score MFMAs have read
+      // them, so both are in flight while the current chunk is consumed.
       int st[4] = {-1, -1, -1, -1};
       bf16x8_t kb[4][KS];
+      u32x4_t vv[TPL];
       if (n_mine > 0) {
         tile_starts(0, st);
+        load_v(st, vv);
         load_k(st, kb);
       }
-      for (int i = 0; i < n_mine; ++i) {
-        u32x4_t vv[TPL];
-        load_v(st, vv);
-        int stn[4] = {-1, -1, -1, -1};
-        bf16x8_t kn[4][KS];
-        if (i + 1 < n_mine) {
-          tile_starts(i + 1, stn);
-          load_k(stn, kn);
-        }
-        if (any_token(st)) consume(st, kb, vv);
+      // (the last chunk has its own copy of the body: a conditional reload would keep
+      // the old register values live beside the new ones)
+      for (int i = 0; i + 1 < n_mine; ++i) {
+        int stn[4];
+        tile_starts(i + 1, stn);
+        auto next_v = [&] { load_v(stn, vv); };
+        auto next_k = [&] { load_k(stn, kb); };
+        consume(st, kb, vv, any_token(st), next_v, next_k);
 #pragma unroll
-        for (int T = 0; T < 4; ++T) {
-          st[T] = stn[T];
-#pragma unroll
-          for (int s = 0; s < KS; ++s) kb[T][s] = kn[T][s];
-        }
+        for (int T = 0; T < 4; ++T) st[T] = stn[T];
       }
+      if (n_mine > 0 && any_token(st)) consume(st, kb, vv, true, [] {}, [] {});
     } else {
       for (int i = 0; i < n_mine; ++i) {
         int st[4];
@@ -429,7 +459,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
         load_k(st, kb);
         u32x4_t vv[TPL];
         load_v(st, vv);
-        if (any_token(st)) consume(st, kb, vv);
+        if (any_token(st)) consume(st, kb, vv, true, [] {}, [] {});
       }
     }
 
@@ -558,14 +588,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
 }
 
 // ---------------------------------------------------------------- merge of the runs
-// One work-group per (query, head); thread = head dim. The head's slots are read CH at
-// a time (32 when every slot holds a run, 8 when runs are marked) -- one memory round
-// trip per CH slots -- and merged with an online rescale in
-// slot order, up to nslot slots or (MARKED) the partial marked last, whichever comes
-// first; empty runs carry m = -inf. A row with no selected token (every m = -inf) gets
-// zeros. Marked slots are read 8 at a time: a query usually has few runs, and every
-// slot read past its last one is wasted bandwidth (measured: 16 at a time cost the
-// 128K batch-8 call 0.5 us).
+// Above 32 slots: one work-group per (query, head); thread = head dim. The head's slots
+// are read CH at a time (16, or 8 when runs are marked) -- one memory round trip per CH
+// slots -- and merged with an online rescale in slot order, up to nslot slots or
+// (MARKED) the partial marked last, whichever comes first; empty runs carry m = -inf.
+// A row with no selected token (every m = -inf) gets zeros. (Reading 32 slots per
+// round trip this way, 64 loads in flight per thread, was 2 us slower per 128K batch-8
+// call than 8 at a time.)
 template <typename T, int D, bool MARKED, int CH>
 __global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ ws_acc,
                                                   const float2* __restrict__ ws_ml,
@@ -616,6 +645,93 @@ __global__ __launch_bounds__(D) void attn_combine(const float* __restrict__ ws_a
     if (MARKED && end) break;
   }
   store_out(out + (size_t)rowi * D + threadIdx.x, ls > 0.f ? a / ls : 0.f);
+}
+
+// The merge for at most 32 slots, every load in one round trip: 256 threads, each
+// holding 16-byte pieces of the head's slots (slot t / (D/4) + k * 1024 / D, dims
+// 4 (t % (D/4)) .. +3), and in every wave lane s holding slot s's (m, l). Each wave finds
+// the marked slot (MARKED), the maximum M and the weights w_s = 2^(m_s - M) itself, so
+// the only barrier is the one of the final sum over the threads that share a piece of
+// the head dims (lane swaps inside a wave, then LDS across the four waves). Slots past
+// the marked one, and the acc of empty runs, are never read into the sums. Against the
+// per-dim merge above with 8 slots per round trip: 128K batch 1 call 17.8 -> 15.8 us,
+// page geometry 27.4 -> 25.3, batch 8 with spread budgets 43.8 -> 43.0, batch 8 equal
+// budgets unchanged (84.3-84.5).
+template <typename T, int D, bool MARKED>
+__global__ __launch_bounds__(256) void attn_merge32(const float* __restrict__ ws_acc,
+                                                    const float2* __restrict__ ws_ml,
+                                                    T* __restrict__ out, int nslot) {
+  constexpr int NV = D / 4;            // 16-byte pieces per slot: 32 (d 128) or 16 (d 64)
+  constexpr int PER = 32 * NV / 256;   // pieces per thread
+  constexpr int SPT = 256 / NV;        // slot step between a thread's pieces
+  const int rowi = blockIdx.x;  // b * Hq + hq
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float4* ap = reinterpret_cast<const float4*>(ws_acc + (size_t)rowi * nslot * D);
+  // slots 0 .. SPT-1 (the first piece of every thread) are read with the (m, l) pairs;
+  // the rest with them too when every slot holds a run, else only up to the marked slot
+  // once it is known (a second round trip only for heads with more than SPT runs)
+  float4 x[PER];
+  x[0] = t / NV < nslot ? ap[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (!MARKED) {
+#pragma unroll
+    for (int k = 1; k < PER; ++k)
+      x[k] = t / NV + SPT * k < nslot ? ap[t + 256 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float2 ml = lane < nslot ? ws_ml[(size_t)rowi * nslot + lane] : make_float2(-INFINITY, 0.f);
+  bool valid = lane < nslot;
+  if constexpr (MARKED) {
+    // the first marked slot (l stored as -l - 1) is the last one of this head
+    const uint64_t mk = __ballot(valid && ml.y < 0.f);
+    int e = nslot - 1;
+    if (mk != 0) {
+      e = __builtin_ctzll(mk);
+      valid = valid && lane <= e;
+      if (lane == e) ml.y = -ml.y - 1.f;
+    }
+#pragma unroll
+    for (int k = 1; k < PER; ++k)
+      x[k] = t / NV + SPT * k <= e ? ap[t + 256 * k] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float m = valid ? ml.x : -INFINITY;
+  const float M = readlane_f(wave_max_to_last(m), 63);
+  const float w = m == -INFINITY ? 0.f : exp2f(m - M);  // M = -inf: every w is 0
+  const float L = group_sum_dpp<64>(w > 0.f ? w * ml.y : 0.f);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const float wk = __shfl(w, t / NV + SPT * k);
+    if (wk > 0.f) {
+      a.x += wk * x[k].x;
+      a.y += wk * x[k].y;
+      a.z += wk * x[k].z;
+      a.w += wk * x[k].w;
+    }
+  }
+  // threads t and t + NV (, t + 2 NV, t + 3 NV) of a wave hold the same dims
+  auto wsum = [](float v) {
+    if constexpr (NV == 16) v = xor16_sum(v);
+    return xor32_sum(v);
+  };
+  a = make_float4(wsum(a.x), wsum(a.y), wsum(a.z), wsum(a.w));
+  __shared__ float4 red[4][NV];
+  if (lane < NV) red[wave][lane] = a;
+  __syncthreads();
+  if (t < NV) {
+    float4 r = red[0][t];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      r.x += red[i][t].x;
+      r.y += red[i][t].y;
+      r.z += red[i][t].z;
+      r.w += red[i][t].w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    T* o = out + (size_t)rowi * D + 4 * t;
+    store_out(o + 0, r.x * inv);
+    store_out(o + 1, r.y * inv);
+    store_out(o + 2, r.z * inv);
+    store_out(o + 3, r.w * inv);
+  }
 }
 
 struct Ws {
@@ -724,12 +840,15 @@ hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
   // runs across queries mark each query's last partial; per-query runs fill all nsplit
   // slots (a fixed trip count, so the loads of every batch issue together: up to 32
   // slots in one round trip)
-  if (sp.flat)
-    hipLaunchKernelGGL((attn_combine<T, D, true, 8>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
+  if (sp.nslot <= 32 && sp.flat)
+    hipLaunchKernelGGL((attn_merge32<T, D, true>), dim3(B * Hq), dim3(256), 0, stream, ws.acc,
                        ws.ml, static_cast<T*>(out), sp.nslot);
   else if (sp.nslot <= 32)
-    hipLaunchKernelGGL((attn_combine<T, D, false, 32>), dim3(B * Hq), dim3(D), 0, stream,
-                       ws.acc, ws.ml, static_cast<T*>(out), sp.nslot);
+    hipLaunchKernelGGL((attn_merge32<T, D, false>), dim3(B * Hq), dim3(256), 0, stream, ws.acc,
+                       ws.ml, static_cast<T*>(out), sp.nslot);
+  else if (sp.flat)
+    hipLaunchKernelGGL((attn_combine<T, D, true, 8>), dim3(B * Hq), dim3(D), 0, stream, ws.acc,
+                       ws.ml, static_cast<T*>(out), sp.nslot);
   else
     hipLaunchKernelGGL((attn_combine<T, D, false, 16>), dim3(B * Hq), dim3(D), 0, stream,
                        ws.acc, ws.ml, static_cast<T*>(out), sp.nslot);

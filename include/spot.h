@@ -17,7 +17,9 @@
  * Conventions shared by every call:
  *  - Every pointer argument is DEVICE memory owned by the caller (allocated and freed
  *    by the caller; the library keeps no pointer after the call returns). The library
- *    allocates nothing, keeps no global state and never synchronises the device.
+ *    allocates nothing and never synchronises the device. Its only global state is
+ *    the per-GPU scratch array of spot_sparse_attn_noalloc (declared below), whose
+ *    device address it looks up once per GPU.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream. Every
  *    call validates its arguments on the host, then enqueues its kernels on `stream`
  *    and returns; results are ready when the stream reaches that point.

@@ -1,4 +1,5 @@
-// Read-bandwidth reference for the benchmark (not part of the decode path).
+// Read-bandwidth and launch-floor references for the benchmark (not part of the decode
+// path).
 //
 // A kernel that does nothing but read: n_blocks 16 KiB blocks of a device buffer, in the
 // order a block list gives, 16-byte non-temporal loads, each work-group taking an equal
@@ -37,6 +38,16 @@ __global__ __launch_bounds__(kThreads) void read_blocks(const u32x4* __restrict_
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
+// Launch-floor probes: an empty kernel, and one that reads and writes one float per
+// thread (a kernel with one memory round trip and nothing else).
+__global__ void empty_kernel() {}
+
+__global__ __launch_bounds__(kThreads) void touch_kernel(const float* __restrict__ a,
+                                                         float* __restrict__ b, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) b[i] = a[i] * 2.f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,6 +65,27 @@ __attribute__((visibility("default"))) int spot_probe_read_blocks(const void* ba
     return -1;
   hipLaunchKernelGGL(read_blocks, dim3(wgs), dim3(kThreads), 0, stream,
                      static_cast<const u32x4*>(base), list, n_blocks / wgs, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Launches `reps` empty kernels of `wgs` work-groups of 256 threads back to back on
+// `stream`. Returns 0, or -1 on a bad argument (nothing launched).
+__attribute__((visibility("default"))) int spot_probe_empty(int wgs, int reps,
+                                                            hipStream_t stream) {
+  if (wgs <= 0 || reps <= 0) return -1;
+  for (int r = 0; r < reps; ++r)
+    hipLaunchKernelGGL(empty_kernel, dim3(wgs), dim3(kThreads), 0, stream);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Launches `reps` kernels back to back on `stream`, each setting b[i] = 2 a[i] for
+// i < n (one thread per element). a and b hold at least n floats.
+__attribute__((visibility("default"))) int spot_probe_touch(const float* a, float* b, int n,
+                                                            int reps, hipStream_t stream) {
+  if (!a || !b || n <= 0 || reps <= 0) return -1;
+  const int wgs = (n + kThreads - 1) / kThreads;
+  for (int r = 0; r < reps; ++r)
+    hipLaunchKernelGGL(touch_kernel, dim3(wgs), dim3(kThreads), 0, stream, a, b, n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -249,6 +249,12 @@ ATTN_CASES = [
     (3, 32, 8, 128, 1024, 8, "bf16", "empty_rows"),
     (1, 32, 8, 128, 70, 2, "bf16", "all"),
     (4, 32, 8, 128, 20000, 256, "bf16", "random"),
+    # more than 32 partial slots per (query, head): the slot-by-slot merge (per-query
+    # runs at batch 1, runs cut across queries at batch 2 and 3, fp32 runs)
+    (1, 8, 1, 128, 13000, 200, "bf16", "random"),
+    (2, 8, 1, 64, 13000, 200, "bf16", "skewed"),
+    (3, 16, 2, 128, 19300, 300, "bf16", "random"),
+    (1, 4, 1, 64, 17000, 256, "f32", "random"),
 ]
 
 
