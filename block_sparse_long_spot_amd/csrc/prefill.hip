@@ -55,8 +55,11 @@ __device__ __forceinline__ TileRow tile_row(int r, int n_tiles, int T, int Tq, i
 // work-group every work-group re-reads the tile's 64 KiB of selector queries (d_idx 64);
 // with many tiles a work-group takes up to 32 groups (a whole 32K-token row of blocks),
 // which cuts that traffic and the work-group count (measured on a 32K prompt in tiles of
-// 128: 49 us with 4 groups, 42 with 8, 38 with 16, 37 with 32).
+// 128: 49 us with 4 groups, 42 with 8, 38 with 16, 37 with 32). 4-bit keys take 16: their
+// decode lengthens each group, and the last tile's row is one work-group's serial chain
+// (INT4 56 -> 44 us, FP4 46 -> 41; 8 groups: 50 and 45).
 constexpr int kScoreMaxCG = 32;
+constexpr int kScoreMaxCG4 = 16;
 
 // The B operand of one MFMA k-step of a key row: this lane's 8 elements of d_idx
 // (32s + 8kg .. +7), held as loaded and turned into exact bf16 values before use.
@@ -718,7 +721,8 @@ hipError_t launch_prefill_score_kf(const uint16_t* q, const float* sel_w, const 
   const long groups = (nb_stride + 15) / 16;  // 16-block column groups
   if (H == 4) {
     // several column groups per work-group once there are work-groups to spare
-    const int CG = (long)B * n_tiles * groups >= 2048 ? kScoreMaxCG : 1;
+    constexpr int kMaxCG = KF == kInt4 || KF == kFp4 ? kScoreMaxCG4 : kScoreMaxCG;
+    const int CG = (long)B * n_tiles * groups >= 2048 ? kMaxCG : 1;
     dim3 grid(static_cast<unsigned>((groups + CG - 1) / CG), B * n_tiles);
 #define SPOT_PS4(DI)                                                                         \
   hipLaunchKernelGGL((prefill_score_kernel<KF, DI>), grid, dim3(256), 0, stream, q, sel_w, k, \
