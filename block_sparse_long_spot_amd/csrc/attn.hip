@@ -251,20 +251,59 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   __shared__ float racc[G][D];
   __shared__ float rm[G], rl[G];
 
+  // The B operand of S' = K.Q^T for query b: column = query head of the group (zero
+  // beyond G), k = head dim.
+  auto load_q = [&](int b, bf16x8_t (&qv)[KS]) {
+    const bool hv = row < G;
+    const uint16_t* qp = q + ((size_t)b * Hq + g * G + (hv ? row : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + s * 32 + kg * 8);
+      if (!hv) v = bf16x8_t{};
+      qv[s] = v;
+    }
+  };
+  // The list entry this lane reads for a run of n_ent entries (wave-uniform count),
+  // relative to the run's start, or -1 if it reads none. This wave's chunks are
+  // wave + i*NW; their entries are read once, one per lane (at most 64 per wave; the
+  // split plan keeps runs within that), so a chunk's tile starts are register reads,
+  // not loads on the critical path.
+  //   BS >= 64: lane i holds the entry of chunk i;
+  //   BS <  64: lane i*EPC + u holds entry u of chunk i.
+  auto entry_of_lane = [&](int n_ent) {
+    const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
+    const int n_mine = (n_chunks - wave + NW - 1) / NW;
+    const int i = lane / EPC, u = lane % EPC;
+    const int e_rel = BS >= kChunk ? (wave + i * NW) / CPE : (wave + i * NW) * EPC + u;
+    return i < n_mine && e_rel < n_ent ? e_rel : -1;
+  };
+  // Read ahead for a full list (count == K_max, the usual case when the cap binds): the
+  // run of query blockIdx.z that this work-group then takes, and the query, are read
+  // together with the counts instead of after them (one round trip instead of two
+  // before the first K/V loads). A run that turns out different is read again.
+  int run_spec = (K_max + nsplit - 1) / nsplit;
+  run_spec = min((run_spec + EPC - 1) / EPC * EPC, bps);
+  const int b_spec = blockIdx.z;
+  const int j0_spec = blockIdx.x * run_spec;
+  const int n_spec = max(0, min(j0_spec + run_spec, K_max) - j0_spec);
+  int e_spec = -1;
+  {
+    const int r = entry_of_lane(n_spec);
+    if (r >= 0) e_spec = sel_idx[(size_t)b_spec * K_max + j0_spec + r];
+  }
+  bf16x8_t q_spec[KS];
+  load_q(b_spec, q_spec);
+
   // Entries [j0, j1) of query b's list (j0 < j1), reduced into slot `slot` of its heads;
   // `last`: no later slot of this query holds a partial.
   auto run_entries = [&](int b, int j0, int j1, int slot, bool last) {
-    // B operand of S' = K.Q^T: column = query head of the group (zero beyond G), k = head dim
+    const bool spec = b == b_spec && j0 == j0_spec && j1 - j0 == n_spec;  // uniform
     bf16x8_t qb[KS];
-    {
-      const bool hv = row < G;
-      const uint16_t* qp = q + ((size_t)b * Hq + g * G + (hv ? row : 0)) * D;
+    if (spec) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qp + s * 32 + kg * 8);
-        if (!hv) v = bf16x8_t{};
-        qb[s] = v;
-      }
+      for (int s = 0; s < KS; ++s) qb[s] = q_spec[s];
+    } else {
+      load_q(b, qb);
     }
     float m = -INFINITY, l = 0.f;  // online-softmax state of head `row`
     floatx4_t o[NT];               // o[dt][r] = O[head 4kg + r][dim 16dt + row]
@@ -277,19 +316,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     const int n_ent = j1 - j0;
     const int n_chunks = BS >= kChunk ? n_ent * CPE : (n_ent + EPC - 1) / EPC;
     const int n_mine = (n_chunks - wave + NW - 1) / NW;
-    // This wave's chunks are wave + i*NW. The list entries they use are read once, one
-    // per lane (at most 64 per wave; the split plan keeps runs within that), so a
-    // chunk's tile starts are register reads, not loads on the critical path.
-    //   BS >= 64: lane i holds the entry of chunk i;
-    //   BS <  64: lane i*EPC + u holds entry u of chunk i.
     int my_blk = -1;
     {
-      const int i = lane / EPC, u = lane % EPC;
-      const int e_rel = BS >= kChunk ? (wave + i * NW) / CPE : (wave + i * NW) * EPC + u;
-      if (i < n_mine && e_rel < n_ent) {
-        const int e = sel_idx[(size_t)b * K_max + j0 + e_rel];
-        my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
+      int e = -1;
+      if (spec) {
+        e = e_spec;
+      } else {
+        const int r = entry_of_lane(n_ent);
+        if (r >= 0) e = sel_idx[(size_t)b * K_max + j0 + r];
       }
+      my_blk = (e < 0 || e >= nbl) ? -1 : e;  // entries outside [0, nbl) are ignored
     }
     // first token of each 16-token tile of chunk i, or -1 for a tile with no block
     auto tile_starts = [&](int i, int (&st)[4]) {
