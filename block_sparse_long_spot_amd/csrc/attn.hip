@@ -873,9 +873,9 @@ hipError_t launch_d(const void* q, const void* k, const void* v, bool fast,
   }
 #undef SPOT_ARGS
   if (e != hipSuccess) return e;
-  // runs across queries mark each query's last partial; per-query runs fill all nsplit
-  // slots (a fixed trip count, so the loads of every batch issue together: up to 32
-  // slots in one round trip)
+  // The merge: runs cut across the batch (flat plans) flag each query's last partial,
+  // so their merge stops there; runs per query fill all nsplit slots. Up to 32 slots
+  // per head the one-round-trip merge, above that the slot-by-slot one.
   if (sp.nslot <= 32 && sp.flat)
     hipLaunchKernelGGL((attn_merge32<T, D, true>), dim3(B * Hq), dim3(256), 0, stream, ws.acc,
                        ws.ml, static_cast<T*>(out), sp.nslot);
