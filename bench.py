@@ -181,6 +181,49 @@ def time_graph(inp, wl, bufs, steps, warmup, stream):
     return wall * 1e6 / steps, a.elapsed_time(b) * 1e3 / steps
 
 
+class GraphSteps:
+    """K decode steps as HIP graphs, the way a server captures the launch-bound part of a
+    token (one graph of up to 200 steps, replayed K // 200 times, plus one graph for the
+    rest): the same kernels with the same arguments as the stream-launched steps,
+    dispatched without host work between them. Calling it runs the K steps on `stream`.
+    `output_matches`: a replay leaves the output the stream-launched steps leave."""
+
+    MAX_STEPS = 200
+
+    def __init__(self, step, steps, stream, out):
+        self.stream = stream
+        self.k = steps
+        g_n = min(steps, self.MAX_STEPS)
+        self.full, self.n_full = self._capture(step, g_n), steps // g_n
+        rest = steps - self.n_full * g_n
+        self.rest = self._capture(step, rest) if rest else None
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            step()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        out.zero_()
+        torch.cuda.synchronize()
+        self()
+        torch.cuda.synchronize()
+        self.output_matches = bool(torch.equal(ref, out))
+
+    def _capture(self, step, n):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=self.stream):
+            for _ in range(n):
+                step()
+        torch.cuda.synchronize()
+        return g
+
+    def __call__(self):
+        for _ in range(self.n_full):
+            self.full.replay()
+        if self.rest is not None:
+            self.rest.replay()
+
+
 def time_flushed(inp, wl, bufs, reps, stream):
     """Per-step time with a 1 GiB write between steps (outside the events), so that no
     step reads data left in the last-level caches by the previous one."""
@@ -707,13 +750,23 @@ def main():
     n_diag = max(a.steps, 500)
     wall, gpu_total_us, per = time_steps(inp, wl, bufs, n_diag, a.warmup, stream)
     us_step_percall = wall * 1e6 / n_diag
-    # headline: K whole steps launched back to back on one stream
-    us_step, _ = time_back_to_back(step, a.steps, a.warmup, stream, events=False)
+    # headline: K whole steps, captured as HIP graphs and replayed, bracketed by device
+    # synchronisations; beside it the same K steps launched from the host one by one
+    graph_steps = GraphSteps(step, a.steps, stream, bufs.out)
+    us_step = time_back_to_back(graph_steps, 1, 1, stream, events=False)[0] / a.steps
+    us_stream, _ = time_back_to_back(step, a.steps, a.warmup, stream, events=False)
     _, us_step_events = time_back_to_back(step, a.steps, 1, stream)
-    log(f"bench: {us_step:.1f} us/step wall, {us_step_events:.1f} us/step events")
-    step_stats = {"bursts": burst_stats(step, a.steps, stream),
+    log(f"bench: {us_step:.1f} us/step (graphs), {us_stream:.1f} us/step (stream launches), "
+        f"{us_step_events:.1f} us/step events")
+    reps = min(100, max(10, 2000 // a.steps))
+    step_stats = {"bursts": quantiles([time_back_to_back(graph_steps, 1, 1, stream,
+                                                         events=False)[0] / a.steps
+                                       for _ in range(reps)]),
+                  "stream_launch_bursts": burst_stats(step, a.steps, stream),
                   "per_step_events": time_step_distribution(step, max(200, a.steps), a.warmup,
                                                             stream)}
+    graphs_ok = graph_steps.output_matches
+    del graph_steps
     log(f"bench: step statistics {step_stats}")
     tokens = selected_tokens(bufs.sel_idx, bufs.sel_cnt, wl.L, wl.block)
     budget = byte_budget(wl, wl.B, tokens)
@@ -755,12 +808,16 @@ def main():
                      "selected_tokens": tokens},
         "queries_per_s": round(wl.B / (us_step * 1e-6), 1),
         "step_us_stats": step_stats,
-        "timing": "value = wall time of K steps launched back to back on one stream "
-                  "(three library calls each, arguments marshalled once, no host "
-                  "synchronisation or events between or around them), bracketed by device "
-                  "synchronisations, divided by K, after settle_steps untimed steps; "
-                  "events_us_per_step = a second such pass with a HIP event on each side; "
-                  "step_us_stats.bursts = the wall-time measurement repeated; "
+        "timing": "value = wall time of K steps, captured once as HIP graphs (graphs."
+                  "steps_per_graph steps each, as a server captures a token's launches) and "
+                  "replayed on one stream, bracketed by device synchronisations, divided by "
+                  "K, after settle_steps untimed steps and one untimed replay; "
+                  "stream_launch_us_per_step = the same K steps launched from the host one "
+                  "call at a time (three library calls each, arguments marshalled once, no "
+                  "host synchronisation or events between them); events_us_per_step = a "
+                  "stream-launched pass with a HIP event on each side; "
+                  "step_us_stats.bursts = the graph measurement repeated, "
+                  "stream_launch_bursts the stream-launched one; "
                   "step_us_stats.per_step_events = an event at every "
                   "step boundary (each event adds a gap of about 2 us); "
                   "roofline.avg_launch_us = HIP events on the same stream around K "
@@ -776,6 +833,9 @@ def main():
         "graph_replay_us_per_step": {"wall": round(g_wall, 3), "events": round(g_event, 3),
                                      "note": "one step per HIP graph; each graph launch "
                                              "adds a gap before its first kernel"},
+        "graphs": {"steps_per_graph": min(a.steps, GraphSteps.MAX_STEPS),
+                   "output_matches_stream_launch": graphs_ok},
+        "stream_launch_us_per_step": round(us_stream, 3),
         "flushed_step_us": quantiles(flushed) if flushed else None,
         "pages_context": "paper: 3.9x FlashAttention, 1.8x Twilight end-to-end decode tok/s "
                          "at 128K on one NVIDIA B200 (not comparable to this metric)",
@@ -792,9 +852,13 @@ def main():
                 for k, v in inp.items()}
         bufs1 = DecodeBuffers.of(wl1, dt)
         step1 = DecodeStep(inp1, wl1, bufs1, stream=stream)
-        u1, _ = time_back_to_back(step1, a.steps, a.warmup, stream, events=False)
+        gs1 = GraphSteps(step1, a.steps, stream, bufs1.out)
+        u1 = time_back_to_back(gs1, 1, 1, stream, events=False)[0] / a.steps
+        u1s, _ = time_back_to_back(step1, a.steps, a.warmup, stream, events=False)
         w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
-        st1 = {"bursts": burst_stats(step1, a.steps, stream),
+        st1 = {"bursts": quantiles([time_back_to_back(gs1, 1, 1, stream, events=False)[0]
+                                    / a.steps for _ in range(reps)]),
+               "stream_launch_bursts": burst_stats(step1, a.steps, stream),
                "per_step_events": time_step_distribution(step1, max(200, a.steps), a.warmup,
                                                          stream)}
         fl1 = time_flushed(inp1, wl1, bufs1, max(50, a.flushed_reps), stream)
@@ -803,6 +867,8 @@ def main():
         fl1q = quantiles(fl1)
         result["batch1"] = {
             "us_per_step": round(u1, 3),
+            "stream_launch_us_per_step": round(u1s, 3),
+            "graphs_output_match": gs1.output_matches,
             "GBps": round(b1["step"] / (u1 * 1e-6) / 1e9, 1),
             "step_us_stats": st1,
             "flushed_step_us": fl1q,
@@ -812,11 +878,12 @@ def main():
                                           / HBM_PEAK_GBPS, 4)},
             "queries_per_s": round(1 / (u1 * 1e-6), 1),
             "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in p1.items()},
-            "note": "batch row 0 of the same inputs. us_per_step / GBps: steps back to "
-                    "back, so the 68 MB a step reads partly come from the 256 MB last-level "
-                    "cache; flushed_step_us / flushed_hbm: a 1 GiB write between steps "
-                    "(outside the events), the HBM figure"}
-        del inp1, bufs1
+            "note": "batch row 0 of the same inputs. us_per_step / GBps: K steps back to "
+                    "back as HIP graphs (stream_launch_us_per_step: launched one call at a "
+                    "time), so the 68 MB a step reads partly come from the 256 MB "
+                    "last-level cache; flushed_step_us / flushed_hbm: a 1 GiB write between "
+                    "steps (outside the events), the HBM figure"}
+        del inp1, bufs1, gs1
     if a.static and wl.name == "c3_128k_b8":
         log("bench: static top-K at half the context")
         result["static_topk_half"] = static_topk_leg(inp, wl, a.steps, a.warmup, stream)
