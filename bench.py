@@ -753,6 +753,11 @@ def main():
     # headline: K whole steps, captured as HIP graphs and replayed, bracketed by device
     # synchronisations; beside it the same K steps launched from the host one by one
     graph_steps = GraphSteps(step, a.steps, stream, bufs.out)
+    # after any idle gap (the capture above, a pause) the GPU needs about 10 ms of load to
+    # reach its steady clocks: the first 20-step bursts after a 0.5 s pause ran 100, 98,
+    # 98 and 97 us per step against 95 after that. So the timed steps follow ~30 ms of
+    # untimed replays with nothing but the bracketing synchronisation in between.
+    settle(graph_steps, 0.03, stream, chunk=1)
     us_step = time_back_to_back(graph_steps, 1, 1, stream, events=False)[0] / a.steps
     us_stream, _ = time_back_to_back(step, a.steps, a.warmup, stream, events=False)
     _, us_step_events = time_back_to_back(step, a.steps, 1, stream)
@@ -811,7 +816,8 @@ def main():
         "timing": "value = wall time of K steps, captured once as HIP graphs (graphs."
                   "steps_per_graph steps each, as a server captures a token's launches) and "
                   "replayed on one stream, bracketed by device synchronisations, divided by "
-                  "K, after settle_steps untimed steps and one untimed replay; "
+                  "K, after settle_steps untimed steps, ~30 ms of untimed replays right before "
+                  "(the GPU's clocks drop in idle gaps) and one untimed replay; "
                   "stream_launch_us_per_step = the same K steps launched from the host one "
                   "call at a time (three library calls each, arguments marshalled once, no "
                   "host synchronisation or events between them); events_us_per_step = a "
@@ -853,6 +859,7 @@ def main():
         bufs1 = DecodeBuffers.of(wl1, dt)
         step1 = DecodeStep(inp1, wl1, bufs1, stream=stream)
         gs1 = GraphSteps(step1, a.steps, stream, bufs1.out)
+        settle(gs1, 0.03, stream, chunk=1)  # steady clocks first, as for the headline
         u1 = time_back_to_back(gs1, 1, 1, stream, events=False)[0] / a.steps
         u1s, _ = time_back_to_back(step1, a.steps, a.warmup, stream, events=False)
         w1, g1, p1 = time_steps(inp1, wl1, bufs1, a.steps, a.warmup, stream)
