@@ -338,6 +338,55 @@ def test_prefill_sequence_two_heads_per_wave_ragged():
                    K_min=8, seed=34, tiles_checked=(0, 16, 31), heads_checked=(0, 1, 6, 7, 30))
 
 
+def test_prefill_edge_lists_large_grid():
+    """Hand-made lists on a two-heads-per-wave grid of 4096 work-groups (128 tiles of 128
+    x 8 KV heads), from position 10 so that 32-row work-groups and 64-token blocks do not
+    align, with L ending inside the last block: an empty list (every row zero); a list
+    whose only block starts after the first 32 rows' last query (those rows are zero, the
+    next 32 attend); invalid, future and unsorted entries; a 130-block list. Every
+    checked row is compared, so rows left unwritten (NaN) fail."""
+    B, Hq, Hkv, Tq, q_pos0, T, K_max = 1, 32, 8, 128, 10, 128 * 128, 160
+    L = q_pos0 + T
+    nb = -(-L // 64)
+    n_tiles = T // Tq
+    log(f"prefill edge lists, {n_tiles} tiles")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(39)
+    Q = torch.randn(B, Hq, T, 128, generator=g, device=DEV).bfloat16()
+    K = torch.randn(B, Hkv, L, 128, generator=g, device=DEV).bfloat16()
+    V = torch.randn(B, Hkv, L, 128, generator=g, device=DEV).bfloat16()
+    lists = {}
+    for t in range(n_tiles):
+        diag = (q_pos0 + t * Tq + Tq - 1) // 64
+        lists[t] = [0, diag]
+    lists[0] = []
+    lists[1] = [3]                         # first token 192: rows 0-31 (138..169) see none
+    lists[2] = [-1, 0, 300, 200, 4, 2]     # invalid, beyond nb, future, then visible ones
+    lists[64] = list(range(130))
+    lists[127] = [nb - 1, nb - 3, 0]       # the block crossing L first, unsorted
+    idx = torch.full((B, n_tiles, K_max), -1, dtype=torch.int32)
+    cnt = torch.zeros(B, n_tiles, dtype=torch.int32)
+    for t, lst in lists.items():
+        if lst:
+            idx[0, t, : len(lst)] = torch.tensor(lst, dtype=torch.int32)
+        cnt[0, t] = len(lst)
+    out = torch.full((B, Hq, T, 128), float("nan"), device=DEV).bfloat16()
+    scale = 1 / math.sqrt(128)
+    _lib.spot_prefill_attn(Q, K, V, idx.to(DEV), cnt.to(DEV), out, q_pos0, scale, Tq=Tq)
+    torch.cuda.synchronize()
+    heads = {(0, h) for h in (0, 1, 2, 3, 17, 31)}
+    got = np64(out)
+    for t in (0, 1, 2, 64, 127):
+        q0, q1 = t * Tq, (t + 1) * Tq
+        sets = [sorted(b for b in lists[t] if 0 <= b < nb)]
+        ref = O.prefill_attention(np64(Q[:, :, q0:q1]), _KV(K), _KV(V), sets, 64, scale,
+                                  q_pos0 + q0, heads=heads)
+        for (b, h) in heads:
+            assert_out_close(got[b, h, q0:q1], ref[b, h], torch.bfloat16, tag=f"tile {t} head {h}")
+    assert not np.isnan(got[0, :, : 2 * Tq]).any()
+    assert (got[0, :, :Tq] == 0).all() and (got[0, :, Tq : Tq + 32] == 0).all()
+
+
 def test_prefill_sequence_long_list_stride():
     """A list stride of 8192 entries (the longest list) on a grid of 1024 row tiles: the
     list's LDS leaves room for three block buffers instead of four."""
