@@ -389,7 +389,8 @@ def test_prefill_edge_lists_large_grid():
 
 def test_prefill_sequence_long_list_stride():
     """A list stride of 8192 entries (the longest list) on a grid of 1024 row tiles: the
-    list's LDS leaves room for three block buffers instead of four."""
+    list takes 32 KiB of LDS beside the two 32 KiB block buffers, so one work-group fits
+    per CU instead of two."""
     _sequence_case(B=1, T=2048, Tq=128, q_pos0=0, Hq=32, Hkv=8, p=0.95, n_sink=1, n_rec=4,
                    K_min=2, seed=36, tiles_checked=(0, 9, 15), heads_checked=(0, 3, 29),
                    K_max=8192)
