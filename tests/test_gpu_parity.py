@@ -660,6 +660,38 @@ def test_graph_replay_matches_eager():
         assert torch.equal(bufs.out, ref[2]), f"replay {i}"
 
 
+def test_graph_replay_headline_shape_dirty_workspace():
+    """The 128K batch-8 decode step (runs cut across the batch, the merge stopping at each
+    query's flagged last slot) captured in a HIP graph as a server would: every replay,
+    with the workspace overwritten by 0xFF bytes (NaN partials) and the outputs poisoned
+    between replays, reproduces the stream-launched step bit for bit."""
+    wl = W.WORKLOADS["c3_128k_b8"]
+    log("graph replay c3_128k_b8")
+    inp = W.make_inputs(wl, device=DEV)
+    bufs = DecodeBuffers.of(wl, inp["q"].dtype)
+    stream = torch.cuda.Stream()
+    step = DecodeStep(inp, wl, bufs, stream=stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    ref = (bufs.scores.clone(), bufs.sel_idx.clone(), bufs.sel_cnt.clone(), bufs.out.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for i in range(3):
+        bufs.workspace.fill_(255)
+        bufs.out.fill_(float("nan"))
+        bufs.sel_idx.fill_(-3)
+        bufs.scores.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, r in zip(("scores", "sel_idx", "sel_cnt", "out"), ref):
+            assert torch.equal(getattr(bufs, name), r), f"replay {i}: {name}"
+    del g
+
+
 def test_page_geometry_scoring_sampled():
     """The paper's selector geometry (per-token keys, 16 per block, 4 heads x 128) at a
     128K context, batch 1: sampled blocks against the oracle, then the top-p rule on the
