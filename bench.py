@@ -710,8 +710,8 @@ def main():
                          "one JSON line instead of the decode headline")
     a = ap.parse_args()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the decode step runs on one device; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU only: the decode step runs on one device and "
+              "there is no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -65,7 +65,7 @@ int check_selector(const void* sel_q, int q_dtype, const void* sel_q_scale, cons
   return SPOT_OK;
 }
 
-// The attention shapes this build has kernels for (after the argument checks).
+// The attention shapes the library has kernels for (after the argument checks).
 int attn_support(int Hq, int Hkv, int d, int block) {
   const int G = Hq / Hkv;
   if (d != 64 && d != 128) return SPOT_ERR_UNSUPPORTED;

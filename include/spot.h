@@ -27,7 +27,7 @@
  *  - Return value: SPOT_OK, or
  *      SPOT_ERR_INVALID      bad argument (null or misaligned pointer, size <= 0, values
  *                            out of range); nothing is enqueued;
- *      SPOT_ERR_UNSUPPORTED  a valid combination this build has no kernel for; nothing
+ *      SPOT_ERR_UNSUPPORTED  a valid combination the library has no kernel for; nothing
  *                            is enqueued;
  *      SPOT_ERR_DEVICE       the HIP runtime refused a launch. A fault inside a kernel
  *                            surfaces at the caller's next synchronisation instead.
