@@ -264,9 +264,12 @@ hipError_t launch_kf(const void* sel_q, int q_fmt, const void* sel_q_scale, cons
   int lpr_log2 = 0;
   while ((1 << lpr_log2) < lpr) ++lpr_log2;
   const int per_wg = 4 * (64 >> lpr_log2);
-  // one key per block and more than 1024 work-groups of one round: 4 rounds per wave
+  // One key per block: R rounds per wave, the largest of 1, 2 and 4 that still leaves
+  // at least 1024 work-groups (measured at 128K: batch 8 takes 2.3 us with 1024
+  // work-groups of 2 rounds, 2.5 with 512 of 4 or 2048 of 1; batch 1, 256 work-groups
+  // of 1 round, 1.9 us, 128 of 2 2.0)
   const long wg1 = ((long)nb + per_wg - 1) / per_wg * B;
-  const int R = kpb == 1 && wg1 > 1024 ? 4 : 1;
+  const int R = kpb != 1 ? 1 : (wg1 >= 4096 ? 4 : (wg1 >= 2048 ? 2 : 1));
   dim3 grid((unsigned)(((long)nb + per_wg * R - 1) / (per_wg * R)), B), block(256);
 #define SPOT_SCORE(DIDX, RR)                                                                 \
   hipLaunchKernelGGL((select_score_kernel<QF, KF, DIDX, RR>), grid, block, 0, stream, sel_q,   \
@@ -275,6 +278,8 @@ hipError_t launch_kf(const void* sel_q, int q_fmt, const void* sel_q_scale, cons
 #define SPOT_SCORE_R(DIDX) \
   if (R == 4)              \
     SPOT_SCORE(DIDX, 4);   \
+  else if (R == 2)         \
+    SPOT_SCORE(DIDX, 2);   \
   else                     \
     SPOT_SCORE(DIDX, 1);
   switch (d_idx) {
