@@ -70,6 +70,13 @@ SCORE_CASES = [
     (1, 31, 1, 16, 32, "fp8", "f32"),
     (2, 50, 2, 4, 64, "int4", "bf16"),
     (2, 2048, 1, 4, 64, "bf16", "fp4"),
+    # one key per block on grids of 2048 and 4096+ one-round work-groups, so each lane
+    # scores 2 or 4 blocks, with the last round ragged (nb not a multiple of a
+    # work-group's blocks)
+    (8, 2047, 1, 4, 64, "bf16", "bf16"),
+    (16, 2050, 1, 4, 64, "f32", "bf16"),
+    (64, 2049, 1, 4, 64, "bf16", "int4"),
+    (32, 1029, 1, 4, 64, "bf16", "fp8"),
 ]
 
 
