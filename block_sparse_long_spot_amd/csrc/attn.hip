@@ -45,6 +45,7 @@
 //    all in fp32.
 // Scores are kept in the log2 domain: z = (q.k) * sm_scale * log2(e), p = 2^(z - m).
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "spot_internal.h"
@@ -296,8 +297,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
 
   // Entries [j0, j1) of query b's list (j0 < j1), reduced into slot `slot` of its heads;
   // `last`: no later slot of this query holds a partial.
-  auto run_entries = [&](int b, int j0, int j1, int slot, bool last) {
-    const bool spec = b == b_spec && j0 == j0_spec && j1 - j0 == n_spec;  // uniform
+  // (TrySpec false: the read-ahead is never used, so it need not stay live across a loop
+  // of calls)
+  auto run_entries = [&](int b, int j0, int j1, int slot, bool last, auto try_spec) {
+    const bool spec =
+        decltype(try_spec)::value && b == b_spec && j0 == j0_spec && j1 - j0 == n_spec;
     bf16x8_t qb[KS];
     if (spec) {
 #pragma unroll
@@ -538,44 +542,29 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
   };
 
   if constexpr (FLAT) {
-    // Runs of one common length `chunk` for every query, as many per query as its count
-    // needs (ceil(count / chunk)), with chunk the shortest of three candidates that
-    // keeps the total within the nsplit * B work-groups: so queries that select very
-    // different numbers of blocks keep the work-groups equally busy. Work-group
-    // x + nsplit*z takes run number x + nsplit*z in query order; run k of a query fills
-    // its slot k, and the query's last run is marked as such. With nearly equal counts
-    // (nsplit runs per query no longer than that) the per-query runs are kept: they use
-    // every work-group, which the HBM-bound kernel prefers, and that decision costs one
-    // scan, one maximum and two divisions. Every wave reduces the B counts itself (no
-    // barrier): lane b holds query b's count.
+    // The B lists laid end to end in query order and cut into runs of one length
+    // `chunk`, ceil(total / (nsplit * B)) entries: work-group x + nsplit*z takes run
+    // number x + nsplit*z, so queries that select very different numbers of blocks keep
+    // the work-groups equally busy. A run may end one query's list and start the next
+    // one's: it reduces each part into a partial of that query, in the query's slot
+    // (run number - first run touching the query), and the run holding a query's last
+    // entry marks that partial as the last. chunk >= ceil(max count / (nslot - 1)) keeps
+    // every query within its nslot slots. With nearly equal counts (nsplit runs per
+    // query no longer than chunk) the per-query runs are kept: every work-group then
+    // reduces one query's run, with no run split between two queries. Every wave reduces
+    // the B counts itself (no barrier): lane b holds query b's count.
     const int c = lane < B ? min(max(sel_cnt[lane], 0), K_max) : 0;
     const int wg = nsplit * B;
-    const int total = __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)c), 63);
+    const int end_incl = (int)wave_incl_scan((uint32_t)c);  // lane b: end of b's list
+    const int total = __builtin_amdgcn_readlane(end_incl, 63);
     const float maxf = wave_max_to_last((float)c);  // counts are exact in fp32
     const int maxc = (int)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(maxf), 63));
-    // no query may have more runs than its nslot slots: chunk >= ceil(maxc / nslot),
-    // which is <= bps (nslot >= nsplit = ceil(K_max / bps) and maxc <= K_max)
-    const int lo = max(1, (maxc + nslot - 1) / nslot);
-    int chunk = max(lo, (total + wg - 1) / wg);
-    const int per_query = (maxc + nsplit - 1) / nsplit;
-    if (per_query > chunk) {
-      // the ideal run length if it is feasible, else one between it and the always
-      // feasible total / (wg - nz) (at most nz runs are partly empty); bps is feasible too
-      // (count <= K_max), and bounds a run by the kernel's per-wave list capacity. Longer
-      // runs mean fewer of them, so raising a candidate to lo keeps it feasible.
-      auto runs_at = [&](int ch) {
-        const int r = c > 0 ? (c + ch - 1) / ch : 0;
-        return __builtin_amdgcn_readlane((int)wave_incl_scan((uint32_t)r), 63);
-      };
-      const int nz = __popcll(__ballot(c > 0));
-      if (runs_at(chunk) > wg) {
-        const int safe =
-            max(lo, wg > nz ? min(bps, max(1, (total + wg - nz - 1) / (wg - nz))) : bps);
-        const int mid = max(lo, (2 * total + 2 * wg - nz - 1) / (2 * wg - nz));
-        chunk = mid < safe && runs_at(mid) <= wg ? mid : safe;
-      }
-    }
-    if (per_query <= chunk) {
+    const int lo = (maxc + nslot - 2) / (nslot - 1);  // nslot >= 2 in flat plans
+    int chunk = max(max(lo, 1), (total + wg - 1) / wg);
+    chunk = (chunk + EPC - 1) / EPC * EPC;
+    int per_query = (maxc + nsplit - 1) / nsplit;
+    per_query = (per_query + EPC - 1) / EPC * EPC;
+    if (per_query <= chunk || chunk > bps) {
       const int split = blockIdx.x, b = blockIdx.z;
       const int cnt = __builtin_amdgcn_readlane(c, b);
       int run = (cnt + nsplit - 1) / nsplit;
@@ -584,27 +573,29 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
       const bool last = split == nsplit - 1;  // every slot is written; the last is marked
       const size_t base = slot_base(b, g, G, Hq, nslot, split);
       if (j0 < cnt)
-        run_entries(b, j0, min(j0 + run, cnt), split, last);
+        run_entries(b, j0, min(j0 + run, cnt), split, last, std::true_type{});
       else if (last)
         store_end_marker<G>(base, nslot, ws_ml);
       else
         store_empty_run<G>(base, nslot, ws_ml);
     } else {
-      const int nrun = c > 0 ? (c + chunk - 1) / chunk : 0;  // lane b: runs of query b
-      const int run_incl = (int)wave_incl_scan((uint32_t)nrun);
       const int sidx = blockIdx.x + nsplit * blockIdx.z;
       if (sidx == 0) {  // queries with no entry: an empty last partial in their first slot
         for (int b = 0; b < B; ++b)
           if (__builtin_amdgcn_readlane(c, b) == 0)
             store_end_marker<G>(slot_base(b, g, G, Hq, nslot, 0), nslot, ws_ml);
       }
-      if (sidx < __builtin_amdgcn_readlane(run_incl, 63)) {
-        // the query of run sidx: queries whose runs all come before it
-        const int b = __popcll(__ballot(lane < B && run_incl <= sidx));
-        const int nb_runs = __builtin_amdgcn_readlane(nrun, b);
-        const int k = sidx - (__builtin_amdgcn_readlane(run_incl, b) - nb_runs);
-        const int cb = __builtin_amdgcn_readlane(c, b);
-        run_entries(b, k * chunk, min(cb, (k + 1) * chunk), k, k == nb_runs - 1);
+      const int s0 = sidx * chunk, s1 = min(s0 + chunk, total);
+      // the queries with entries in [s0, s1), lowest first (a wave-uniform mask, the same
+      // in every wave of the work-group)
+      uint64_t touch = __ballot(c > 0 && end_incl > s0 && end_incl - c < s1);
+      while (touch) {
+        const int b = __builtin_ctzll(touch);
+        touch &= touch - 1;
+        const int e = __builtin_amdgcn_readlane(end_incl, b);
+        const int beg = e - __builtin_amdgcn_readlane(c, b);
+        run_entries(b, max(s0, beg) - beg, min(s1, e) - beg, sidx - beg / chunk, e <= s1,
+                    std::false_type{});
       }
     }
   } else {
@@ -619,7 +610,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(
     if (j0 >= cnt)
       store_empty_run<G>(slot_base(b, g, G, Hq, nslot, split), nslot, ws_ml);
     else
-      run_entries(b, j0, min(j0 + run, cnt), split, false);
+      run_entries(b, j0, min(j0 + run, cnt), split, false, std::true_type{});
   }
 }
 

@@ -275,6 +275,10 @@ def _sets_for(pattern, B, nb, K_max, g):
             s = sorted(set(torch.randperm(nb - 1, generator=g)[: c - 1].tolist()) | {nb - 1})
         elif pattern == "empty_rows":
             s = [] if b % 2 == 0 else sorted(torch.randperm(nb, generator=g)[:K_max].tolist())
+        elif pattern == "one_long":  # one full row, then rows of 0 to 3 entries, so that
+            # a run of the batch-wide cut spans several queries (some of them empty)
+            c = K_max if b == 0 else (0, 1, 2, 1, 3)[b % 5]
+            s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
         elif pattern == "skewed":   # a few full rows, the rest short or empty
             c = K_max if b % 5 == 0 else (0 if b % 7 == 3 else 1 + b % 4)
             s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
@@ -311,6 +315,11 @@ ATTN_BLOCK_CASES = [
     (16, 8, 1, 64, 8192, 16, 300, "bf16", "skewed"),
     (8, 16, 4, 128, 8192, 32, 200, "bf16", "skewed"),
     (4, 8, 2, 128, 8192, 64, 128, "bf16", "invalid_prefix"),
+    # runs of a few entries, each spanning up to five queries (the full first row takes
+    # ~26 of its 32 slots)
+    (8, 32, 8, 128, 8192, 64, 128, "bf16", "one_long"),
+    (16, 8, 2, 128, 4096, 16, 64, "bf16", "one_long"),
+    (12, 8, 2, 64, 8192, 32, 256, "bf16", "one_long"),
     # longest runs of the split plan: 16 chunks per wave (64 list entries at block 16)
     (4, 8, 8, 64, 32768, 16, 2048, "bf16", "random"),
     (8, 8, 8, 64, 16384, 32, 512, "bf16", "random"),
