@@ -224,11 +224,10 @@ class GraphSteps:
             self.rest.replay()
 
 
-def time_flushed(inp, wl, bufs, reps, stream):
-    """Per-step time with a 1 GiB write between steps (outside the events), so that no
-    step reads data left in the last-level caches by the previous one."""
+def time_flushed_call(fn, reps, stream):
+    """us of single calls of `fn` on `stream`, each after a 1 GiB write (outside the
+    events), so that no call reads data left in the last-level caches by the one before."""
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    step = DecodeStep(inp, wl, bufs, stream=stream)
     times = []
     torch.cuda.synchronize()  # inputs made on torch's default stream are complete
     with torch.cuda.stream(stream):
@@ -237,12 +236,17 @@ def time_flushed(inp, wl, bufs, reps, stream):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            step()
+            fn()
             b.record(stream)
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b) * 1e3)
     del scratch
     return times
+
+
+def time_flushed(inp, wl, bufs, reps, stream):
+    """Per-step time with a 1 GiB write between steps (outside the events)."""
+    return time_flushed_call(DecodeStep(inp, wl, bufs, stream=stream), reps, stream)
 
 
 def time_step_distribution(fn, n, warmup, stream):
@@ -460,11 +464,19 @@ def page_geometry_step(steps, warmup, stream):
     wl = W.WORKLOADS["page_128k_b1"]
     inp = W.make_inputs(wl, device="cuda")
     bufs = DecodeBuffers.of(wl, inp["q"].dtype)
-    us, _ = time_back_to_back(DecodeStep(inp, wl, bufs, stream=stream), steps, warmup, stream)
+    step = DecodeStep(inp, wl, bufs, stream=stream)
+    us, _ = time_back_to_back(step, steps, warmup, stream)
     _, _, per = time_steps(inp, wl, bufs, steps, warmup, stream)
     tok = selected_tokens(bufs.sel_idx, bufs.sel_cnt, wl.L, wl.block)
     bb = byte_budget(wl, wl.B, tok)
     mean = {k: statistics.fmean(v) for k, v in per.items()}
+    # the step and the attention call after a 1 GiB write each, and the read-only kernel
+    # over the call's K/V bytes the same way (as 16 KiB blocks: the call reads 4 KiB
+    # pieces, which a read-only kernel of that size reads within a few per cent as fast)
+    fl = quantiles(time_flushed_call(step, 30, stream))
+    fa = quantiles(time_flushed_call(step.calls[2], 30, stream))
+    rc = read_ceiling(bb["attn"], stream, reps=30, flushed=True)
+    rc["attn_frac_of_it"] = round(bb["attn"] / (fa["median"] * 1e-6) / 1e9 / rc["GBps"], 4)
     res = {"workload": wl.name,
            "geometry": "L 131072, block 16, 16 per-token selector keys per block, 4 x 128 "
                        "bf16, batch 1; p 0.9, K_min 32, sink 8, recency 16 blocks, no cap",
@@ -475,8 +487,9 @@ def page_geometry_step(steps, warmup, stream):
            "per_call_us_mean": {k: round(v, 3) for k, v in mean.items()},
            "score_bytes": bb["score"],
            "score_GBps": round(bb["score"] / (mean["score"] * 1e-6) / 1e9, 1),
+           "flushed_step_us": fl, "flushed_attn_call_us": fa, "read_ceiling_flushed": rc,
            "paper_selector_us_per_layer_B200": round(1550.0 / 36, 1)}
-    del inp, bufs
+    del inp, bufs, step
     torch.cuda.empty_cache()
     return res
 
@@ -595,19 +608,21 @@ def launch_floor(stream, reps=2000):
     return res
 
 
-def read_ceiling(nbytes, stream, reps=20):
+def read_ceiling(nbytes, stream, reps=20, flushed=False):
     """What a kernel that only reads sustains on this GPU for the attention's access
     pattern: about `nbytes` as 16 KiB blocks (one 64-token block of one KV head at
     d = 128 in bf16) picked in random order from a buffer twice that size, 16-byte
     non-temporal loads, no compute. Best of 256, 512 and 1024 work-groups, HIP events
-    around `reps` back-to-back launches on `stream`."""
+    around `reps` back-to-back launches on `stream`; flushed: the median of `reps`
+    single launches, each after a 1 GiB write (as a decode step meets the K/V cache
+    when other work ran in between)."""
     import ctypes
     lib = ctypes.CDLL(PROBE_LIB)
     lib.spot_probe_read_blocks.restype = ctypes.c_int
     lib.spot_probe_read_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     blk = 16384
-    n = nbytes // blk // 2048 * 2048
+    n = max(512, nbytes // blk // 512 * 512)
     buf = torch.ones(2 * n * blk // 2, dtype=torch.bfloat16, device="cuda")
     g = torch.Generator().manual_seed(7)
     lst = torch.randperm(2 * n, generator=g)[:n].to(torch.int32).cuda()
@@ -615,6 +630,8 @@ def read_ceiling(nbytes, stream, reps=20):
     per = {}
     with torch.cuda.stream(stream):
         for wgs in (256, 512, 1024):
+            if n % (2 * wgs):
+                continue
             def go():
                 st = lib.spot_probe_read_blocks(buf.data_ptr(), lst.data_ptr(), n, wgs,
                                                 sink.data_ptr(), stream.cuda_stream)
@@ -622,19 +639,24 @@ def read_ceiling(nbytes, stream, reps=20):
                     raise RuntimeError("spot_probe_read_blocks failed")
             for _ in range(3):
                 go()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                go()
-            e1.record(stream)
-            e1.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            if flushed:
+                us = statistics.median(time_flushed_call(go, reps, stream))
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    go()
+                e1.record(stream)
+                e1.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
             per[wgs] = {"us": round(us, 3), "GBps": round(n * blk / (us * 1e-6) / 1e9, 1)}
     del buf, lst, sink
     best = max(v["GBps"] for v in per.values())
     return {"GBps": best, "bytes": n * blk, "per_workgroups": per,
             "what": "read-only kernel, the same bytes as 16 KiB blocks in random order, "
-                    "16-byte non-temporal loads, no compute (read_ceiling.hip)"}
+                    "16-byte non-temporal loads, no compute (read_ceiling.hip)"
+                    + (", one launch after a 1 GiB write, median" if flushed else "")}
 
 
 def cpu_baseline(wl, inp, b_sample, b_single=None):
@@ -781,6 +803,8 @@ def main():
     med = {k: statistics.median(v) for k, v in per.items()}
     log(f"bench: per-call event means {mean}")
     flushed = time_flushed(inp, wl, bufs, a.flushed_reps, stream) if a.flushed_reps else []
+    flushed_attn = (quantiles(time_flushed_call(attn_call, a.flushed_reps, stream))
+                    if a.flushed_reps else None)
     g_wall, g_event = time_graph(inp, wl, bufs, a.steps, a.warmup, stream)
     log(f"bench: graph replay {g_wall:.1f} us/step wall")
     attn_gbps = budget["attn"] / (attn_us * 1e-6) / 1e9
@@ -843,6 +867,7 @@ def main():
                    "output_matches_stream_launch": graphs_ok},
         "stream_launch_us_per_step": round(us_stream, 3),
         "flushed_step_us": quantiles(flushed) if flushed else None,
+        "flushed_attn_call_us": flushed_attn,
         "pages_context": "paper: 3.9x FlashAttention, 1.8x Twilight end-to-end decode tok/s "
                          "at 128K on one NVIDIA B200 (not comparable to this metric)",
     }
@@ -850,6 +875,11 @@ def main():
     rc = read_ceiling(budget["attn"], stream)
     rc["attn_frac_of_it"] = round(attn_gbps / rc["GBps"], 4)
     rc["step_frac_of_it"] = round(budget["step"] / (us_step * 1e-6) / 1e9 / rc["GBps"], 4)
+    if flushed_attn:
+        rcf = read_ceiling(budget["attn"], stream, reps=a.flushed_reps, flushed=True)
+        rcf["attn_frac_of_it"] = round(
+            budget["attn"] / (flushed_attn["median"] * 1e-6) / 1e9 / rcf["GBps"], 4)
+        rc["flushed"] = rcf
     result["read_ceiling"] = rc
     result["launch_floor"] = launch_floor(stream)
     if a.extra_b1 and wl.name == "c3_128k_b8":
@@ -869,9 +899,13 @@ def main():
                "per_step_events": time_step_distribution(step1, max(200, a.steps), a.warmup,
                                                          stream)}
         fl1 = time_flushed(inp1, wl1, bufs1, max(50, a.flushed_reps), stream)
+        fa1 = quantiles(time_flushed_call(step1.calls[2], max(50, a.flushed_reps), stream))
         tok1 = selected_tokens(bufs1.sel_idx, bufs1.sel_cnt, wl1.L, wl1.block)
         b1 = byte_budget(wl1, 1, tok1)
         fl1q = quantiles(fl1)
+        rc1 = read_ceiling(b1["attn"], stream, reps=max(50, a.flushed_reps), flushed=True)
+        rc1["attn_frac_of_it"] = round(b1["attn"] / (fa1["median"] * 1e-6) / 1e9 / rc1["GBps"],
+                                       4)
         result["batch1"] = {
             "us_per_step": round(u1, 3),
             "stream_launch_us_per_step": round(u1s, 3),
@@ -883,13 +917,17 @@ def main():
                             "GBps": round(b1["step"] / (fl1q["median"] * 1e-6) / 1e9, 1),
                             "frac": round(b1["step"] / (fl1q["median"] * 1e-6) / 1e9
                                           / HBM_PEAK_GBPS, 4)},
+            "flushed_attn_call_us": fa1,
+            "read_ceiling_flushed": rc1,
             "queries_per_s": round(1 / (u1 * 1e-6), 1),
             "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in p1.items()},
             "note": "batch row 0 of the same inputs. us_per_step / GBps: K steps back to "
                     "back as HIP graphs (stream_launch_us_per_step: launched one call at a "
                     "time), so the 68 MB a step reads partly come from the 256 MB "
                     "last-level cache; flushed_step_us / flushed_hbm: a 1 GiB write between "
-                    "steps (outside the events), the HBM figure"}
+                    "steps (outside the events), the HBM figure; flushed_attn_call_us: the "
+                    "attention call alone, the same way; read_ceiling_flushed: the read-only "
+                    "kernel over the call's K/V bytes, the same way"}
         del inp1, bufs1, gs1
     if a.static and wl.name == "c3_128k_b8":
         log("bench: static top-K at half the context")
