@@ -473,9 +473,9 @@ def page_geometry_step(steps, warmup, stream):
     # the step and the attention call after a 1 GiB write each, and the read-only kernel
     # over the call's K/V bytes the same way (as 16 KiB blocks: the call reads 4 KiB
     # pieces, which a read-only kernel of that size reads within a few per cent as fast)
-    fl = quantiles(time_flushed_call(step, 30, stream))
-    fa = quantiles(time_flushed_call(step.calls[2], 30, stream))
-    rc = read_ceiling(bb["attn"], stream, reps=30, flushed=True)
+    fl = quantiles(time_flushed_call(step, 200, stream))
+    fa = quantiles(time_flushed_call(step.calls[2], 200, stream))
+    rc = read_ceiling(bb["attn"], stream, reps=200, flushed=True)
     rc["attn_frac_of_it"] = round(bb["attn"] / (fa["median"] * 1e-6) / 1e9 / rc["GBps"], 4)
     res = {"workload": wl.name,
            "geometry": "L 131072, block 16, 16 per-token selector keys per block, 4 x 128 "
@@ -717,7 +717,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c3_128k_b8", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flushed-reps", type=int, default=50)
+    ap.add_argument("--flushed-reps", type=int, default=200)
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed back-to-back steps before any timing")
     ap.add_argument("--extra-b1", action="store_true", default=True)
@@ -898,12 +898,12 @@ def main():
                "stream_launch_bursts": burst_stats(step1, a.steps, stream),
                "per_step_events": time_step_distribution(step1, max(200, a.steps), a.warmup,
                                                          stream)}
-        fl1 = time_flushed(inp1, wl1, bufs1, max(50, a.flushed_reps), stream)
-        fa1 = quantiles(time_flushed_call(step1.calls[2], max(50, a.flushed_reps), stream))
+        fl1 = time_flushed(inp1, wl1, bufs1, max(200, a.flushed_reps), stream)
+        fa1 = quantiles(time_flushed_call(step1.calls[2], max(200, a.flushed_reps), stream))
         tok1 = selected_tokens(bufs1.sel_idx, bufs1.sel_cnt, wl1.L, wl1.block)
         b1 = byte_budget(wl1, 1, tok1)
         fl1q = quantiles(fl1)
-        rc1 = read_ceiling(b1["attn"], stream, reps=max(50, a.flushed_reps), flushed=True)
+        rc1 = read_ceiling(b1["attn"], stream, reps=max(200, a.flushed_reps), flushed=True)
         rc1["attn_frac_of_it"] = round(b1["attn"] / (fa1["median"] * 1e-6) / 1e9 / rc1["GBps"],
                                        4)
         result["batch1"] = {
