@@ -676,13 +676,17 @@ def test_graph_replay_matches_eager():
         assert torch.equal(bufs.out, ref[2]), f"replay {i}"
 
 
-def test_graph_replay_headline_shape_dirty_workspace():
+@pytest.mark.parametrize("spread", [None, (1.3, 2.0)], ids=["equal_budgets", "spread_budgets"])
+def test_graph_replay_headline_shape_dirty_workspace(spread):
     """The 128K batch-8 decode step (runs cut across the batch, the merge stopping at each
     query's flagged last slot) captured in a HIP graph as a server would: every replay,
     with the workspace overwritten by 0xFF bytes (NaN partials) and the outputs poisoned
-    between replays, reproduces the stream-launched step bit for bit."""
+    between replays, reproduces the stream-launched step bit for bit. With budgets spread
+    over the batch (Zipf 1.3-2.0 per row) the runs span two or three queries each."""
     wl = W.WORKLOADS["c3_128k_b8"]
-    log("graph replay c3_128k_b8")
+    if spread is not None:
+        wl = wl.with_(zipf_spread=spread)
+    log(f"graph replay c3_128k_b8 spread={spread}")
     inp = W.make_inputs(wl, device=DEV)
     bufs = DecodeBuffers.of(wl, inp["q"].dtype)
     stream = torch.cuda.Stream()
@@ -692,6 +696,8 @@ def test_graph_replay_headline_shape_dirty_workspace():
         step()
     torch.cuda.synchronize()
     ref = (bufs.scores.clone(), bufs.sel_idx.clone(), bufs.sel_cnt.clone(), bufs.out.clone())
+    if spread is not None:  # the rows really select different numbers of blocks
+        assert len(set(bufs.sel_cnt.tolist())) > 2, bufs.sel_cnt.tolist()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         step()
