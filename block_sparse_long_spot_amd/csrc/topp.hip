@@ -348,36 +348,30 @@ __global__ __launch_bounds__(NT) void select_topp_kernel(const float* __restrict
   }
   {
     // Target t (0: mass T, 1: count tl, 2: count th) is reached in the one bin whose
-    // prefix is below it and whose prefix plus content is not. Each thread finds its
-    // hit, if any, with selects over its bins; only the wave holding a hit stores it.
-    u64 Ps[BPT];  // packed prefix above each of this thread's bins
-    {
-      u64 P = before + incl - loc;
-#pragma unroll
-      for (int i = 0; i < BPT; ++i) {
-        Ps[i] = P;
-        P += hb[i];
-      }
-    }
+    // prefix is below it and whose prefix plus content is not. The threads' bin ranges
+    // partition the prefix, so one thread holds that bin: it is the thread whose whole
+    // range brackets the target (one test per thread), and only it looks at its bins.
+    const u64 P0 = before + incl - loc;  // packed prefix above this thread's bins
+    const u64 P1 = before + incl;        // ... and above the bins after them
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       const u64 X = t == 0 ? T : static_cast<u64>(t == 1 ? tl : th);
       if (X == 0) continue;  // uniform
-      int hit = -1;
-      u64 hpre = 0, hcnt = 0;
+      const u64 lo_x = t == 0 ? (P0 & kMassMask) : (P0 >> kCntShift);
+      const u64 hi_x = t == 0 ? (P1 & kMassMask) : (P1 >> kCntShift);
+      if (lo_x < X && X <= hi_x) {
+        u64 P = P0;
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) {
-        const u64 below = t == 0 ? (Ps[i] & kMassMask) : (Ps[i] >> kCntShift);
-        const u64 in = t == 0 ? (hb[i] & kMassMask) : (hb[i] >> kCntShift);
-        const bool h = below < X && X <= below + in;
-        hit = h ? i : hit;
-        hpre = h ? Ps[i] : hpre;
-        hcnt = h ? (hb[i] >> kCntShift) : hcnt;
-      }
-      if (__ballot(hit >= 0) != 0 && hit >= 0) {
-        sh.f_bin[t] = tid * BPT + hit;
-        sh.f_pre[t] = hpre;
-        sh.f_cnt[t] = hcnt;
+        for (int i = 0; i < BPT; ++i) {
+          const u64 below = t == 0 ? (P & kMassMask) : (P >> kCntShift);
+          const u64 in = t == 0 ? (hb[i] & kMassMask) : (hb[i] >> kCntShift);
+          if (below < X && X <= below + in) {
+            sh.f_bin[t] = tid * BPT + i;
+            sh.f_pre[t] = P;
+            sh.f_cnt[t] = hb[i] >> kCntShift;
+          }
+          P += hb[i];
+        }
       }
     }
   }
