@@ -277,10 +277,14 @@ def _sets_for(pattern, B, nb, K_max, g):
             s = [] if b % 2 == 0 else sorted(torch.randperm(nb, generator=g)[:K_max].tolist())
         elif pattern == "one_long":  # one full row, then rows of 0 to 3 entries, so that
             # a run of the batch-wide cut spans several queries (some of them empty)
-            c = K_max if b == 0 else (0, 1, 2, 1, 3)[b % 5]
+            c = min(K_max if b == 0 else (0, 1, 2, 1, 3)[b % 5], K_max, nb)
+            s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
+        elif pattern == "heavy":  # heavy-tailed counts: many short rows, some empty
+            u = float(torch.rand(1, generator=g))
+            c = 0 if u < 0.2 else max(1, int(min(nb, K_max) * u ** 3))
             s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
         elif pattern == "skewed":   # a few full rows, the rest short or empty
-            c = K_max if b % 5 == 0 else (0 if b % 7 == 3 else 1 + b % 4)
+            c = min(K_max if b % 5 == 0 else (0 if b % 7 == 3 else 1 + b % 4), K_max, nb)
             s = sorted(torch.randperm(nb, generator=g)[:c].tolist())
         else:
             c = int(torch.randint(1, K_max + 1, (1,), generator=g))
@@ -329,6 +333,32 @@ ATTN_BLOCK_CASES = [
 
 @pytest.mark.parametrize("case", ATTN_BLOCK_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_sparse_attn_block_sizes(case):
+    B, Hq, Hkv, d, L, block, K_max, dt, pattern = case
+    _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag=str(case), dirty_ws=True)
+
+
+def _flat_configs(n=32, seed=777):
+    """Seeded bf16 attention cases at batch 2..48 (runs cut from the batch's lists laid end
+    to end, which may span queries), with uneven counts and a dirty workspace."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        B = rng.randint(2, 48)
+        Hkv, G = rng.choice([1, 2, 4, 8]), rng.choice([1, 2, 4, 8])
+        d, block = rng.choice([64, 128]), rng.choice([16, 32, 64, 128])
+        L = rng.randint(2, 120) * block + rng.choice([0, rng.randint(1, block - 1)])
+        nb = -(-L // block)
+        K_max = rng.randint(1, nb)
+        if B * G * Hkv * K_max * block > (1 << 22):
+            continue
+        out.append((B, G * Hkv, Hkv, d, L, block, K_max, "bf16",
+                    rng.choice(["heavy", "heavy", "one_long", "skewed", "random"])))
+    return out
+
+
+@pytest.mark.parametrize("case", _flat_configs(), ids=lambda c: "-".join(map(str, c)))
+def test_sparse_attn_flat_sweep(case):
     B, Hq, Hkv, d, L, block, K_max, dt, pattern = case
     _attn_case(B, Hq, Hkv, d, L, block, K_max, dt, pattern, tag=str(case), dirty_ws=True)
 
