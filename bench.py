@@ -249,6 +249,39 @@ def time_flushed(inp, wl, bufs, reps, stream):
     return time_flushed_call(DecodeStep(inp, wl, bufs, stream=stream), reps, stream)
 
 
+def time_flushed_graph(step, stream, n=20, reps=15):
+    """Per-step time after a 1 GiB write, without an event beside every step (each adds a
+    gap of about 2 us): one HIP graph of n (write, step) pairs and one of the n writes
+    alone, each replayed `reps` times between device synchronisations; the step's time
+    is the difference of the two medians divided by n. The write is a fill kernel."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    graphs = []
+    for with_step in (True, False):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                scratch.fill_(1.0)
+                if with_step:
+                    step()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    med = []
+    for g in graphs:
+        g.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        med.append(statistics.median(ts))
+    del graphs, scratch
+    torch.cuda.empty_cache()
+    return round((med[0] - med[1]) * 1e6 / n, 3)
+
+
 def time_step_distribution(fn, n, warmup, stream):
     """Per-step times of n back-to-back steps: one HIP event recorded on `stream` at every
     step boundary (each adds a small gap, so the mean sits a little above the headline's
@@ -805,6 +838,7 @@ def main():
     flushed = time_flushed(inp, wl, bufs, a.flushed_reps, stream) if a.flushed_reps else []
     flushed_attn = (quantiles(time_flushed_call(attn_call, a.flushed_reps, stream))
                     if a.flushed_reps else None)
+    flushed_graph = time_flushed_graph(step, stream) if a.flushed_reps else None
     g_wall, g_event = time_graph(inp, wl, bufs, a.steps, a.warmup, stream)
     log(f"bench: graph replay {g_wall:.1f} us/step wall")
     attn_gbps = budget["attn"] / (attn_us * 1e-6) / 1e9
@@ -868,6 +902,7 @@ def main():
         "stream_launch_us_per_step": round(us_stream, 3),
         "flushed_step_us": quantiles(flushed) if flushed else None,
         "flushed_attn_call_us": flushed_attn,
+        "flushed_graph_us_per_step": flushed_graph,
         "pages_context": "paper: 3.9x FlashAttention, 1.8x Twilight end-to-end decode tok/s "
                          "at 128K on one NVIDIA B200 (not comparable to this metric)",
     }
@@ -900,6 +935,7 @@ def main():
                                                          stream)}
         fl1 = time_flushed(inp1, wl1, bufs1, max(200, a.flushed_reps), stream)
         fa1 = quantiles(time_flushed_call(step1.calls[2], max(200, a.flushed_reps), stream))
+        fg1 = time_flushed_graph(step1, stream)
         tok1 = selected_tokens(bufs1.sel_idx, bufs1.sel_cnt, wl1.L, wl1.block)
         b1 = byte_budget(wl1, 1, tok1)
         fl1q = quantiles(fl1)
@@ -918,6 +954,10 @@ def main():
                             "frac": round(b1["step"] / (fl1q["median"] * 1e-6) / 1e9
                                           / HBM_PEAK_GBPS, 4)},
             "flushed_attn_call_us": fa1,
+            "flushed_graph_us_per_step": fg1,
+            "flushed_graph_hbm": {"GBps": round(b1["step"] / (fg1 * 1e-6) / 1e9, 1),
+                                  "frac": round(b1["step"] / (fg1 * 1e-6) / 1e9
+                                                / HBM_PEAK_GBPS, 4)},
             "read_ceiling_flushed": rc1,
             "queries_per_s": round(1 / (u1 * 1e-6), 1),
             "per_call_us_mean": {k: round(statistics.fmean(v), 3) for k, v in p1.items()},
@@ -926,8 +966,11 @@ def main():
                     "time), so the 68 MB a step reads partly come from the 256 MB "
                     "last-level cache; flushed_step_us / flushed_hbm: a 1 GiB write between "
                     "steps (outside the events), the HBM figure; flushed_attn_call_us: the "
-                    "attention call alone, the same way; read_ceiling_flushed: the read-only "
-                    "kernel over the call's K/V bytes, the same way"}
+                    "attention call alone, the same way; flushed_graph_us_per_step: the same "
+                    "write before every step with no event beside the steps (graphs of 20 "
+                    "write + step pairs minus graphs of the 20 writes); read_ceiling_flushed: "
+                    "the read-only kernel over the call's K/V bytes, the same way as "
+                    "flushed_attn_call_us"}
         del inp1, bufs1, gs1
     if a.static and wl.name == "c3_128k_b8":
         log("bench: static top-K at half the context")
